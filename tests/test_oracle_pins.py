@@ -1,0 +1,504 @@
+"""Pins of the fp64 oracle to facts fixed by the pages and by mathematics.
+
+Each test checks the oracle against something other than itself: worked
+examples the pages print (tests/golden), closed forms, invariants, brute
+force on tiny inputs and independent library routines.  The final group
+plants plausible mistakes into copies of oracle functions and shows that the
+pins catch them.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import akv_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------------------
+# bfloat16 rounding
+# ---------------------------------------------------------------------------
+def test_bf16_matches_torch_for_fp32_inputs():
+    """For float32-representable inputs, fp64->bf16 in one step equals torch's
+    float32->bfloat16 conversion (round half to even, no double rounding)."""
+    import torch
+    rng = np.random.default_rng(0)
+    mant = rng.uniform(-2, 2, size=200000).astype(np.float32)
+    expo = rng.integers(-140, 128, size=mant.shape).astype(np.float32)
+    x = (mant * np.exp2(expo)).astype(np.float32)
+    x = x[np.isfinite(x)]
+    # force exact ties too: patterns whose low 16 bits are 0x8000
+    ties = (rng.integers(0, 2**31, size=20000, dtype=np.uint32) & 0xFFFF0000) | 0x8000
+    x = np.concatenate([x, ties.view(np.float32)[np.isfinite(ties.view(np.float32))]])
+    ref = torch.from_numpy(x.copy()).to(torch.bfloat16).to(torch.float64).numpy()
+    got = O.bf16_round(x.astype(np.float64))
+    assert np.array_equal(got, ref)
+
+
+def test_bf16_hand_built_ties_and_edges():
+    t = O.bf16_round
+    assert t(1 + 2**-8) == 1.0                       # tie -> even (mantissa 0)
+    assert t(1 + 3 * 2**-8) == 1 + 2**-6             # tie -> even (mantissa 2)
+    assert t(1 + 2**-8 + 2**-40) == 1 + 2**-7        # just above a tie: up
+    assert t(-(1 + 2**-8 + 2**-40)) == -(1 + 2**-7)
+    # one-step rounding differs from fp64 -> fp32 -> bf16 here
+    x = 1 + 2**-8 + 2**-40
+    assert np.float64(np.float32(x)) == 1 + 2**-8    # fp32 loses the 2^-40
+    # overflow: max stays, the tie above max goes to inf, just below stays max
+    assert t(O.BF16_MAX) == O.BF16_MAX
+    assert t(O.BF16_MAX + 2.0**119) == np.inf
+    assert t(O.BF16_MAX + 2.0**118) == O.BF16_MAX
+    assert t(-(O.BF16_MAX + 2.0**119)) == -np.inf
+    # subnormals: spacing 2^-133
+    assert t(2.0**-133) == 2.0**-133
+    assert t(2.0**-134) == 0.0                       # tie between 0 and 2^-133 -> 0
+    assert t(3 * 2.0**-134) == 2.0**-132             # tie -> even
+    assert t(2.0**-134 + 2.0**-160) == 2.0**-133
+    # signed zero is kept
+    assert math.copysign(1.0, t(-0.0)) == -1.0
+    assert math.copysign(1.0, t(-1e-50)) == -1.0
+    assert np.isnan(t(np.nan))
+
+
+def test_bf16_fixed_points_all_patterns():
+    """Every finite bf16 value is a fixed point and its bits round-trip."""
+    u = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    v = O.bf16_from_bits(u)
+    fin = np.isfinite(v)
+    assert np.array_equal(O.bf16_round(v[fin]), v[fin])
+    assert np.array_equal(O.bf16_bits(v[fin]), u[fin])
+    # ulp distance: neighbours are 1 apart, +0/-0 coincide
+    assert O.bf16_ulp_distance(np.uint16(0x3F80), np.uint16(0x3F81)) == 1
+    assert O.bf16_ulp_distance(np.uint16(0x0000), np.uint16(0x8000)) == 0
+    assert O.bf16_ulp_distance(np.uint16(0x0001), np.uint16(0x8001)) == 2
+
+
+# ---------------------------------------------------------------------------
+# RoPE frequencies and rotation
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("d,base", [(128, 1e4), (128, 5e5), (64, 1.5e5)])
+def test_theta_closed_form(d, base):
+    th = O.rope_theta(d, base)
+    assert th.shape == (d // 2,)
+    assert th[0] == 1.0
+    i = np.arange(d // 2)
+    np.testing.assert_allclose(np.log(th), -(2.0 * i / d) * np.log(base), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(th[1:] / th[:-1], base ** (-2.0 / d), rtol=1e-14)
+
+
+@pytest.mark.parametrize("delta", [1, -1, 7, -1024, -15360, -131071, 65535])
+def test_rotation_unit_vectors(delta):
+    """x = e_0 turns to (cos delta, sin delta) on pair 0 (theta_0 = 1); y = e_{d/2}
+    turns to (-sin delta, cos delta).  Pins sign, pairing and theta_0."""
+    d = 128
+    th = O.rope_theta(d, 5e5)
+    ex = np.zeros(d); ex[0] = 1.0
+    ey = np.zeros(d); ey[d // 2] = 1.0
+    rx = O.rotate_pairs(ex, delta, th)
+    ry = O.rotate_pairs(ey, delta, th)
+    assert rx[0] == np.cos(float(delta)) and rx[d // 2] == np.sin(float(delta))
+    assert ry[0] == -np.sin(float(delta)) and ry[d // 2] == np.cos(float(delta))
+    others = np.ones(d, bool); others[[0, d // 2]] = False
+    assert not rx[others].any() and not ry[others].any()
+
+
+@pytest.mark.parametrize("d,base", [(128, 5e5), (64, 1.5e5)])
+def test_rotation_matches_complex_multiplication(d, base):
+    """Pair i as the complex number x + i*y, multiplied by exp(i*delta*theta_i)."""
+    rng = np.random.default_rng(1)
+    k = rng.standard_normal((50, d))
+    delta = rng.integers(-131071, 131072, size=50)
+    th = O.rope_theta(d, base)
+    got = O.rotate_pairs(k, delta, th)
+    z = (k[:, : d // 2] + 1j * k[:, d // 2:]) * np.exp(1j * np.outer(delta, th))
+    np.testing.assert_allclose(got[:, : d // 2], z.real, atol=1e-12)
+    np.testing.assert_allclose(got[:, d // 2:], z.imag, atol=1e-12)
+
+
+def test_rotation_preserves_pair_norms():
+    rng = np.random.default_rng(2)
+    k = rng.standard_normal((100, 128))
+    th = O.rope_theta(128, 5e5)
+    r = O.rotate_pairs(k, rng.integers(-131071, 131072, size=100), th)
+    n0 = np.hypot(k[:, :64], k[:, 64:])
+    n1 = np.hypot(r[:, :64], r[:, 64:])
+    np.testing.assert_allclose(n1, n0, rtol=1e-13)
+
+
+def test_rotation_composition_and_inverse_fp64():
+    rng = np.random.default_rng(3)
+    k = rng.standard_normal((64, 128))
+    th = O.rope_theta(128, 5e5)
+    a = rng.integers(-50000, 50000, size=64)
+    b = rng.integers(-50000, 50000, size=64)
+    two = O.rotate_pairs(O.rotate_pairs(k, a, th), b, th)
+    one = O.rotate_pairs(k, a + b, th)
+    np.testing.assert_allclose(two, one, atol=1e-10)
+    back = O.rotate_pairs(O.rotate_pairs(k, a, th), -a, th)
+    np.testing.assert_allclose(back, k, atol=1e-10)
+
+
+def _pair_norm(k):
+    h = k.shape[-1] // 2
+    n = np.hypot(k[..., :h], k[..., h:])
+    return np.concatenate([n, n], axis=-1)
+
+
+def test_rerotation_bf16_composition_inverse_identity():
+    """After bf16 rounding: p->q->s vs p->s and p->q->p stay within 2^-7 of the
+    pair norm (three / two half-spacing roundings of components bounded by the
+    norm); delta = 0 is bit-identical ([AKV] sec. 5.5: equal positions copy)."""
+    import torch
+    rng = np.random.default_rng(4)
+    n, L, H, d = 40, 2, 3, 128
+    k = torch.randn(n, L, H, d, generator=torch.Generator().manual_seed(5)
+                    ).to(torch.bfloat16).to(torch.float64).numpy()
+    k[0, 0, 0, :4] = -0.0
+    th = O.rope_theta(d, 5e5)
+    p = rng.integers(0, 60000, size=n)
+    q = rng.integers(0, 60000, size=n)
+    s = rng.integers(0, 60000, size=n)
+    kq = O.rerotate_keys(k, q - p, th)
+    ks = O.rerotate_keys(kq, s - q, th)
+    direct = O.rerotate_keys(k, s - p, th)
+    bound = 2.0 ** -7 * _pair_norm(k)
+    assert np.all(np.abs(ks - direct) <= bound)
+    kp = O.rerotate_keys(kq, p - q, th)
+    assert np.all(np.abs(kp - k) <= bound)
+    same = O.rerotate_keys(k, np.zeros(n, np.int64), th)
+    assert np.array_equal(O.bf16_bits(same), O.bf16_bits(k))
+    # every rotated value is a bf16 value
+    assert np.array_equal(O.bf16_round(kq), kq)
+
+
+def test_relative_position_property():
+    """(R(a+s) q).(R(b+s) k) = (R(a) q).(R(b) k): scores depend only on a-b."""
+    rng = np.random.default_rng(6)
+    th = O.rope_theta(128, 5e5)
+    for _ in range(20):
+        qv, kv = rng.standard_normal(128), rng.standard_normal(128)
+        a, b, s = (int(x) for x in rng.integers(0, 100000, size=3))
+        lhs = O.rotate_pairs(qv, a + s, th) @ O.rotate_pairs(kv, b + s, th)
+        rhs = O.rotate_pairs(qv, a, th) @ O.rotate_pairs(kv, b, th)
+        assert abs(lhs - rhs) <= 1e-9
+
+
+# ---------------------------------------------------------------------------
+# drop / reposition / append semantics
+# ---------------------------------------------------------------------------
+def _filled_cache(n, L=1, H=2, d=8, base=1e4, seed=0):
+    rng = np.random.default_rng(seed)
+    c = O.OracleCache(L, H, d, base)
+    k = O.bf16_round(rng.standard_normal((n, L, H, d)))
+    v = O.bf16_round(rng.standard_normal((n, L, H, d)))
+    c.append(0, np.arange(100, 100 + n), k, v)
+    return c, k, v
+
+
+def test_drop_brute_force_every_small_mask():
+    """Every mask of length <= 10 against a literal list filter."""
+    for n in range(0, 11):
+        for bits in itertools.product((0, 1), repeat=n):
+            c, k, v = _filled_cache(n)
+            before = [(int(t), int(p)) for t, p in zip(c.seqs[0].token_ids, c.seqs[0].pos)]
+            src = c.drop(0, np.array(bits, np.uint8))
+            want = [e for e, m in zip(before, bits) if not m]
+            s = c.seqs[0]
+            assert [(int(t), int(p)) for t, p in zip(s.token_ids, s.pos)] == want
+            assert list(src) == [i for i, m in enumerate(bits) if not m]
+            assert s.next_pos == n                      # eq. 4: next position not lowered
+            assert np.array_equal(s.k, k[src]) and np.array_equal(s.v, v[src])
+
+
+def test_reposition_canonical_and_explicit():
+    c, k, v = _filled_cache(12)
+    c.drop(0, np.array([0, 1, 1, 0, 0, 0, 1, 0, 0, 0, 0, 1], np.uint8))
+    s = c.seqs[0]
+    old_pos = s.pos.copy()
+    v_before = s.v.copy()
+    delta = c.reposition(0)
+    assert list(s.pos) == list(range(8)) and s.next_pos == 8
+    assert np.array_equal(delta, np.arange(8) - old_pos)
+    assert np.array_equal(s.v, v_before)                # V never touched
+    c.reposition(0, np.array([3, 4, 9, 10, 11, 20, 21, 40]))
+    assert s.next_pos == 41
+    with pytest.raises(ValueError):
+        c.reposition(0, np.array([3, 3, 9, 10, 11, 20, 21, 40]))
+    with pytest.raises(ValueError):
+        c.reposition(0, np.array([-1, 3, 9, 10, 11, 20, 21, 40]))
+    # empty cache: next position 0
+    c.drop(0, np.ones(8, np.uint8))
+    assert s.next_pos == 41                              # drop keeps next_pos
+    c.reposition(0)
+    assert s.next_pos == 0 and len(s) == 0
+
+
+def test_fig10_walkthrough():
+    g = json.load(open(os.path.join(GOLDEN, "fig10_positions.json")))
+    c = O.OracleCache(1, 1, 2, 1e4, with_kv=False)
+    ids = {}
+    for step in g["steps"]:
+        s = c.seqs[0]
+        names = {v: k for k, v in ids.items()}
+        if step["op"] == "append":
+            for t in step["tokens"]:
+                ids[t] = len(ids)
+                c.append(0, [ids[t]])
+        else:
+            mask = None
+            if "drop" in step:
+                mask = np.array([names[int(t)] in step["drop"] for t in s.token_ids], np.uint8)
+            if step["op"] == "drop":
+                c.drop(0, mask)
+            elif step["op"] == "repos":
+                c.reposition(0)
+            else:
+                c.drop_reposition(0, mask)
+        names = {v: k for k, v in ids.items()}
+        got = {names[int(t)]: int(p) for t, p in zip(s.token_ids, s.pos)}
+        assert got == step["expect"], step
+        assert s.next_pos == step["next_pos"], step
+
+
+def _apply_request(cache, msg_lens, cache_ops, k=None, v=None):
+    """Message-level request grammar: each message is an implicit append; after
+    message i, drop the listed messages, then reposition if i is listed."""
+    owner = []
+    off = 0
+    for i, n in enumerate(msg_lens):
+        if k is None:
+            cache.append(0, np.arange(off, off + n))
+        else:
+            cache.append(0, np.arange(off, off + n), k[off:off + n], v[off:off + n])
+        owner += [i] * n
+        off += n
+        s = cache.seqs[0]
+        drops = cache_ops.get("drop_message", {}).get(str(i), [])
+        rep = i in cache_ops.get("reposition", [])
+        mask = np.array([owner[t] in drops for t in s.token_ids], np.uint8)
+        if drops and rep:
+            cache.drop_reposition(0, mask)
+        elif drops:
+            cache.drop(0, mask)
+        elif rep:
+            cache.reposition(0)
+    return owner
+
+
+@pytest.mark.parametrize("lens", [(3, 2, 5, 2, 4), (1, 1, 1, 1, 1), (16, 17, 33, 5, 40)])
+def test_five_message_example(lens):
+    g = json.load(open(os.path.join(GOLDEN, "five_message_example.json")))
+    rng = np.random.default_rng(7)
+    N = sum(lens)
+    kk = O.bf16_round(rng.standard_normal((N, 2, 2, 8)))
+    vv = O.bf16_round(rng.standard_normal((N, 2, 2, 8)))
+    c = O.OracleCache(2, 2, 8, 1e4)
+    owner = _apply_request(c, lens, g["cache_ops"], kk, vv)
+    s = c.seqs[0]
+    surv = [t for t in range(N) if owner[t] in g["expect_surviving_messages"]]
+    assert list(s.token_ids) == surv
+    r = len(surv)
+    assert r == N - lens[2]
+    assert list(s.pos) == list(range(r)) and s.next_pos == r
+    # messages 0,1 keep K bit-exactly; messages 3,4 moved down by len(msg 2)
+    n01 = lens[0] + lens[1]
+    assert np.array_equal(s.k[:n01], kk[:n01])
+    th = O.rope_theta(8, 1e4)
+    want = O.bf16_round(O.rotate_pairs(kk[n01 + lens[2]:], -lens[2], th))
+    assert np.array_equal(s.k[n01:], want)
+    assert np.array_equal(s.v, vv[surv])
+    # the next append goes to position r
+    c.append(0, [N], np.zeros((1, 2, 2, 8)), np.zeros((1, 2, 2, 8)))
+    assert s.pos[-1] == r
+
+
+def test_drop_then_reposition_order():
+    """At one boundary drop runs before reposition: the survivors end at 0..r-1."""
+    c, _, _ = _filled_cache(6)
+    mask = np.array([0, 1, 0, 1, 0, 0], np.uint8)
+    src, delta = c.drop_reposition(0, mask)
+    assert list(src) == [0, 2, 4, 5]
+    assert list(delta) == [0, -1, -2, -2]
+    assert list(c.seqs[0].pos) == [0, 1, 2, 3] and c.seqs[0].next_pos == 4
+
+
+# ---------------------------------------------------------------------------
+# decode attention
+# ---------------------------------------------------------------------------
+def test_attention_closed_forms():
+    rng = np.random.default_rng(8)
+    d = 16
+    k = rng.standard_normal((9, d))
+    v = rng.standard_normal((9, d))
+    q = rng.standard_normal(d)
+    assert np.array_equal(O.attend(q, k[:1], v[:1]), v[0])              # one key: weight 1
+    np.testing.assert_allclose(O.attend(np.zeros(d), k, v), v.mean(0), rtol=0, atol=1e-15)
+    same = np.repeat(k[:1], 9, axis=0)
+    np.testing.assert_allclose(O.attend(q, same, v), v.mean(0), rtol=0, atol=1e-15)
+    assert not O.attend(q, k[:0], v[:0]).any()                         # empty: zeros
+    # a huge score selects its value
+    kk = k.copy(); kk[3] = 50.0 * q / np.linalg.norm(q)
+    np.testing.assert_allclose(O.attend(q * 10, kk, v), v[3], atol=1e-12)
+
+
+def test_attention_matches_torch_sdpa_gqa():
+    import torch
+    rng = np.random.default_rng(9)
+    L, Hkv, G, d, n = 2, 2, 4, 32, 37
+    c = O.OracleCache(L, Hkv, d, 1e4)
+    k = O.bf16_round(rng.standard_normal((n, L, Hkv, d)))
+    v = O.bf16_round(rng.standard_normal((n, L, Hkv, d)))
+    c.append(0, np.arange(n), k, v)
+    q = O.bf16_round(rng.standard_normal((L, Hkv * G, d)))
+    got = c.decode_attention(0, q, active_len=29)
+    for l in range(L):
+        kt = torch.from_numpy(k[:29, l]).permute(1, 0, 2).repeat_interleave(G, 0)  # [Hq, n, d]
+        vt = torch.from_numpy(v[:29, l]).permute(1, 0, 2).repeat_interleave(G, 0)
+        qt = torch.from_numpy(q[l])[:, None, :]                                    # [Hq, 1, d]
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt)[:, 0]
+        np.testing.assert_allclose(got[l], ref.numpy(), atol=1e-12)
+
+
+def test_drop_then_attend_equals_subset_attention():
+    rng = np.random.default_rng(10)
+    L, Hkv, d, n = 1, 2, 16, 30
+    c = O.OracleCache(L, Hkv, d, 1e4)
+    k = O.bf16_round(rng.standard_normal((n, L, Hkv, d)))
+    v = O.bf16_round(rng.standard_normal((n, L, Hkv, d)))
+    c.append(0, np.arange(n), k, v)
+    mask = (rng.uniform(size=n) < 0.4).astype(np.uint8)
+    q = O.bf16_round(rng.standard_normal((L, 4, d)))
+    c.drop(0, mask)
+    got = c.decode_attention(0, q)
+    keep = np.flatnonzero(mask == 0)
+    for h in range(4):
+        want = O.attend(q[0, h], k[keep, 0, h // 2], v[keep, 0, h // 2])
+        assert np.array_equal(got[0, h], want)
+
+
+# ---------------------------------------------------------------------------
+# replay (eq. 6)
+# ---------------------------------------------------------------------------
+def test_replay_is_deterministic_and_metadata_only_agrees():
+    from agent_kv_cache_amd.workloads import c4_history, mask_for_messages
+    h = c4_history(turns=12, total=900, assistant_range=(8, 40), tool_range=(16, 120))
+
+    def run(with_kv):
+        c = O.OracleCache(1, 1, 4, 1.5e5, with_kv=with_kv)
+        rng = np.random.default_rng(11)
+        ops = []
+        for op in h.ops:
+            s = c.seqs[0]
+            if op[0] == "append":
+                mid, n = op[1], op[2]
+                tid = np.arange(h.msg_start[mid], h.msg_start[mid] + n)
+                kv = (O.bf16_round(rng.standard_normal((n, 1, 1, 4))),
+                      O.bf16_round(rng.standard_normal((n, 1, 1, 4)))) if with_kv else ()
+                ops.append(("append", 0, tid) + kv)
+            else:
+                mask = mask_for_messages(s.token_ids, h, op[1]) if op[0] != "repos" else None
+                ops.append(("drop", 0, mask) if op[0] == "drop" else
+                           ("repos", 0, None) if op[0] == "repos" else
+                           ("drop_repos", 0, mask, None))
+            O.replay(c, ops[-1:])
+        return c, ops
+
+    c1, ops = run(True)
+    c2 = O.replay(O.OracleCache(1, 1, 4, 1.5e5), ops)
+    c3, _ = run(False)
+    a, b, m = c1.seqs[0], c2.seqs[0], c3.seqs[0]
+    assert np.array_equal(a.token_ids, b.token_ids) and np.array_equal(a.k, b.k)
+    assert np.array_equal(a.token_ids, m.token_ids) and np.array_equal(a.pos, m.pos)
+    assert a.next_pos == m.next_pos
+    # with keep_turns = 3 only the last three tool responses survive
+    tools = {mid for mid in range(1, 24, 2)}
+    live = {mid for mid in tools if np.any(mask_for_messages(a.token_ids, h, [mid]))}
+    assert live == {19, 21, 23}
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes: the pins above must fail on plausible oracle bugs
+# ---------------------------------------------------------------------------
+def _rot_wrong_sign(k, delta, theta):
+    half = k.shape[-1] // 2
+    ang = np.asarray(delta, np.float64)[..., None] * theta
+    c, s = np.cos(ang), np.sin(ang)
+    x, y = k[..., :half], k[..., half:]
+    return np.concatenate([x * c + y * s, y * c - x * s], axis=-1)
+
+
+def _rot_adjacent_pairs(k, delta, theta):
+    x, y = k[..., 0::2], k[..., 1::2]
+    ang = np.asarray(delta, np.float64)[..., None] * theta
+    c, s = np.cos(ang), np.sin(ang)
+    out = np.empty_like(k)
+    out[..., 0::2] = x * c - y * s
+    out[..., 1::2] = y * c + x * s
+    return out
+
+
+def _theta_off_by_one(d, base):
+    i = np.arange(1, d // 2 + 1, dtype=np.float64)
+    return np.power(base, -2.0 * i / d)
+
+
+def _bf16_via_fp32(x):
+    import torch
+    return torch.from_numpy(np.asarray(x, np.float64).astype(np.float32)).to(
+        torch.bfloat16).to(torch.float64).numpy()
+
+
+def test_planted_mistakes_are_caught(monkeypatch):
+    d = 128
+    th = O.rope_theta(d, 5e5)
+    ex = np.zeros(d); ex[0] = 1.0
+    # wrong rotation sign: the unit-vector pin fails
+    r = _rot_wrong_sign(ex, 5, th)
+    assert not (r[0] == np.cos(5.0) and r[d // 2] == np.sin(5.0))
+    # adjacent (GPT-J style) pairing: the unit-vector pin fails
+    r = _rot_adjacent_pairs(ex, 5, th)
+    assert r[d // 2] != np.sin(5.0)
+    # theta index off by one: theta_0 pin fails
+    assert _theta_off_by_one(d, 5e5)[0] != 1.0
+    # fp32 double rounding: the one-step tie pin fails
+    assert _bf16_via_fp32(1 + 2**-8 + 2**-40) != 1 + 2**-7
+    # drop that lowers next_pos (a plausible misreading of eq. 4): Fig. 10 fails
+    orig = O.OracleCache.drop
+
+    def drop_lowering(self, b, mask):
+        src = orig(self, b, mask)
+        self.seqs[b].next_pos = len(self.seqs[b])
+        return src
+
+    monkeypatch.setattr(O.OracleCache, "drop", drop_lowering)
+    with pytest.raises(AssertionError):
+        test_fig10_walkthrough()
+    monkeypatch.setattr(O.OracleCache, "drop", orig)
+    # reposition that also rotates V: the five-message pin fails
+    orig_rep = O.OracleCache.reposition
+
+    def rep_rotating_v(self, b, new_pos=None):
+        s = self.seqs[b]
+        old = s.pos.copy()
+        delta = orig_rep(self, b, new_pos)
+        if self.with_kv:
+            s.v = O.rerotate_keys(s.v, s.pos - old, self.theta)
+        return delta
+
+    monkeypatch.setattr(O.OracleCache, "reposition", rep_rotating_v)
+    with pytest.raises(AssertionError):
+        test_five_message_example((3, 2, 5, 2, 4))
+    monkeypatch.setattr(O.OracleCache, "reposition", orig_rep)
+    # attention scaled by 1/d instead of 1/sqrt(d): the SDPA pin fails
+    orig_att = O.attend
+
+    def attend_bad_scale(q, k, v):
+        return orig_att(q / np.sqrt(q.shape[-1]), k, v)
+
+    monkeypatch.setattr(O, "attend", attend_bad_scale)
+    with pytest.raises(AssertionError):
+        test_attention_matches_torch_sdpa_gqa()
