@@ -1,0 +1,230 @@
+"""ctypes binding of libakv.so (include/akv.h) -- argument marshalling only.
+
+Every step of the hot path runs in the HIP kernels behind the C ABI; PyTorch
+only provides device memory and the current stream.  There is no CPU
+fallback: if libakv.so is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import re
+from typing import Optional
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libakv.so")
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "akv.h")
+
+STATUS = {0: "AKV_OK", 1: "AKV_ERR_ARG", 2: "AKV_ERR_ORDER", 3: "AKV_ERR_POS_MISMATCH",
+          4: "AKV_ERR_NO_BLOCKS", 5: "AKV_ERR_CAPACITY", 6: "AKV_ERR_HIP"}
+KERNELS = {"plan": 0, "move": 1, "commit": 2, "attn": 3, "combine": 4, "append": 5}
+PAGE = 16
+
+
+class AkvError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {STATUS.get(code, code)}")
+        self.code = code
+
+
+class AkvCacheDesc(C.Structure):
+    _fields_ = [
+        ("n_layers", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
+        ("block_size", C.c_int32), ("n_blocks", C.c_int32), ("n_seqs", C.c_int32),
+        ("max_blocks_per_seq", C.c_int32), ("rope_base", C.c_double),
+        ("k_pool", C.c_void_p), ("v_pool", C.c_void_p), ("block_table", C.c_void_p),
+        ("seq_lens", C.c_void_p), ("next_pos", C.c_void_p), ("positions", C.c_void_p),
+        ("token_ids", C.c_void_p), ("free_stack", C.c_void_p), ("free_count", C.c_void_p),
+        ("scratch", C.c_void_p), ("scratch_bytes", C.c_size_t),
+    ]
+
+
+_lib = None
+_P = C.c_void_p
+
+
+def lib() -> C.CDLL:
+    """Load libakv.so once; raise loudly when it is not there."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                           "or python -m agent_kv_cache_amd.build")
+    L = C.CDLL(LIB_PATH)
+    sig = {
+        "akv_scratch_bytes": (C.c_size_t, [C.POINTER(AkvCacheDesc)]),
+        "akv_cache_init": (C.c_int, [C.POINTER(AkvCacheDesc), C.POINTER(_P)]),
+        "akv_cache_free": (None, [_P]),
+        "akv_cache_reset": (C.c_int, [_P, _P, _P]),
+        "akv_append": (C.c_int, [_P, _P, C.c_int64, _P, _P, _P, _P]),
+        "akv_drop": (C.c_int, [_P, _P, _P]),
+        "akv_reposition": (C.c_int, [_P, _P, _P, _P]),
+        "akv_drop_reposition": (C.c_int, [_P, _P, _P, _P]),
+        "akv_decode_workspace_bytes": (C.c_size_t, [_P, C.c_int32, C.c_int32]),
+        "akv_decode_attention": (C.c_int, [_P, _P, _P, C.c_int32, C.c_int32, C.c_int32, _P,
+                                           _P, C.c_size_t, _P]),
+        "akv_sync_status": (C.c_int, [_P, _P]),
+        "akv_status_string": (C.c_char_p, [C.c_int]),
+        "akv_profile_enable": (C.c_int, [_P, C.c_int]),
+        "akv_profile_read": (C.c_int, [_P, C.c_int, C.POINTER(C.c_double),
+                                       C.POINTER(C.c_int64), C.c_int]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = L
+    return L
+
+
+def header_functions() -> list:
+    """Names of the functions include/akv.h declares."""
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(akv_[a-z_]+)\s*\(", txt)))
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _check(code: int, what: str):
+    if code != 0:
+        raise AkvError(code, what)
+
+
+class AkvCache:
+    """A paged bf16 KV cache in device memory plus its libakv handle.
+
+    Tensors (all on `device`, owned here):
+      k_pool, v_pool : bf16 [L][NB][Hkv][16][d]
+      positions, token_ids : int32 [NB][16]
+      meta : int32 buffer holding block_table [B][maxpg], seq_lens [B],
+             next_pos [B], free_count [1] and free_stack [NB] as views, so the
+             whole per-sequence state can be snapshotted with one copy.
+    """
+
+    def __init__(self, n_layers: int, n_kv_heads: int, head_dim: int, n_blocks: int,
+                 n_seqs: int, max_blocks_per_seq: int, rope_base: float,
+                 device: str = "cuda"):
+        import torch
+        self.L, self.H, self.D = n_layers, n_kv_heads, head_dim
+        self.NB, self.B, self.maxpg = n_blocks, n_seqs, max_blocks_per_seq
+        self.S = max_blocks_per_seq * PAGE
+        self.rope_base = float(rope_base)
+        self.device = torch.device(device)
+        shape = (n_layers, n_blocks, n_kv_heads, PAGE, head_dim)
+        self.k_pool = torch.empty(shape, dtype=torch.bfloat16, device=self.device)
+        self.v_pool = torch.empty(shape, dtype=torch.bfloat16, device=self.device)
+        self.positions = torch.empty((n_blocks, PAGE), dtype=torch.int32, device=self.device)
+        self.token_ids = torch.empty((n_blocks, PAGE), dtype=torch.int32, device=self.device)
+        nt = n_seqs * max_blocks_per_seq
+        self._o_lens = nt
+        self._o_next = nt + n_seqs
+        self._o_fc = nt + 2 * n_seqs
+        self._o_fs = self._o_fc + 4
+        self.meta = torch.zeros(self._o_fs + n_blocks, dtype=torch.int32, device=self.device)
+        self.block_table = self.meta[:nt].view(n_seqs, max_blocks_per_seq)
+        self.seq_lens = self.meta[self._o_lens:self._o_lens + n_seqs]
+        self.next_pos = self.meta[self._o_next:self._o_next + n_seqs]
+        self.free_count = self.meta[self._o_fc:self._o_fc + 1]
+        self.free_stack = self.meta[self._o_fs:]
+        desc = AkvCacheDesc(n_layers, n_kv_heads, head_dim, PAGE, n_blocks, n_seqs,
+                            max_blocks_per_seq, self.rope_base)
+        nbytes = lib().akv_scratch_bytes(C.byref(desc))
+        if nbytes == 0:
+            raise AkvError(1, "akv_scratch_bytes")
+        self.scratch = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        for f, t in (("k_pool", self.k_pool), ("v_pool", self.v_pool),
+                     ("block_table", self.block_table), ("seq_lens", self.seq_lens),
+                     ("next_pos", self.next_pos), ("positions", self.positions),
+                     ("token_ids", self.token_ids), ("free_stack", self.free_stack),
+                     ("free_count", self.free_count), ("scratch", self.scratch)):
+            setattr(desc, f, t.data_ptr())
+        desc.scratch_bytes = nbytes
+        self.desc = desc
+        h = _P()
+        _check(lib().akv_cache_init(C.byref(desc), C.byref(h)), "akv_cache_init")
+        self.handle = h
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and _lib is not None:
+            _lib.akv_cache_free(h)
+            self.handle = None
+
+    # -- ops ---------------------------------------------------------------
+    def reset(self, page_order=None, stream=None):
+        arr = None
+        if page_order is not None:
+            import numpy as np
+            po = np.ascontiguousarray(page_order, dtype=np.int32)
+            arr = po.ctypes.data_as(_P)
+        _check(lib().akv_cache_reset(self.handle, arr, _stream(stream)), "akv_cache_reset")
+
+    def append(self, counts, n_new: int, k_new=None, v_new=None, token_ids=None, stream=None):
+        _check(lib().akv_append(self.handle, _ptr(counts), int(n_new), _ptr(k_new), _ptr(v_new),
+                                _ptr(token_ids), _stream(stream)), "akv_append")
+
+    def drop(self, drop_mask, stream=None):
+        _check(lib().akv_drop(self.handle, _ptr(drop_mask), _stream(stream)), "akv_drop")
+
+    def reposition(self, old_pos=None, new_pos=None, stream=None):
+        _check(lib().akv_reposition(self.handle, _ptr(old_pos), _ptr(new_pos), _stream(stream)),
+               "akv_reposition")
+
+    def drop_reposition(self, drop_mask, new_pos=None, stream=None):
+        _check(lib().akv_drop_reposition(self.handle, _ptr(drop_mask), _ptr(new_pos),
+                                         _stream(stream)), "akv_drop_reposition")
+
+    def decode_workspace_bytes(self, n_layers: int, n_q_heads: int) -> int:
+        return int(lib().akv_decode_workspace_bytes(self.handle, n_layers, n_q_heads))
+
+    def decode_attention(self, q, out, workspace, active_len=None, layer_begin: int = 0,
+                         n_layers: Optional[int] = None, stream=None):
+        nL = self.L - layer_begin if n_layers is None else n_layers
+        Hq = q.shape[-2]
+        _check(lib().akv_decode_attention(self.handle, _ptr(q), _ptr(active_len), layer_begin,
+                                          nL, Hq, _ptr(out), _ptr(workspace),
+                                          workspace.numel() * workspace.element_size()
+                                          if workspace is not None else 0, _stream(stream)),
+               "akv_decode_attention")
+
+    def sync_status(self, stream=None) -> int:
+        return int(lib().akv_sync_status(self.handle, _stream(stream)))
+
+    def profile_enable(self, on: bool = True):
+        _check(lib().akv_profile_enable(self.handle, int(on)), "akv_profile_enable")
+
+    def profile_read(self, kernel: str, reset: bool = False):
+        ms, n = C.c_double(), C.c_int64()
+        _check(lib().akv_profile_read(self.handle, KERNELS[kernel], C.byref(ms), C.byref(n),
+                                      int(reset)), "akv_profile_read")
+        return ms.value, n.value
+
+    # -- state export (for checks; plain tensor reads) ----------------------
+    def seq_state(self, b: int):
+        """(token_ids, positions, page ids) of sequence b's active entries, on the host."""
+        import numpy as np
+        n = int(self.seq_lens[b].item())
+        npg = (n + PAGE - 1) // PAGE
+        pages = self.block_table[b, :npg].cpu().numpy()
+        tok = self.token_ids[self.block_table[b, :npg].long()].reshape(-1)[:n].cpu().numpy()
+        pos = self.positions[self.block_table[b, :npg].long()].reshape(-1)[:n].cpu().numpy()
+        return tok.astype(np.int64), pos.astype(np.int64), pages
+
+    def gather_rows(self, b: int, layer: int, which: str = "k"):
+        """bf16 rows [n, Hkv, d] of sequence b at `layer`, in active order (device tensor)."""
+        n = int(self.seq_lens[b].item())
+        npg = (n + PAGE - 1) // PAGE
+        pool = self.k_pool if which == "k" else self.v_pool
+        pages = self.block_table[b, :npg].long()
+        rows = pool[layer, pages]                      # [npg, H, 16, d]
+        return rows.permute(0, 2, 1, 3).reshape(npg * PAGE, self.H, self.D)[:n]

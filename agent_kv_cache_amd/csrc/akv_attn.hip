@@ -1,0 +1,242 @@
+// Split-K GQA decode attention over the active KV, for gfx950.
+//
+// o = softmax(q K^T / sqrt(d)) V over the first active_len entries of each
+// sequence (the active cache of [CE] sec. 3.1/3.3: dropped entries are no
+// longer present after compaction, so only surviving KV is read).
+//
+// Grid (split, kv head, sequence*layer); 4 waves per workgroup, wave w takes
+// pages w, w+4, ... of the split.  Per 16-token page a wave
+//   - loads K straight into MFMA A-operand registers (lane = token row,
+//     16-B loads) and computes S^T[16 tok x 16 q-head] with
+//     v_mfma_f32_16x16x32_bf16 (the GQA group is padded to 16 columns),
+//   - does the online softmax in the MFMA output layout (4 tokens per lane,
+//     row max/sum with two cross-lane xor shuffles),
+//   - stages the V page in its own LDS slice and reads it transposed as the
+//     A operand of v_mfma_f32_16x16x16_bf16, whose B operand P^T is exactly
+//     the softmax output already held by the lane (no shuffles).
+// The next page's K and V are loaded before the current one is consumed.
+// Waves merge through LDS; with several splits the partial (m, l, O) go to
+// the workspace and a combine kernel merges them (log-sum-exp in base 2).
+#include "akv_internal.h"
+
+#include <math.h>
+
+namespace akv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kAttnWaves = 4;
+
+__device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t *p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(p));
+}
+
+__device__ __forceinline__ short f32_to_bf16_bits(float x) {
+  return __builtin_bit_cast(short, (__bf16)x);
+}
+
+template <int D>
+__global__ __launch_bounds__(kAttnWaves * 64) void attn_kernel(
+    Dev d, const uint16_t *__restrict__ q, const int32_t *__restrict__ active_len, int l0,
+    int nL, int Hq, uint16_t *__restrict__ out, float *__restrict__ part, int nsplit) {
+  constexpr int KC = D / 32;      // QK MFMA steps (K = 32 of d each)
+  constexpr int NT = D / 16;      // PV output tiles of 16 dims
+  constexpr int VC = D / 32;      // 16-B V chunks per lane per page
+  constexpr int C8 = D / 8;       // 16-B chunks per row
+  constexpr int VROW = D + 8;     // padded LDS row, elements
+  __shared__ __attribute__((aligned(16))) uint16_t s_v[kAttnWaves][kPage][VROW];
+  __shared__ float s_m[kAttnWaves][16], s_l[kAttnWaves][16];
+  __shared__ float s_o[kAttnWaves][16][D];
+
+  const int s = blockIdx.x, g = blockIdx.y, bl = blockIdx.z;
+  const int b = bl / nL, li = bl - b * nL, l = l0 + li;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int hh = lane & 15, kg = lane >> 4;
+  const int G = Hq / d.H;
+
+  const int seqlen = d.lens[b];
+  int len = active_len ? active_len[b] : seqlen;
+  if (len < 0 || len > seqlen) {
+    if (threadIdx.x == 0 && s == 0 && g == 0) atomicCAS(&d.ctl[CTL_ERR], 0, (int)AKV_ERR_ARG);
+    len = len < 0 ? 0 : seqlen;
+  }
+  const int P = (len + kPage - 1) / kPage;
+  const int chunk = (P + nsplit - 1) / nsplit;
+  const int p0 = s * chunk, p1 = min(P, p0 + chunk);
+
+  // Query rows as the B operand: column hh = query head g*G + hh.
+  bf16x8 qb[KC];
+  {
+    const uint16_t *qrow = q + (((size_t)b * nL + li) * Hq + (size_t)g * G + hh) * D;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      if (hh < G) qb[c] = load_bf16x8(qrow + 8 * kg + 32 * c);
+      else qb[c] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+    }
+  }
+
+  const float scale = 1.4426950408889634f / sqrtf((float)D);  // log2(e)/sqrt(d)
+  float m = -INFINITY, lsum = 0.f;
+  floatx4 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const int32_t *trow = d.table + (size_t)b * d.maxpg;
+  const size_t hstride = (size_t)kPage * D;
+  const size_t head_base = ((size_t)l * d.NB * d.H + g) * hstride;
+  const size_t page_stride = (size_t)d.H * hstride;
+
+  bf16x8 ka[KC];
+  uint4 vv[VC];
+  int p = p0 + wave;
+  if (p < p1) {
+    const size_t off = head_base + (size_t)trow[p] * page_stride;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) ka[c] = load_bf16x8(d.k + off + hh * D + 8 * kg + 32 * c);
+#pragma unroll
+    for (int c = 0; c < VC; ++c) vv[c] = *reinterpret_cast<const uint4 *>(d.v + off + 8 * (lane + 64 * c));
+  }
+  while (p < p1) {
+    const int pn = p + kAttnWaves;
+    bf16x8 kan[KC];
+    uint4 vvn[VC];
+    if (pn < p1) {
+      const size_t off = head_base + (size_t)trow[pn] * page_stride;
+#pragma unroll
+      for (int c = 0; c < KC; ++c) kan[c] = load_bf16x8(d.k + off + hh * D + 8 * kg + 32 * c);
+#pragma unroll
+      for (int c = 0; c < VC; ++c) vvn[c] = *reinterpret_cast<const uint4 *>(d.v + off + 8 * (lane + 64 * c));
+    }
+    // S^T[token 4*kg + j][head hh]
+    floatx4 sacc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < KC; ++c) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[c], qb[c], sacc, 0, 0, 0);
+    const int tok0 = p * kPage + 4 * kg;
+    float sv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sv[j] = (tok0 + j < len) ? sacc[j] * scale : -INFINITY;
+    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mnew = fmaxf(m, mx);
+    const float alpha = exp2f(m - mnew);
+    float pj[4], ps = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      pj[j] = exp2f(sv[j] - mnew);
+      ps += pj[j];
+    }
+    lsum = lsum * alpha + ps;
+    m = mnew;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] *= alpha;
+    // stage V (rows past the active length are zeroed: never multiply junk)
+#pragma unroll
+    for (int c = 0; c < VC; ++c) {
+      const int ci = lane + 64 * c, row = ci / C8, col = (ci % C8) * 8;
+      uint4 v = vv[c];
+      if (p * kPage + row >= len) v = make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4 *>(&s_v[wave][row][col]) = v;
+    }
+    const short4v pb = short4v{f32_to_bf16_bits(pj[0]), f32_to_bf16_bits(pj[1]),
+                               f32_to_bf16_bits(pj[2]), f32_to_bf16_bits(pj[3])};
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int col = 16 * t + hh;
+      const short4v va = short4v{(short)s_v[wave][4 * kg + 0][col], (short)s_v[wave][4 * kg + 1][col],
+                                 (short)s_v[wave][4 * kg + 2][col], (short)s_v[wave][4 * kg + 3][col]};
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, acc[t], 0, 0, 0);
+    }
+#pragma unroll
+    for (int c = 0; c < KC; ++c) ka[c] = kan[c];
+#pragma unroll
+    for (int c = 0; c < VC; ++c) vv[c] = vvn[c];
+    p = pn;
+  }
+
+  // ---- merge the four waves ----
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  if (kg == 0) {
+    s_m[wave][hh] = m;
+    s_l[wave][hh] = lsum;
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s_o[wave][hh][16 * t + 4 * kg + j] = acc[t][j];
+  __syncthreads();
+  const size_t row0 = ((size_t)b * nL + li) * Hq + (size_t)g * G;
+  for (int e = threadIdx.x; e < G * D; e += kAttnWaves * 64) {
+    const int h = e / D, dim = e - h * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, s_m[w][h]);
+    float L = 0.f, o = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kAttnWaves; ++w) {
+        const float f = exp2f(s_m[w][h] - M);
+        L += f * s_l[w][h];
+        o += f * s_o[w][h][dim];
+      }
+    }
+    if (nsplit == 1) {
+      out[(row0 + h) * D + dim] = (uint16_t)f32_to_bf16_bits(L > 0.f ? o / L : 0.f);
+    } else {
+      float *pr = part + ((row0 + h) * nsplit + s) * (size_t)(D + 2);
+      if (dim == 0) {
+        pr[0] = M;
+        pr[1] = L;
+      }
+      pr[2 + dim] = o;
+    }
+  }
+}
+
+// Merge split partials of one (sequence, layer, query head) row.
+template <int D>
+__global__ __launch_bounds__(D) void combine_kernel(const float *__restrict__ part,
+                                                    uint16_t *__restrict__ out, int nsplit) {
+  const size_t row = blockIdx.x;
+  const int dim = threadIdx.x;
+  const float *pr = part + row * nsplit * (size_t)(D + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pr[s * (D + 2)]);
+  float L = 0.f, o = 0.f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < nsplit; ++s) {
+      const float *ps = pr + s * (D + 2);
+      const float f = exp2f(ps[0] - M);
+      L += f * ps[1];
+      o += f * ps[2 + dim];
+    }
+  }
+  out[row * D + dim] = (uint16_t)f32_to_bf16_bits(L > 0.f ? o / L : 0.f);
+}
+
+hipError_t launch_attention(const Dev &d, const uint16_t *q, const int32_t *active_len, int l0,
+                            int nL, int Hq, uint16_t *out, float *part, int nsplit,
+                            hipStream_t st) {
+  const dim3 grid(nsplit, d.H, d.B * nL), block(kAttnWaves * 64);
+  if (d.D == 128)
+    hipLaunchKernelGGL(attn_kernel<128>, grid, block, 0, st, d, q, active_len, l0, nL, Hq, out,
+                       part, nsplit);
+  else
+    hipLaunchKernelGGL(attn_kernel<64>, grid, block, 0, st, d, q, active_len, l0, nL, Hq, out,
+                       part, nsplit);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const float *part, uint16_t *out, int rows, int nsplit, int D,
+                          hipStream_t st) {
+  if (D == 128)
+    hipLaunchKernelGGL(combine_kernel<128>, dim3(rows), dim3(128), 0, st, part, out, nsplit);
+  else
+    hipLaunchKernelGGL(combine_kernel<64>, dim3(rows), dim3(64), 0, st, part, out, nsplit);
+  return hipGetLastError();
+}
+
+}  // namespace akv

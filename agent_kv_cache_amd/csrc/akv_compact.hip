@@ -1,0 +1,628 @@
+// Drop / reposition / append kernels of libakv for gfx950.
+//
+// [CE] = review of "Cache Engineering for Agents", sec. 3.3 eqs. (3)-(5);
+// [AKV] = "[Repo Review] AKV", sec. 1 (drop then reposition), sec. 5.5
+// (reposition kernel: un-rotate at p / rotate to q, copy when p == q, V is
+// copied and never rotated, writes go to a separate destination slot).
+//
+// One drop / reposition runs as three stream-ordered kernels:
+//   plan   : one workgroup per sequence scans the keep flags page by page
+//            (16 mask bytes per thread, one 16-B load), builds the gather map
+//            src[j] and the per-survivor rotation delta q - p, and finds the
+//            first dropped slot and the first changed position.  The last
+//            workgroup to finish (ticket counter) takes exclusive prefix sums
+//            over sequences, checks the free pool and latches errors.
+//   move   : a persistent grid walks (layer chunk, output page) items.  Pages
+//            from the first dropped page on are rebuilt out of place in fresh
+//            pages (K re-rotated when its delta is non-zero, V copied bitwise);
+//            pages before it whose positions change are re-rotated in place.
+//            16-B loads/stores, one (row, 8 NeoX pairs) per thread.
+//   commit : new page-table entries, freed pages back on the free stack,
+//            lengths and next positions.
+#include "akv_internal.h"
+
+#include <climits>
+
+namespace akv {
+
+constexpr int kPlanThreads = 1024;
+constexpr int kMoveThreads = 256;
+
+// ---------------------------------------------------------------------------
+// helpers
+// ---------------------------------------------------------------------------
+// Exclusive block-wide prefix sum of one int per thread.  `wave_tmp` holds
+// NT/64 + 1 ints of LDS.  Returns the exclusive prefix; *total gets the sum.
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan(int x, int *wave_tmp, int *total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  int v = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(v, o, 64);
+    if (lane >= o) v += y;
+  }
+  if (lane == 63) wave_tmp[wid] = v;
+  __syncthreads();
+  if (wid == 0) {
+    int w = (lane < NT / 64) ? wave_tmp[lane] : 0;
+    int s = w;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      int y = __shfl_up(s, o, 64);
+      if (lane >= o) s += y;
+    }
+    if (lane < NT / 64) wave_tmp[lane] = s - w;
+    if (lane == NT / 64 - 1) wave_tmp[NT / 64] = s;
+  }
+  __syncthreads();
+  const int res = v - x + wave_tmp[wid];
+  *total = wave_tmp[NT / 64];
+  __syncthreads();
+  return res;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 r;
+  r.x = (__bf16)a;
+  r.y = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// fp64 -> fp32 such that a following fp32 -> bf16 round-to-nearest-even gives
+// the correctly rounded bf16 of x (one rounding).  A double rounding error can
+// only occur when the fp32 value sits exactly on a bf16 halfway point
+// (low 16 bits 0x8000) while x is not that value; then the fp32 value is
+// nudged one fp32 step towards x, which breaks the tie the right way.
+__device__ __forceinline__ float f64_to_f32_for_bf16(double x) {
+  float f = (float)x;
+  uint32_t u = __float_as_uint(f);
+  if (__builtin_expect((u & 0xFFFFu) == 0x8000u, 0)) {
+    double back = (double)f;
+    if (back != x) u += (fabs(x) > fabs(back)) ? 1u : 0xFFFFFFFFu;
+  }
+  return __uint_as_float(u);
+}
+
+// ---------------------------------------------------------------------------
+// plan
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(
+    Dev d, const uint8_t *__restrict__ mask, const int32_t *__restrict__ new_pos,
+    const int32_t *__restrict__ old_pos, int mode, int move_grid) {
+  __shared__ int s_wave[kPlanThreads / 64 + 1];
+  __shared__ int s_fdrop, s_fpos, s_err, s_last, s_gerr;
+  const int b = blockIdx.x, t = threadIdx.x;
+  const size_t S = (size_t)d.S;
+  const int len = d.lens[b];
+  const int P = (len + kPage - 1) / kPage;
+  if (t == 0) {
+    s_fdrop = len;
+    s_fpos = INT_MAX;
+    s_err = 0;
+  }
+  __syncthreads();
+  const int32_t *trow = d.table + (size_t)b * d.maxpg;
+  int running = 0, err = 0, fpos = INT_MAX;
+  for (int base = 0; base < P; base += kPlanThreads) {
+    const int pg = base + t;
+    unsigned keep = 0;
+    if (pg < P) {
+      const int nvalid = min(kPage, len - pg * kPage);
+      const unsigned valid = (nvalid == kPage) ? 0xFFFFu : ((1u << nvalid) - 1u);
+      keep = valid;
+      if (mode & M_DROP) {
+        const uint4 m = *reinterpret_cast<const uint4 *>(mask + b * S + (size_t)pg * kPage);
+        const uint32_t w[4] = {m.x, m.y, m.z, m.w};
+        unsigned dropbits = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            dropbits |= (((w[q] >> (8 * e)) & 0xFFu) != 0u) << (4 * q + e);
+        dropbits &= valid;
+        keep = valid & ~dropbits;
+        if (dropbits) atomicMin(&s_fdrop, pg * kPage + __ffs(dropbits) - 1);
+      }
+    }
+    int total;
+    const int excl = block_exclusive_scan<kPlanThreads>(__popc(keep), s_wave, &total);
+    if (keep) {
+      int j = running + excl;
+      const int32_t *prow = d.pos + (size_t)trow[pg] * kPage;
+      for (int r = 0; r < kPage; ++r) {
+        if (!((keep >> r) & 1u)) continue;
+        const int s = pg * kPage + r;
+        if (mode & M_DROP) d.src_map[b * S + j] = s;
+        if (mode & M_REPOS) {
+          const int p = prow[r];
+          if ((mode & M_OLDPOS) && old_pos[b * S + s] != p) err = max(err, (int)AKV_ERR_POS_MISMATCH);
+          int q = j;
+          if (mode & M_NEWPOS) {
+            q = new_pos[b * S + j];
+            if (q < 0 || (j > 0 && new_pos[b * S + j - 1] >= q)) err = max(err, (int)AKV_ERR_ORDER);
+          }
+          const int delta = q - p;
+          d.delta_map[b * S + j] = delta;
+          if (delta != 0 && j < fpos) fpos = j;
+        }
+        ++j;
+      }
+    }
+    running += total;
+  }
+  if (err) atomicMax(&s_err, err);
+  if (fpos != INT_MAX) atomicMin(&s_fpos, fpos);
+  __syncthreads();
+  if (t == 0) {
+    int *si = d.seq_info + (size_t)b * kSeqInfo;
+    const int rnew = running;
+    const int Pn = (rnew + kPage - 1) / kPage;
+    int fbd = P, nmove = 0, nfreed = 0;
+    if ((mode & M_DROP) && s_fdrop < len) {
+      fbd = s_fdrop / kPage;
+      nmove = max(0, Pn - fbd);
+      nfreed = P - fbd;
+    }
+    int fip = P, ninp = 0;
+    int nnext = d.next_pos[b];
+    if (mode & M_REPOS) {
+      if (s_fpos < rnew) {
+        fip = s_fpos / kPage;
+        ninp = max(0, min(fbd, Pn) - fip);
+      }
+      nnext = rnew == 0 ? 0 : ((mode & M_NEWPOS) ? new_pos[b * S + rnew - 1] + 1 : rnew);
+    }
+    si[SI_NEW_LEN] = rnew;
+    si[SI_FBD] = fbd;
+    si[SI_FIP] = fip;
+    si[SI_N_MOVE] = nmove;
+    si[SI_N_INPLACE] = ninp;
+    si[SI_N_FREED] = nfreed;
+    si[SI_NEW_NEXT] = nnext;
+    si[SI_ERR] = s_err;
+    si[SI_OLD_LEN] = len;
+  }
+  // ---- last workgroup: prefix sums over sequences, pool check, latch ----
+  __threadfence();
+  __syncthreads();
+  if (t == 0) s_last = (atomicAdd(&d.ctl[CTL_DONE], 1) == (int)gridDim.x - 1);
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  if (t == 0) s_gerr = 0;
+  __syncthreads();
+  int run_m = 0, run_i = 0, run_f = 0;
+  for (int base = 0; base < d.B; base += kPlanThreads) {
+    const int bb = base + t;
+    int nm = 0, ni = 0, nf = 0, e = 0;
+    int *si = d.seq_info + (size_t)bb * kSeqInfo;
+    if (bb < d.B) {
+      nm = __atomic_load_n(&si[SI_N_MOVE], __ATOMIC_RELAXED);
+      ni = __atomic_load_n(&si[SI_N_INPLACE], __ATOMIC_RELAXED);
+      nf = __atomic_load_n(&si[SI_N_FREED], __ATOMIC_RELAXED);
+      e = __atomic_load_n(&si[SI_ERR], __ATOMIC_RELAXED);
+    }
+    int tm, ti, tf;
+    const int em = block_exclusive_scan<kPlanThreads>(nm, s_wave, &tm);
+    const int ei = block_exclusive_scan<kPlanThreads>(ni, s_wave, &ti);
+    const int ef = block_exclusive_scan<kPlanThreads>(nf, s_wave, &tf);
+    if (bb < d.B) {
+      si[SI_MOVE_OFF] = run_m + em;
+      si[SI_INPLACE_OFF] = run_i + ei;
+      si[SI_FREED_OFF] = run_f + ef;
+    }
+    if (e) atomicMax(&s_gerr, e);
+    run_m += tm;
+    run_i += ti;
+    run_f += tf;
+  }
+  __syncthreads();
+  if (t == 0) {
+    int e = s_gerr;
+    const int fc = *d.free_count;
+    if (!e && run_m > fc) e = AKV_ERR_NO_BLOCKS;
+    const int latched = d.ctl[CTL_ERR];
+    if (e || latched) {
+      if (!latched) d.ctl[CTL_ERR] = e;
+      d.ctl[CTL_OP_OK] = 0;
+      d.ctl[CTL_T_MOVE] = 0;
+      d.ctl[CTL_T_INPLACE] = 0;
+    } else {
+      d.ctl[CTL_OP_OK] = 1;
+      d.ctl[CTL_T_MOVE] = run_m;
+      d.ctl[CTL_T_INPLACE] = run_i;
+      d.ctl[CTL_F_TOTAL] = run_f;
+      d.ctl[CTL_FC_OLD] = fc;
+      d.ctl[CTL_BASE] = fc - run_m;
+      // Layers per move item: as many as keep ~8 items per workgroup of the
+      // persistent grid, so the cos/sin set-up of an item is amortised over
+      // as many (layer, head) slices as the load balance allows.
+      const long long pages = (long long)run_m + run_i;
+      const long long target = 8LL * move_grid;
+      long long lpi = pages > 0 ? (pages * d.L) / target : d.L;
+      lpi = lpi < 1 ? 1 : (lpi > d.L ? d.L : lpi);
+      d.ctl[CTL_LPI] = (int)lpi;
+    }
+    d.ctl[CTL_DONE] = 0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// move / re-rotate
+// ---------------------------------------------------------------------------
+// Rotate 8 NeoX pairs: lo holds x_i (8 bf16), hi holds y_i = k[i + d/2].
+// x' = x cos - y sin, y' = y cos + x sin in fp64, one rounding to bf16.
+__device__ __forceinline__ void rotate8(uint4 &lo, uint4 &hi, const double *c, const double *s) {
+  uint32_t a[4] = {lo.x, lo.y, lo.z, lo.w};
+  uint32_t bb[4] = {hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float xo[2], yo[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const double x = (double)bf16_to_f32((a[q] >> (16 * e)) & 0xFFFFu);
+      const double y = (double)bf16_to_f32((bb[q] >> (16 * e)) & 0xFFFFu);
+      const double cc = c[2 * q + e], ss = s[2 * q + e];
+      xo[e] = f64_to_f32_for_bf16(fma(x, cc, -(y * ss)));
+      yo[e] = f64_to_f32_for_bf16(fma(y, cc, x * ss));
+    }
+    a[q] = f32x2_to_bf16x2(xo[0], xo[1]);
+    bb[q] = f32x2_to_bf16x2(yo[0], yo[1]);
+  }
+  lo = make_uint4(a[0], a[1], a[2], a[3]);
+  hi = make_uint4(bb[0], bb[1], bb[2], bb[3]);
+}
+
+template <int D>
+__global__ __launch_bounds__(kMoveThreads) void move_kernel(Dev d, int mode) {
+  constexpr int HALF = D / 2;
+  constexpr int CH = D / 16;             // 16-B chunks per half row
+  constexpr int TPH = kPage * CH;        // threads per (layer, head) slice
+  constexpr int NS = kMoveThreads / TPH; // slices per pass
+  constexpr int U = 2;                   // slices loaded before any store
+  __shared__ int s_b, s_po, s_dst, s_mv;
+  __shared__ int s_blk[kPage], s_row[kPage], s_valid[kPage], s_delta[kPage], s_rep[kPage];
+  __shared__ int s_repval[kPage], s_nrep;
+  __shared__ double2 s_cs[kPage][HALF];
+
+  if (d.ctl[CTL_OP_OK] == 0) return;
+  const int Tm = d.ctl[CTL_T_MOVE], Ti = d.ctl[CTL_T_INPLACE];
+  const int npages = Tm + Ti;
+  if (npages == 0) return;
+  const int lpi = d.ctl[CTL_LPI];
+  const int fc_old = d.ctl[CTL_FC_OLD];
+  const int nlc = (d.L + lpi - 1) / lpi;
+  const int nitems = npages * nlc;
+  const int t = threadIdx.x;
+  const int r = (t % TPH) / CH, pc = t % CH, slot = t / TPH;
+  const size_t S = (size_t)d.S;
+  const size_t hstride = (size_t)kPage * D;
+  const size_t lstride = (size_t)d.NB * d.H * hstride;
+
+  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+    const int lc = item / npages, pg = item - lc * npages;
+    __syncthreads();  // LDS of the previous item is no longer read
+    if (t == 0) {
+      const bool mv = pg < Tm;
+      const int key = mv ? pg : pg - Tm;
+      const int of = mv ? SI_MOVE_OFF : SI_INPLACE_OFF;
+      int lo = 0, hi = d.B - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (d.seq_info[(size_t)mid * kSeqInfo + of] <= key) lo = mid; else hi = mid - 1;
+      }
+      const int *si = d.seq_info + (size_t)lo * kSeqInfo;
+      const int po = (mv ? si[SI_FBD] : si[SI_FIP]) + (key - si[of]);
+      s_b = lo;
+      s_po = po;
+      s_mv = mv;
+      s_dst = mv ? d.free_stack[fc_old - 1 - pg] : d.table[(size_t)lo * d.maxpg + po];
+      if (mv && lc == 0) d.stage[pg] = s_dst;
+    }
+    __syncthreads();
+    const int b = s_b, po = s_po, dst = s_dst;
+    const bool mv = s_mv;
+    if (t < kPage) {
+      const int rnew = d.seq_info[(size_t)b * kSeqInfo + SI_NEW_LEN];
+      const int j = po * kPage + t;
+      const bool valid = j < rnew;
+      const int i = !valid ? 0 : ((mv && (mode & M_DROP)) ? d.src_map[b * S + j] : j);
+      const int delta = (valid && (mode & M_REPOS)) ? d.delta_map[b * S + j] : 0;
+      const int blk = valid ? d.table[(size_t)b * d.maxpg + (i >> 4)] : 0;
+      s_blk[t] = blk;
+      s_row[t] = i & 15;
+      s_valid[t] = valid;
+      s_delta[t] = delta;
+      if (lc == 0) {
+        const size_t so = (size_t)blk * kPage + (i & 15), dn = (size_t)dst * kPage + t;
+        if (mv) {
+          d.pos[dn] = valid ? d.pos[so] + delta : -1;
+          d.tok[dn] = valid ? d.tok[so] : -1;
+        } else if (valid && delta != 0) {
+          d.pos[dn] += delta;
+        }
+      }
+    }
+    __syncthreads();
+    const bool rot_any = (mode & M_REPOS) != 0;
+    if (rot_any) {
+      if (t == 0) {
+        int n = 0;
+        for (int rr = 0; rr < kPage; ++rr) {
+          const int dl = s_delta[rr];
+          int k = 0;
+          while (k < n && s_repval[k] != dl) ++k;
+          if (k == n) s_repval[n++] = dl;
+          s_rep[rr] = k;
+        }
+        s_nrep = n;
+      }
+      __syncthreads();
+      const int ntask = s_nrep * HALF;
+      for (int task = t; task < ntask; task += kMoveThreads) {
+        const int ri = task / HALF, i = task - ri * HALF;
+        const int dl = s_repval[ri];
+        double sn = 0.0, cs = 1.0;
+        if (dl != 0) sincos((double)dl * d.theta[i], &sn, &cs);
+        s_cs[ri][i] = make_double2(cs, sn);
+      }
+      __syncthreads();
+    }
+    const bool valid = s_valid[r] != 0;
+    const int delta = s_delta[r];
+    double cc[8], ss[8];
+    if (rot_any && delta != 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const double2 v = s_cs[s_rep[r]][8 * pc + e];
+        cc[e] = v.x;
+        ss[e] = v.y;
+      }
+    }
+    const bool do_k = valid ? (mv || delta != 0) : mv;
+    const bool do_v = mv;
+    const int l0 = lc * lpi, l1 = min(d.L, l0 + lpi);
+    const int nsl = (l1 - l0) * d.H;
+    const size_t src_row = (size_t)s_blk[r] * d.H * hstride + (size_t)s_row[r] * D + 8 * pc;
+    const size_t dst_row = (size_t)dst * d.H * hstride + (size_t)r * D + 8 * pc;
+    if (!do_k) continue;
+    for (int i0 = slot; i0 < nsl; i0 += NS * U) {
+      uint4 klo[U], khi[U], vlo[U], vhi[U];
+      size_t dofs[U];
+      bool on[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int idx = i0 + u * NS;
+        on[u] = idx < nsl;
+        const int l = l0 + idx / d.H, h = idx % d.H;
+        const size_t off = (size_t)l * lstride + (size_t)h * hstride;
+        dofs[u] = dst_row + off;
+        klo[u] = khi[u] = vlo[u] = vhi[u] = make_uint4(0, 0, 0, 0);
+        if (on[u] && valid) {
+          const size_t so = src_row + off;
+          klo[u] = *reinterpret_cast<const uint4 *>(d.k + so);
+          khi[u] = *reinterpret_cast<const uint4 *>(d.k + so + HALF);
+          if (do_v) {
+            vlo[u] = *reinterpret_cast<const uint4 *>(d.v + so);
+            vhi[u] = *reinterpret_cast<const uint4 *>(d.v + so + HALF);
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (!on[u]) continue;
+        if (valid && delta != 0) rotate8(klo[u], khi[u], cc, ss);
+        *reinterpret_cast<uint4 *>(d.k + dofs[u]) = klo[u];
+        *reinterpret_cast<uint4 *>(d.k + dofs[u] + HALF) = khi[u];
+        if (do_v) {
+          *reinterpret_cast<uint4 *>(d.v + dofs[u]) = vlo[u];
+          *reinterpret_cast<uint4 *>(d.v + dofs[u] + HALF) = vhi[u];
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// commit
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void commit_kernel(Dev d) {
+  if (d.ctl[CTL_OP_OK] == 0) return;
+  const int b = blockIdx.x;
+  const int *si = d.seq_info + (size_t)b * kSeqInfo;
+  const int fbd = si[SI_FBD], nmove = si[SI_N_MOVE], nfreed = si[SI_N_FREED];
+  const int moff = si[SI_MOVE_OFF], foff = si[SI_FREED_OFF];
+  const int base = d.ctl[CTL_BASE];
+  int32_t *trow = d.table + (size_t)b * d.maxpg;
+  for (int k = threadIdx.x; k < nfreed; k += blockDim.x) {
+    const int po = fbd + k;
+    const int old = trow[po];
+    d.free_stack[base + foff + k] = old;
+    trow[po] = (k < nmove) ? d.stage[moff + k] : -1;
+  }
+  if (threadIdx.x == 0) {
+    d.lens[b] = si[SI_NEW_LEN];
+    d.next_pos[b] = si[SI_NEW_NEXT];
+    if (b == 0) *d.free_count = base + d.ctl[CTL_F_TOTAL];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// append ([CE] eq. 3)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kPlanThreads) void append_plan_kernel(Dev d, const int32_t *counts) {
+  __shared__ int s_wave[kPlanThreads / 64 + 1];
+  __shared__ int s_err;
+  const int t = threadIdx.x;
+  if (t == 0) s_err = 0;
+  __syncthreads();
+  int run_n = 0, run_p = 0;
+  for (int base = 0; base < d.B; base += kPlanThreads) {
+    const int b = base + t;
+    int n = 0, need = 0;
+    if (b < d.B) {
+      n = counts[b];
+      const int old = d.lens[b];
+      const int po = (old + kPage - 1) / kPage;
+      const long long pn = ((long long)old + n + kPage - 1) / kPage;
+      if (n < 0) atomicMax(&s_err, (int)AKV_ERR_ARG);
+      else if (pn > d.maxpg) atomicMax(&s_err, (int)AKV_ERR_CAPACITY);
+      else need = (int)pn - po;
+      int *si = d.seq_info + (size_t)b * kSeqInfo;
+      si[SI_OLD_LEN] = old;
+      si[SI_OLD_NEXT] = d.next_pos[b];
+      si[SI_N_MOVE] = need;
+    }
+    int tn, tp;
+    const int en = block_exclusive_scan<kPlanThreads>(max(n, 0), s_wave, &tn);
+    const int ep = block_exclusive_scan<kPlanThreads>(need, s_wave, &tp);
+    if (b < d.B) {
+      int *si = d.seq_info + (size_t)b * kSeqInfo;
+      si[SI_APP_OFF] = run_n + en;
+      si[SI_MOVE_OFF] = run_p + ep;
+    }
+    run_n += tn;
+    run_p += tp;
+  }
+  __syncthreads();
+  const int fc = *d.free_count;
+  __shared__ int s_ok;
+  if (t == 0) {
+    int e = s_err;
+    if (!e && run_p > fc) e = AKV_ERR_NO_BLOCKS;
+    const int latched = d.ctl[CTL_ERR];
+    if (e && !latched) d.ctl[CTL_ERR] = e;
+    s_ok = !(e || latched);
+    d.ctl[CTL_OP_OK] = s_ok;
+  }
+  __syncthreads();
+  if (!s_ok) return;
+  for (int b = 0; b < d.B; ++b) {
+    const int *si = d.seq_info + (size_t)b * kSeqInfo;
+    const int need = si[SI_N_MOVE], off = si[SI_MOVE_OFF];
+    const int po = (si[SI_OLD_LEN] + kPage - 1) / kPage;
+    for (int k = t; k < need; k += kPlanThreads)
+      d.table[(size_t)b * d.maxpg + po + k] = d.free_stack[fc - 1 - (off + k)];
+  }
+  __syncthreads();
+  for (int base = 0; base < d.B; base += kPlanThreads) {
+    const int b = base + t;
+    if (b < d.B) {
+      const int n = counts[b];
+      const int *si = d.seq_info + (size_t)b * kSeqInfo;
+      d.lens[b] = si[SI_OLD_LEN] + n;
+      d.next_pos[b] = si[SI_OLD_NEXT] + n;
+    }
+  }
+  if (t == 0) *d.free_count = fc - run_p;
+}
+
+// One workgroup per new token: copies its K/V rows of every (layer, head)
+// with 16-B accesses and writes its position and token id.
+template <int D>
+__global__ __launch_bounds__(256) void append_copy_kernel(Dev d, int64_t n_new,
+                                                          const uint16_t *__restrict__ k_new,
+                                                          const uint16_t *__restrict__ v_new,
+                                                          const int32_t *__restrict__ tok_new) {
+  if (d.ctl[CTL_OP_OK] == 0) return;
+  __shared__ int s_page, s_row;
+  const int64_t tk = blockIdx.x;
+  if (threadIdx.x == 0) {
+    int lo = 0, hi = d.B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (d.seq_info[(size_t)mid * kSeqInfo + SI_APP_OFF] <= tk) lo = mid; else hi = mid - 1;
+    }
+    // skip sequences that append nothing but share the offset
+    const int *si = d.seq_info + (size_t)lo * kSeqInfo;
+    const int j = (int)(tk - si[SI_APP_OFF]);
+    const int slot = si[SI_OLD_LEN] + j;
+    const int page = d.table[(size_t)lo * d.maxpg + slot / kPage];
+    s_page = page;
+    s_row = slot % kPage;
+    d.pos[(size_t)page * kPage + slot % kPage] = si[SI_OLD_NEXT] + j;
+    d.tok[(size_t)page * kPage + slot % kPage] = tok_new[tk];
+  }
+  __syncthreads();
+  const int page = s_page, row = s_row;
+  constexpr int C8 = D / 8;
+  const int nchunk = d.L * d.H * C8;
+  for (int c = threadIdx.x; c < nchunk; c += blockDim.x) {
+    const int e8 = c % C8, lh = c / C8, h = lh % d.H, l = lh / d.H;
+    const size_t src = (((size_t)l * n_new + tk) * d.H + h) * D + 8 * e8;
+    const size_t dst = (((size_t)l * d.NB + page) * d.H + h) * (size_t)(kPage * D) + (size_t)row * D + 8 * e8;
+    *reinterpret_cast<uint4 *>(d.k + dst) = *reinterpret_cast<const uint4 *>(k_new + src);
+    *reinterpret_cast<uint4 *>(d.v + dst) = *reinterpret_cast<const uint4 *>(v_new + src);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// reset
+// ---------------------------------------------------------------------------
+__global__ void reset_kernel(Dev d, const int32_t *order) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t ntab = (int64_t)d.B * d.maxpg;
+  if (i < ntab) d.table[i] = -1;
+  if (i < d.B) {
+    d.lens[i] = 0;
+    d.next_pos[i] = 0;
+  }
+  if (i < d.NB) d.free_stack[d.NB - 1 - i] = order ? order[i] : (int)i;
+  if (i == 0) {
+    *d.free_count = d.NB;
+    for (int c = 0; c < CTL_COUNT; ++c) d.ctl[c] = 0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_plan(const Dev &d, const uint8_t *mask, const int32_t *new_pos,
+                       const int32_t *old_pos, int mode, int move_grid, hipStream_t st) {
+  hipLaunchKernelGGL(plan_kernel, dim3(d.B), dim3(kPlanThreads), 0, st, d, mask, new_pos,
+                     old_pos, mode, move_grid);
+  return hipGetLastError();
+}
+
+hipError_t launch_move(const Dev &d, int mode, int grid, hipStream_t st) {
+  if (d.D == 128)
+    hipLaunchKernelGGL(move_kernel<128>, dim3(grid), dim3(kMoveThreads), 0, st, d, mode);
+  else
+    hipLaunchKernelGGL(move_kernel<64>, dim3(grid), dim3(kMoveThreads), 0, st, d, mode);
+  return hipGetLastError();
+}
+
+hipError_t launch_commit(const Dev &d, hipStream_t st) {
+  hipLaunchKernelGGL(commit_kernel, dim3(d.B), dim3(256), 0, st, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const Dev &d, const int32_t *counts, int64_t n_new,
+                         const uint16_t *k_new, const uint16_t *v_new, const int32_t *tok_new,
+                         hipStream_t st, hipEvent_t ev_mid) {
+  hipLaunchKernelGGL(append_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, d, counts);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || n_new == 0) return e;
+  (void)ev_mid;
+  if (d.D == 128)
+    hipLaunchKernelGGL(append_copy_kernel<128>, dim3((unsigned)n_new), dim3(256), 0, st, d,
+                       n_new, k_new, v_new, tok_new);
+  else
+    hipLaunchKernelGGL(append_copy_kernel<64>, dim3((unsigned)n_new), dim3(256), 0, st, d,
+                       n_new, k_new, v_new, tok_new);
+  return hipGetLastError();
+}
+
+hipError_t launch_reset(const Dev &d, const int32_t *order_dev, hipStream_t st) {
+  const int64_t n = std::max<int64_t>((int64_t)d.B * d.maxpg, std::max<int64_t>(d.NB, d.B));
+  const unsigned grid = (unsigned)((n + 255) / 256);
+  hipLaunchKernelGGL(reset_kernel, dim3(grid), dim3(256), 0, st, d, order_dev);
+  return hipGetLastError();
+}
+
+}  // namespace akv

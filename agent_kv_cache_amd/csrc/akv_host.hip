@@ -1,0 +1,332 @@
+// Host side of libakv: argument validation, launch planning, the C ABI of
+// include/akv.h and optional per-kernel event timing.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+#include <vector>
+
+#include "akv_internal.h"
+
+using akv::Dev;
+
+struct akv_cache {
+  akv_cache_desc desc;
+  Dev dev;
+  akv::ScratchLayout layout;
+  int device = 0;
+  int n_cu = 256;
+  int move_grid = 2048;
+  bool profile = false;
+  struct Rec {
+    int kernel;
+    hipEvent_t a, b;
+  };
+  std::vector<Rec> pending;
+  std::vector<hipEvent_t> spare;
+  double total_ms[AKV_KERNEL_COUNT] = {};
+  int64_t launches[AKV_KERNEL_COUNT] = {};
+};
+
+namespace {
+
+#define AKV_HIP(expr)                           \
+  do {                                          \
+    if ((expr) != hipSuccess) return AKV_ERR_HIP; \
+  } while (0)
+
+hipEvent_t take_event(akv_cache *c) {
+  if (!c->spare.empty()) {
+    hipEvent_t e = c->spare.back();
+    c->spare.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Records an event pair around one launch when profiling is on.
+struct Timed {
+  akv_cache *c;
+  int kernel;
+  hipStream_t st;
+  hipEvent_t a = nullptr, b = nullptr;
+  Timed(akv_cache *c_, int k, hipStream_t s) : c(c_), kernel(k), st(s) {
+    if (c->profile) {
+      a = take_event(c);
+      b = take_event(c);
+      if (a && b) hipEventRecord(a, st);
+    }
+  }
+  ~Timed() {
+    if (a && b) {
+      hipEventRecord(b, st);
+      c->pending.push_back({kernel, a, b});
+    }
+  }
+};
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int nsplit_for(const akv_cache *c, int nL) {
+  const long long base = (long long)c->desc.n_seqs * nL * c->desc.n_kv_heads;
+  const long long target = 8LL * c->n_cu;
+  long long ns = (target + base - 1) / base;
+  const long long cap = std::max(1, c->desc.max_blocks_per_seq / 4);
+  ns = std::min(ns, cap);
+  return (int)std::max(1LL, ns);
+}
+
+akv_status run_compaction(akv_cache *c, const uint8_t *mask, const int32_t *new_pos,
+                          const int32_t *old_pos, int mode, void *stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  {
+    Timed tm(c, AKV_KERNEL_PLAN, st);
+    AKV_HIP(akv::launch_plan(c->dev, mask, new_pos, old_pos, mode, c->move_grid, st));
+  }
+  {
+    Timed tm(c, AKV_KERNEL_MOVE, st);
+    AKV_HIP(akv::launch_move(c->dev, mode, c->move_grid, st));
+  }
+  {
+    Timed tm(c, AKV_KERNEL_COMMIT, st);
+    AKV_HIP(akv::launch_commit(c->dev, st));
+  }
+  return AKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t akv_scratch_bytes(const akv_cache_desc *d) {
+  if (!d || d->n_seqs < 1 || d->max_blocks_per_seq < 1 || d->n_blocks < 1) return 0;
+  return akv::scratch_layout(d->n_seqs, d->max_blocks_per_seq * akv::kPage, d->n_blocks).total;
+}
+
+akv_status akv_cache_init(const akv_cache_desc *d, akv_cache **out) {
+  if (!d || !out) return AKV_ERR_ARG;
+  *out = nullptr;
+  if (d->n_layers < 1 || d->n_kv_heads < 1 || d->n_blocks < 1 || d->n_seqs < 1 ||
+      d->max_blocks_per_seq < 1)
+    return AKV_ERR_ARG;
+  if (d->block_size != akv::kPage) return AKV_ERR_ARG;
+  if (d->head_dim != 64 && d->head_dim != 128) return AKV_ERR_ARG;
+  if (!(d->rope_base > 0.0) || !isfinite(d->rope_base)) return AKV_ERR_ARG;
+  if ((long long)d->max_blocks_per_seq * akv::kPage > INT32_MAX / 2) return AKV_ERR_ARG;
+  if (!d->k_pool || !d->v_pool || !d->block_table || !d->seq_lens || !d->next_pos ||
+      !d->positions || !d->token_ids || !d->free_stack || !d->free_count || !d->scratch)
+    return AKV_ERR_ARG;
+  if (!aligned(d->k_pool, 16) || !aligned(d->v_pool, 16) || !aligned(d->scratch, 256) ||
+      !aligned(d->positions, 16) || !aligned(d->token_ids, 16))
+    return AKV_ERR_ARG;
+  if (d->scratch_bytes < akv_scratch_bytes(d)) return AKV_ERR_ARG;
+
+  akv_cache *c = new (std::nothrow) akv_cache();
+  if (!c) return AKV_ERR_ARG;
+  c->desc = *d;
+  const int S = d->max_blocks_per_seq * akv::kPage;
+  c->layout = akv::scratch_layout(d->n_seqs, S, d->n_blocks);
+  char *sb = static_cast<char *>(d->scratch);
+  Dev &v = c->dev;
+  v.k = d->k_pool;
+  v.v = d->v_pool;
+  v.table = d->block_table;
+  v.lens = d->seq_lens;
+  v.next_pos = d->next_pos;
+  v.pos = d->positions;
+  v.tok = d->token_ids;
+  v.free_stack = d->free_stack;
+  v.free_count = d->free_count;
+  v.ctl = reinterpret_cast<int32_t *>(sb + c->layout.ctl);
+  v.theta = reinterpret_cast<const double *>(sb + c->layout.theta);
+  v.seq_info = reinterpret_cast<int32_t *>(sb + c->layout.seq_info);
+  v.src_map = reinterpret_cast<int32_t *>(sb + c->layout.src_map);
+  v.delta_map = reinterpret_cast<int32_t *>(sb + c->layout.delta_map);
+  v.stage = reinterpret_cast<int32_t *>(sb + c->layout.stage);
+  v.L = d->n_layers;
+  v.H = d->n_kv_heads;
+  v.D = d->head_dim;
+  v.NB = d->n_blocks;
+  v.B = d->n_seqs;
+  v.maxpg = d->max_blocks_per_seq;
+  v.S = S;
+
+  if (hipGetDevice(&c->device) != hipSuccess ||
+      hipDeviceGetAttribute(&c->n_cu, hipDeviceAttributeMultiprocessorCount, c->device) !=
+          hipSuccess) {
+    delete c;
+    return AKV_ERR_HIP;
+  }
+  c->move_grid = 8 * c->n_cu;
+
+  // theta_i = base^(-2i/d), double, uploaded once.
+  double theta[akv::kMaxHalf] = {};
+  for (int i = 0; i < d->head_dim / 2; ++i)
+    theta[i] = pow(d->rope_base, -2.0 * (double)i / (double)d->head_dim);
+  if (hipMemcpy(sb + c->layout.theta, theta, sizeof(theta), hipMemcpyHostToDevice) != hipSuccess) {
+    delete c;
+    return AKV_ERR_HIP;
+  }
+  *out = c;
+  return AKV_OK;
+}
+
+void akv_cache_free(akv_cache *c) {
+  if (!c) return;
+  for (auto &r : c->pending) {
+    hipEventDestroy(r.a);
+    hipEventDestroy(r.b);
+  }
+  for (auto e : c->spare) hipEventDestroy(e);
+  delete c;
+}
+
+akv_status akv_cache_reset(akv_cache *c, const int32_t *page_order, void *stream) {
+  if (!c) return AKV_ERR_ARG;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int NB = c->desc.n_blocks;
+  const int32_t *order_dev = nullptr;
+  if (page_order) {
+    std::vector<char> seen(NB, 0);
+    for (int i = 0; i < NB; ++i) {
+      const int32_t p = page_order[i];
+      if (p < 0 || p >= NB || seen[p]) return AKV_ERR_ARG;
+      seen[p] = 1;
+    }
+    AKV_HIP(hipStreamSynchronize(st));
+    AKV_HIP(hipMemcpy(c->dev.stage, page_order, sizeof(int32_t) * NB, hipMemcpyHostToDevice));
+    order_dev = c->dev.stage;
+  }
+  AKV_HIP(akv::launch_reset(c->dev, order_dev, st));
+  return AKV_OK;
+}
+
+akv_status akv_append(akv_cache *c, const int32_t *counts, int64_t n_new, const uint16_t *k_new,
+                      const uint16_t *v_new, const int32_t *token_ids, void *stream) {
+  if (!c || !counts || n_new < 0 || n_new > INT32_MAX) return AKV_ERR_ARG;
+  if (n_new > 0 && (!k_new || !v_new || !token_ids)) return AKV_ERR_ARG;
+  if (n_new > 0 && (!aligned(k_new, 16) || !aligned(v_new, 16))) return AKV_ERR_ARG;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  Timed tm(c, AKV_KERNEL_APPEND, st);
+  AKV_HIP(akv::launch_append(c->dev, counts, n_new, k_new, v_new, token_ids, st, nullptr));
+  return AKV_OK;
+}
+
+akv_status akv_drop(akv_cache *c, const uint8_t *drop_mask, void *stream) {
+  if (!c || !drop_mask || !aligned(drop_mask, 16)) return AKV_ERR_ARG;
+  return run_compaction(c, drop_mask, nullptr, nullptr, akv::M_DROP, stream);
+}
+
+akv_status akv_reposition(akv_cache *c, const int32_t *old_pos, const int32_t *new_pos,
+                          void *stream) {
+  if (!c) return AKV_ERR_ARG;
+  int mode = akv::M_REPOS;
+  if (new_pos) mode |= akv::M_NEWPOS;
+  if (old_pos) mode |= akv::M_OLDPOS;
+  return run_compaction(c, nullptr, new_pos, old_pos, mode, stream);
+}
+
+akv_status akv_drop_reposition(akv_cache *c, const uint8_t *drop_mask, const int32_t *new_pos,
+                               void *stream) {
+  if (!c || !drop_mask || !aligned(drop_mask, 16)) return AKV_ERR_ARG;
+  int mode = akv::M_DROP | akv::M_REPOS;
+  if (new_pos) mode |= akv::M_NEWPOS;
+  return run_compaction(c, drop_mask, new_pos, nullptr, mode, stream);
+}
+
+size_t akv_decode_workspace_bytes(const akv_cache *c, int32_t n_layers, int32_t n_q_heads) {
+  if (!c || n_layers < 1 || n_q_heads < 1) return 0;
+  const int ns = nsplit_for(c, n_layers);
+  if (ns == 1) return 256;
+  return akv::align256((size_t)c->desc.n_seqs * n_layers * n_q_heads * ns *
+                       (size_t)(c->desc.head_dim + 2) * sizeof(float));
+}
+
+akv_status akv_decode_attention(akv_cache *c, const uint16_t *q, const int32_t *active_len,
+                                int32_t layer_begin, int32_t n_layers, int32_t n_q_heads,
+                                uint16_t *out, void *workspace, size_t workspace_bytes,
+                                void *stream) {
+  if (!c || !q || !out) return AKV_ERR_ARG;
+  if (layer_begin < 0 || n_layers < 1 || layer_begin + n_layers > c->desc.n_layers)
+    return AKV_ERR_ARG;
+  if (n_q_heads < 1 || n_q_heads % c->desc.n_kv_heads != 0 ||
+      n_q_heads / c->desc.n_kv_heads > 16)
+    return AKV_ERR_ARG;
+  if (!aligned(q, 16) || !aligned(out, 2)) return AKV_ERR_ARG;
+  if ((long long)c->desc.n_seqs * n_layers > 65535) return AKV_ERR_ARG;
+  const int ns = nsplit_for(c, n_layers);
+  if (ns > 1 && (!workspace || workspace_bytes < akv_decode_workspace_bytes(c, n_layers, n_q_heads)))
+    return AKV_ERR_ARG;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  {
+    Timed tm(c, AKV_KERNEL_ATTN, st);
+    AKV_HIP(akv::launch_attention(c->dev, q, active_len, layer_begin, n_layers, n_q_heads, out,
+                                  static_cast<float *>(workspace), ns, st));
+  }
+  if (ns > 1) {
+    Timed tm(c, AKV_KERNEL_COMBINE, st);
+    AKV_HIP(akv::launch_combine(static_cast<float *>(workspace), out,
+                                c->desc.n_seqs * n_layers * n_q_heads, ns, c->desc.head_dim, st));
+  }
+  return AKV_OK;
+}
+
+akv_status akv_sync_status(akv_cache *c, void *stream) {
+  if (!c) return AKV_ERR_ARG;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  AKV_HIP(hipStreamSynchronize(st));
+  int32_t err = 0;
+  AKV_HIP(hipMemcpy(&err, c->dev.ctl + akv::CTL_ERR, sizeof(err), hipMemcpyDeviceToHost));
+  if (err) {
+    const int32_t zero = 0;
+    AKV_HIP(hipMemcpy(c->dev.ctl + akv::CTL_ERR, &zero, sizeof(zero), hipMemcpyHostToDevice));
+  }
+  return static_cast<akv_status>(err);
+}
+
+const char *akv_status_string(akv_status s) {
+  switch (s) {
+    case AKV_OK: return "ok";
+    case AKV_ERR_ARG: return "invalid argument";
+    case AKV_ERR_ORDER: return "new positions must be >= 0 and strictly increasing";
+    case AKV_ERR_POS_MISMATCH: return "old positions differ from the stored positions";
+    case AKV_ERR_NO_BLOCKS: return "free page pool too small";
+    case AKV_ERR_CAPACITY: return "sequence exceeds max_blocks_per_seq";
+    case AKV_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+akv_status akv_profile_enable(akv_cache *c, int on) {
+  if (!c) return AKV_ERR_ARG;
+  c->profile = on != 0;
+  return AKV_OK;
+}
+
+akv_status akv_profile_read(akv_cache *c, int kernel, double *total_ms, int64_t *launches,
+                            int reset) {
+  if (!c || kernel < 0 || kernel >= AKV_KERNEL_COUNT) return AKV_ERR_ARG;
+  for (auto &r : c->pending) {
+    AKV_HIP(hipEventSynchronize(r.b));
+    float ms = 0.f;
+    AKV_HIP(hipEventElapsedTime(&ms, r.a, r.b));
+    c->total_ms[r.kernel] += ms;
+    c->launches[r.kernel] += 1;
+    c->spare.push_back(r.a);
+    c->spare.push_back(r.b);
+  }
+  c->pending.clear();
+  if (total_ms) *total_ms = c->total_ms[kernel];
+  if (launches) *launches = c->launches[kernel];
+  if (reset) {
+    std::fill(c->total_ms, c->total_ms + AKV_KERNEL_COUNT, 0.0);
+    std::fill(c->launches, c->launches + AKV_KERNEL_COUNT, 0);
+  }
+  return AKV_OK;
+}
+
+}  // extern "C"

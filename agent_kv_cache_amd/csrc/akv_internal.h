@@ -1,0 +1,101 @@
+// Internal declarations shared by the libakv host code and kernels.
+// Not part of the public ABI (see include/akv.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/akv.h"
+
+namespace akv {
+
+constexpr int kPage = 16;       // tokens per page
+constexpr int kMaxHalf = 64;    // head_dim / 2 upper bound (head_dim <= 128)
+
+// Control words at the start of the scratch buffer (int32 each).
+enum Ctl : int {
+  CTL_ERR = 0,        // latched error code (sticky until akv_sync_status)
+  CTL_DONE = 1,       // last-block ticket of the plan kernels
+  CTL_OP_OK = 2,      // 1 when the planned op may commit
+  CTL_T_MOVE = 3,     // pages moved out of place (all sequences)
+  CTL_T_INPLACE = 4,  // pages re-rotated in place
+  CTL_F_TOTAL = 5,    // pages returned to the free stack
+  CTL_BASE = 6,       // free_count before the op minus CTL_T_MOVE
+  CTL_FC_OLD = 7,     // free_count before the op
+  CTL_LPI = 8,        // layers per move item chosen by the plan
+  CTL_COUNT = 64
+};
+
+// Per-sequence plan record (int32 x kSeqInfo).
+enum SeqInfo : int {
+  SI_NEW_LEN = 0,    // survivors r'
+  SI_FBD = 1,        // first page rewritten out of place (== pages if none)
+  SI_FIP = 2,        // first page re-rotated in place
+  SI_N_MOVE = 3,
+  SI_N_INPLACE = 4,
+  SI_N_FREED = 5,
+  SI_NEW_NEXT = 6,   // next_pos after the op
+  SI_ERR = 7,
+  SI_MOVE_OFF = 8,   // exclusive prefix over sequences
+  SI_INPLACE_OFF = 9,
+  SI_FREED_OFF = 10,
+  SI_OLD_LEN = 11,
+  SI_OLD_NEXT = 12,
+  SI_APP_OFF = 13,   // append: offset of this sequence's tokens in the input
+  kSeqInfo = 16
+};
+
+// Mode bits of the compaction plan.
+enum Mode : int {
+  M_DROP = 1,        // a drop mask is given
+  M_REPOS = 2,       // positions change (canonical unless M_NEWPOS)
+  M_NEWPOS = 4,      // explicit new positions
+  M_OLDPOS = 8,      // validate old positions
+};
+
+// Device view of one cache, passed by value to every kernel.
+struct Dev {
+  uint16_t *k, *v;
+  int32_t *table, *lens, *next_pos, *pos, *tok, *free_stack, *free_count;
+  int32_t *ctl, *seq_info, *src_map, *delta_map, *stage;
+  const double *theta;        // [d/2]
+  int L, H, D, NB, B, maxpg, S;
+};
+
+// Scratch layout (byte offsets from the scratch base, each 256-B aligned).
+struct ScratchLayout {
+  size_t ctl, theta, seq_info, src_map, delta_map, stage, total;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline ScratchLayout scratch_layout(int B, int S, int NB) {
+  ScratchLayout s;
+  size_t o = 0;
+  s.ctl = o;       o = align256(o + CTL_COUNT * 4);
+  s.theta = o;     o = align256(o + kMaxHalf * 8);
+  s.seq_info = o;  o = align256(o + size_t(B) * kSeqInfo * 4);
+  s.src_map = o;   o = align256(o + size_t(B) * S * 4);
+  s.delta_map = o; o = align256(o + size_t(B) * S * 4);
+  s.stage = o;     o = align256(o + size_t(NB) * 4);
+  s.total = o;
+  return s;
+}
+
+// Launchers (each in the .hip file that defines its kernels).
+hipError_t launch_plan(const Dev &d, const uint8_t *mask, const int32_t *new_pos,
+                       const int32_t *old_pos, int mode, int move_grid, hipStream_t st);
+hipError_t launch_move(const Dev &d, int mode, int grid, hipStream_t st);
+hipError_t launch_commit(const Dev &d, hipStream_t st);
+hipError_t launch_append(const Dev &d, const int32_t *counts, int64_t n_new,
+                         const uint16_t *k_new, const uint16_t *v_new,
+                         const int32_t *tok_new, hipStream_t st,
+                         hipEvent_t ev_mid);
+hipError_t launch_reset(const Dev &d, const int32_t *order_dev, hipStream_t st);
+hipError_t launch_attention(const Dev &d, const uint16_t *q, const int32_t *active_len,
+                            int l0, int nL, int Hq, uint16_t *out, float *part,
+                            int nsplit, hipStream_t st);
+hipError_t launch_combine(const float *part, uint16_t *out, int rows, int nsplit,
+                          int D, hipStream_t st);
+
+}  // namespace akv

@@ -1,0 +1,99 @@
+"""Set-up helpers for caches shaped like the pages' agent workloads.
+
+Allocation and filling only: sizes the page pool, appends seeded bf16 data
+through akv_append in chunks, uploads drop masks.  No step of the method is
+computed here.
+"""
+from __future__ import annotations
+
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+from .binding import PAGE, AkvCache
+from .workloads import Shape, randn_bf16
+
+CHUNK = 4096  # tokens per generated data chunk (fixes the seed of every chunk)
+
+
+def pages_for(n: int) -> int:
+    return (int(n) + PAGE - 1) // PAGE
+
+
+def moved_pages(n: int, mask: Optional[np.ndarray]) -> int:
+    """Upper bound of fresh pages a drop of `mask` over n entries takes."""
+    if mask is None or not mask[:n].any():
+        return 0
+    f = int(np.flatnonzero(mask[:n])[0])
+    r = n - int(mask[:n].astype(bool).sum())
+    return max(0, pages_for(r) - f // PAGE)
+
+
+def chunk_seed(data_seed: int, b: int, c: int, which: int) -> int:
+    return (data_seed * 1_000_003 + b * 65_537 + c * 31 + which) % (2 ** 63)
+
+
+def seq_chunk(shape: Shape, data_seed: int, b: int, c: int, n: int, which: str, device):
+    """bf16 [L, n, Hkv, d] data of tokens [c*CHUNK, c*CHUNK + n) of sequence b."""
+    w = 0 if which == "k" else 1
+    return randn_bf16((shape.n_layers, n, shape.n_kv_heads, shape.head_dim),
+                      chunk_seed(data_seed, b, c, w), device=device)
+
+
+def make_cache(shape: Shape, seq_lens: Sequence[int], extra_pages: int,
+               max_blocks_per_seq: Optional[int] = None, device: str = "cuda") -> AkvCache:
+    nb = sum(pages_for(n) for n in seq_lens) + int(extra_pages)
+    maxpg = max_blocks_per_seq or max(1, max(pages_for(n) for n in seq_lens))
+    return AkvCache(shape.n_layers, shape.n_kv_heads, shape.head_dim, max(nb, 1),
+                    len(seq_lens), maxpg, shape.rope_base, device=device)
+
+
+def fill(cache: AkvCache, shape: Shape, seq_lens: Sequence[int], data_seed: int,
+         gen_device: str = "cuda", token_base: Optional[List[int]] = None):
+    """Append every sequence's tokens chunk by chunk (seeded per chunk).
+
+    Token ids of sequence b are token_base[b] + 0, 1, ... (default b * 2^24).
+    """
+    import torch
+    dev = cache.device
+    B = len(seq_lens)
+    nchunks = max((int(n) + CHUNK - 1) // CHUNK for n in seq_lens) if B else 0
+    for c in range(nchunks):
+        counts, ks, vs, toks = [], [], [], []
+        for b, n in enumerate(seq_lens):
+            m = max(0, min(CHUNK, int(n) - c * CHUNK))
+            counts.append(m)
+            if m:
+                ks.append(seq_chunk(shape, data_seed, b, c, m, "k", gen_device).to(dev))
+                vs.append(seq_chunk(shape, data_seed, b, c, m, "v", gen_device).to(dev))
+                base = (b << 24) if token_base is None else token_base[b]
+                toks.append(torch.arange(base + c * CHUNK, base + c * CHUNK + m,
+                                         dtype=torch.int32, device=dev))
+        n_new = sum(counts)
+        cnt = torch.tensor(counts, dtype=torch.int32, device=dev)
+        if n_new == 0:
+            continue
+        k = torch.cat(ks, dim=1).contiguous()
+        v = torch.cat(vs, dim=1).contiguous()
+        cache.append(cnt, n_new, k, v, torch.cat(toks))
+        del k, v, ks, vs
+
+
+def mask_tensor(cache: AkvCache, masks: Sequence[Optional[np.ndarray]]):
+    """u8 [B][S] device mask, row b = masks[b] padded with zeros."""
+    import torch
+    m = np.zeros((cache.B, cache.S), dtype=np.uint8)
+    for b, mb in enumerate(masks):
+        if mb is not None:
+            m[b, :len(mb)] = mb
+    return torch.from_numpy(m).to(cache.device)
+
+
+def pos_tensor(cache: AkvCache, rows: Sequence[Optional[np.ndarray]]):
+    """int32 [B][S] device array, row b = rows[b] padded with zeros."""
+    import torch
+    a = np.zeros((cache.B, cache.S), dtype=np.int32)
+    for b, r in enumerate(rows):
+        if r is not None:
+            a[b, :len(r)] = r
+    return torch.from_numpy(a).to(cache.device)

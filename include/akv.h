@@ -1,0 +1,203 @@
+/*
+ * akv.h -- C ABI of libakv.so: the data-parallel hot path of agent cache
+ * engineering (drop / reposition of a paged bf16 KV cache, and decode
+ * attention over the active KV) for AMD Instinct MI355X (gfx950).
+ *
+ * Sources, cited by page title and section:
+ *   [CE]  review of "Cache Engineering for Agents" (euisuk-chung.github.io,
+ *         2026-10-29): sec. 3.3 eq. (3) append, eq. (4) drop, eq. (5)
+ *         reposition; sec. 3.4 eq. (6) the state is fixed by the op history;
+ *         Appendix A.1.1 / Figure 10 position walk-through.
+ *   [AKV] "[Repo Review] AKV" (euisuk-chung.github.io, 2026-10-23): sec. 1
+ *         drop runs before reposition at one boundary; sec. 3 / 5.3 a plan
+ *         that is invalid is rejected as a whole; sec. 5.3 the layout keeps
+ *         positions, a keep mask, next_position and old/new position
+ *         transition arrays; sec. 5.5 the reposition kernel (un-rotate at p,
+ *         rotate to q, copy when p == q, V copied, separate destination slot).
+ *
+ * Conventions
+ *   - All tensors are DEVICE memory owned by the caller (the library never
+ *     allocates device memory).  bf16 values travel as uint16_t bit patterns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Every call is stream-ordered and asynchronous; the library never
+ *     synchronises except inside akv_sync_status / akv_profile_read.
+ *   - Page size is fixed at 16 tokens.  Pool layout (bf16, row-major):
+ *         k_pool, v_pool : [n_layers][n_blocks][n_kv_heads][16][head_dim]
+ *     so one (layer, page, kv head) chunk is 16*head_dim contiguous values.
+ *   - Per-page metadata: positions, token_ids : int32 [n_blocks][16].
+ *   - Per-sequence metadata: block_table int32 [n_seqs][max_blocks_per_seq]
+ *     (-1 = unused), seq_lens int32 [n_seqs] (active entries), next_pos
+ *     int32 [n_seqs].  Free pages: free_stack int32 [n_blocks] and
+ *     free_count int32 [1]; pages are handed out from the top of the stack
+ *     (free_stack[free_count-1] first).
+ *   - Per-token argument arrays (masks, positions) have one row per sequence
+ *     with row stride S = max_blocks_per_seq * 16 entries; entry i of row b
+ *     refers to the i-th active entry of sequence b and entries at or beyond
+ *     that sequence's length are ignored.
+ *   - Errors: arguments the host can check are rejected with an error code
+ *     before anything is enqueued (cache unchanged).  Checks that need device
+ *     data (a decreasing new position, an old position that does not match,
+ *     too few free pages, a page table overflow) are made on the device
+ *     before any write; the whole operation then becomes a no-op, the first
+ *     such error is latched in the device error word, and every later
+ *     mutating call on the cache is a no-op until akv_sync_status() reads
+ *     and clears it.  This mirrors whole-request rejection in [AKV] sec. 3
+ *     and 5.3.
+ *   - Concurrent calls on one cache from different streams race; callers
+ *     serialise them on one stream.
+ */
+#ifndef AKV_H
+#define AKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  AKV_OK = 0,
+  AKV_ERR_ARG = 1,          /* null pointer, bad shape, out-of-range value */
+  AKV_ERR_ORDER = 2,        /* new positions negative or not strictly increasing */
+  AKV_ERR_POS_MISMATCH = 3, /* old_pos differs from the stored positions */
+  AKV_ERR_NO_BLOCKS = 4,    /* free pool too small for the new pages */
+  AKV_ERR_CAPACITY = 5,     /* a sequence would exceed max_blocks_per_seq */
+  AKV_ERR_HIP = 6           /* a HIP runtime call failed */
+} akv_status;
+
+typedef struct akv_cache akv_cache; /* opaque host-side handle */
+
+typedef struct {
+  int32_t n_layers;           /* L  >= 1 */
+  int32_t n_kv_heads;         /* Hkv >= 1 */
+  int32_t head_dim;           /* d: 64 or 128 */
+  int32_t block_size;         /* must be 16 */
+  int32_t n_blocks;           /* NB pages in the pool, >= 1 */
+  int32_t n_seqs;             /* B sequences, >= 1 */
+  int32_t max_blocks_per_seq; /* page-table row length, >= 1 */
+  double rope_base;           /* theta_i = rope_base^(-2i/d), NeoX half split */
+  uint16_t *k_pool;           /* bf16 [L][NB][Hkv][16][d] */
+  uint16_t *v_pool;           /* bf16 [L][NB][Hkv][16][d] */
+  int32_t *block_table;       /* [B][max_blocks_per_seq] */
+  int32_t *seq_lens;          /* [B] */
+  int32_t *next_pos;          /* [B] */
+  int32_t *positions;         /* [NB][16] */
+  int32_t *token_ids;         /* [NB][16] */
+  int32_t *free_stack;        /* [NB] */
+  int32_t *free_count;        /* [1] */
+  void *scratch;              /* device, >= akv_scratch_bytes(desc) bytes, 256-B aligned */
+  size_t scratch_bytes;
+} akv_cache_desc;
+
+/* Device scratch the cache needs (compaction plan, error word, RoPE
+ * frequencies).  Owned by the caller, lives as long as the cache. */
+size_t akv_scratch_bytes(const akv_cache_desc *desc);
+
+/* Validate `desc`, upload theta_i (computed on the host in double) into the
+ * scratch and return a host handle in *out.  Does not touch the pools or
+ * metadata; call akv_cache_reset before first use.  Errors: AKV_ERR_ARG,
+ * AKV_ERR_HIP. */
+akv_status akv_cache_init(const akv_cache_desc *desc, akv_cache **out);
+void akv_cache_free(akv_cache *c);
+
+/* Empty every sequence: seq_lens = next_pos = 0, block_table = -1,
+ * free_count = NB, and the free stack such that pages are handed out in the
+ * order page_order[0], page_order[1], ... (page_order: HOST int32 [NB], a
+ * permutation of 0..NB-1; NULL = 0, 1, 2, ...).  Clears the error word.
+ * Errors: AKV_ERR_ARG (not a permutation), AKV_ERR_HIP. */
+akv_status akv_cache_reset(akv_cache *c, const int32_t *page_order, void *stream);
+
+/* [CE] eq. (3): append counts[b] new entries to each sequence b.
+ *   counts    : DEVICE int32 [B], >= 0
+ *   n_new     : host copy of sum(counts) (sizes the launch)
+ *   k_new     : DEVICE bf16 [L][n_new][Hkv][d], keys already rotated at
+ *               their positions (the model computed them), tokens ordered by
+ *               sequence then by append order
+ *   v_new     : DEVICE bf16 [L][n_new][Hkv][d]
+ *   token_ids : DEVICE int32 [n_new]
+ * Entry j of sequence b lands at slot len_b + j with position
+ * next_pos_b + j; then len_b and next_pos_b advance by counts[b].
+ * Device-detected: AKV_ERR_NO_BLOCKS, AKV_ERR_CAPACITY (whole call no-op). */
+akv_status akv_append(akv_cache *c, const int32_t *counts, int64_t n_new,
+                      const uint16_t *k_new, const uint16_t *v_new,
+                      const int32_t *token_ids, void *stream);
+
+/* [CE] eq. (4): drop the active entries whose mask byte is non-zero.
+ *   drop_mask : DEVICE uint8 [B][S]
+ * Survivors keep their order, K, V, position and token id; seq_lens shrink;
+ * next_pos is unchanged.  Survivors from the first dropped entry's page on
+ * are moved into fresh pages (out of place); pages before it are untouched;
+ * the old pages return to the free stack.  Needs up to ceil(len/16) free
+ * pages per sequence while it runs (device-detected AKV_ERR_NO_BLOCKS). */
+akv_status akv_drop(akv_cache *c, const uint8_t *drop_mask, void *stream);
+
+/* [CE] eq. (5): move every active entry from its position p to q.
+ *   old_pos : DEVICE int32 [B][S] or NULL.  If given it must equal the
+ *             stored positions (the transition's source, [AKV] sec. 5.3);
+ *             otherwise AKV_ERR_POS_MISMATCH and the call is a no-op.
+ *   new_pos : DEVICE int32 [B][S] or NULL (= canonical 0..len-1).  Must be
+ *             >= 0 and strictly increasing per sequence (AKV_ERR_ORDER).
+ * K' = R(q - p) K with pair i = (k[i], k[i+d/2]) turned by (q - p)*theta_i,
+ * computed in fp64 from bf16 and rounded once to bf16 (nearest, ties even);
+ * entries with q == p are left bit-identical; V is not touched.  In place.
+ * next_pos = last q + 1 (0 for an empty sequence). */
+akv_status akv_reposition(akv_cache *c, const int32_t *old_pos,
+                          const int32_t *new_pos, void *stream);
+
+/* Drop then reposition at one boundary ([AKV] sec. 1), fused into one
+ * compaction pass: survivors are moved and re-rotated in the same kernel.
+ *   drop_mask : DEVICE uint8 [B][S]
+ *   new_pos   : DEVICE int32 [B][S] indexed by SURVIVOR rank j, or NULL
+ *               (= canonical 0..r-1, the next append then goes to r).
+ * Result is bit-identical to akv_drop followed by akv_reposition. */
+akv_status akv_drop_reposition(akv_cache *c, const uint8_t *drop_mask,
+                               const int32_t *new_pos, void *stream);
+
+/* Decode attention over the active KV for layers
+ * [layer_begin, layer_begin + n_layers):
+ *   q          : DEVICE bf16 [B][n_layers][n_q_heads][d], already rotated at
+ *                the query's position by the caller
+ *   active_len : DEVICE int32 [B] or NULL (= seq_lens).  Values outside
+ *                [0, seq_len] are clamped and AKV_ERR_ARG is latched.
+ *   out        : DEVICE bf16 [B][n_layers][n_q_heads][d]
+ *   workspace  : DEVICE, >= akv_decode_workspace_bytes(...) bytes
+ * o = softmax(q K^T / sqrt(d)) V over the first active_len entries; query
+ * head h reads kv head h / (n_q_heads / n_kv_heads); no entry beyond
+ * active_len and no self token; an empty sequence gives zeros.
+ * Host-checked: n_q_heads multiple of n_kv_heads with ratio <= 16, layer
+ * range inside [0, L). */
+size_t akv_decode_workspace_bytes(const akv_cache *c, int32_t n_layers,
+                                  int32_t n_q_heads);
+akv_status akv_decode_attention(akv_cache *c, const uint16_t *q,
+                                const int32_t *active_len, int32_t layer_begin,
+                                int32_t n_layers, int32_t n_q_heads,
+                                uint16_t *out, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
+/* Synchronise `stream`, return the latched device error (AKV_OK if none)
+ * and clear it. */
+akv_status akv_sync_status(akv_cache *c, void *stream);
+const char *akv_status_string(akv_status s);
+
+/* Optional per-kernel timing with HIP events recorded on the launch stream.
+ * Kernel ids: */
+enum {
+  AKV_KERNEL_PLAN = 0,     /* keep-scan / compaction plan */
+  AKV_KERNEL_MOVE = 1,     /* fused move + re-rotation */
+  AKV_KERNEL_COMMIT = 2,   /* page table / free stack commit */
+  AKV_KERNEL_ATTN = 3,     /* split-K decode attention */
+  AKV_KERNEL_COMBINE = 4,  /* split-K merge */
+  AKV_KERNEL_APPEND = 5,   /* append plan + copy */
+  AKV_KERNEL_COUNT = 6
+};
+akv_status akv_profile_enable(akv_cache *c, int on);
+/* Synchronises the recorded events; *total_ms and *launches accumulate
+ * since the last reset.  reset != 0 clears the accumulators afterwards. */
+akv_status akv_profile_read(akv_cache *c, int kernel, double *total_ms,
+                            int64_t *launches, int reset);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* AKV_H */
