@@ -1,0 +1,252 @@
+#!/usr/bin/env python3
+"""Benchmark of the agent-cache hot path on one MI355X.
+
+One step = restore the per-sequence state (page table, lengths, next
+positions, free stack: one small device copy) + fused drop+reposition
+(plan, move/re-rotate, commit kernels) + decode attention over all layers
+(split-K kernel + combine).  The default workload is the Llama-3.1-8B-shaped
+cache (32 layers, 8 kv heads, d=128, 32768 tokens, six seeded tool spans of
+1024..4096 tokens dropped, canonical reposition, 32 query heads).
+
+Prints ONE JSON line.  `value` = algorithmic KV bytes of the whole step
+(drop+reposition and decode) / wall time per step, in GB/s.  The `roofline`
+object covers the dominant kernel (per-launch algorithmic bytes / average
+launch time from HIP events recorded on the launch stream); `parts` gives
+both parts; `cpu_baseline` times the fp64 oracle on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+METRIC = "KV GB/s for drop+reposition and decode attention; % of HBM peak, 1 GPU"
+
+
+def algorithmic_bytes(shape, seq_lens, masks):
+    """Bytes the method must move, for caches whose positions are 0..n-1.
+
+    drop+reposition: survivors whose slot changes (at or after the first
+    dropped entry) read and write K and V once; survivors whose position
+    changes in place read and write K (none for canonical input positions);
+    plus the mask bytes, the positions read for every survivor and the
+    positions and token ids moved with the moved rows.
+    decode: K and V of every survivor once, q in and out, the page ids.
+    """
+    L, H, D = shape.n_layers, shape.n_kv_heads, shape.head_dim
+    row = L * H * D * 2                      # one token's K (or V), all layers
+    moved = surv = total = pages = 0
+    for n, m in zip(seq_lens, masks):
+        m = np.asarray(m[:n]).astype(bool)
+        r = n - int(m.sum())
+        surv += r
+        total += n
+        pages += (r + 15) // 16
+        if m.any():
+            f = int(np.flatnonzero(m)[0])
+            moved += r - f
+    b_move = moved * (2 * row) * 2 + moved * 12
+    b_dr = b_move + total + 4 * surv
+    b_att = surv * 2 * row + 2 * (len(seq_lens) * L * shape.n_q_heads * D * 2) + 4 * pages
+    return dict(moved=moved, survivors=surv, tokens=total, b_move=b_move, b_dr=b_dr,
+                b_att=b_att, b_att_kv=surv * 2 * row)
+
+
+def cpu_baseline(wl, layer_stride: int, time_budget_s: float = 25.0):
+    """The fp64 oracle (as it stands) on a layer sample of the same workload."""
+    from threadpoolctl import threadpool_limits
+
+    from agent_kv_cache_amd import harness as Hn
+    from agent_kv_cache_amd.workloads import randn_bf16
+    from oracle import akv_oracle as O
+    import torch
+
+    sh = wl.shape
+    layers = list(range(0, sh.n_layers, layer_stride))
+    oc = O.OracleCache(len(layers), sh.n_kv_heads, sh.head_dim, sh.rope_base, n_seqs=wl.n_seqs)
+    gen = "cuda" if torch.cuda.is_available() else "cpu"
+    for b, n in enumerate(wl.seq_lens):
+        for c in range((n + Hn.CHUNK - 1) // Hn.CHUNK):
+            m = min(Hn.CHUNK, n - c * Hn.CHUNK)
+            k = Hn.seq_chunk(sh, wl.data_seed, b, c, m, "k", gen)[layers]
+            v = Hn.seq_chunk(sh, wl.data_seed, b, c, m, "v", gen)[layers]
+            oc.append(b, (b << 24) + c * Hn.CHUNK + np.arange(m),
+                      k.permute(1, 0, 2, 3).cpu().double().numpy(),
+                      v.permute(1, 0, 2, 3).cpu().double().numpy())
+    q = randn_bf16((wl.n_seqs, len(layers), sh.n_q_heads, sh.head_dim), 202,
+                   device=gen).cpu().double().numpy()
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for b in range(wl.n_seqs):
+            oc.drop_reposition(b, wl.masks[b])
+        t1 = time.perf_counter()
+        for b in range(wl.n_seqs):
+            oc.decode_attention(b, q[b])
+        t2 = time.perf_counter()
+    ab = algorithmic_bytes(sh, wl.seq_lens, wl.masks)
+    frac = len(layers) / sh.n_layers
+    b_total = (ab["b_dr"] + ab["b_att"]) * frac
+    return {
+        "value": round(b_total / (t2 - t0) / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{wl.name}: layers {layers[0]}..{layers[-1]} step {layer_stride} "
+                  f"({len(layers)} of {sh.n_layers}), all tokens; fused drop+reposition "
+                  f"{t1 - t0:.2f} s + decode {t2 - t1:.2f} s on one host core, bytes scaled "
+                  f"by the layer fraction",
+        "drop_reposition_gbps": round(ab["b_dr"] * frac / (t1 - t0) / 1e9, 4),
+        "decode_gbps": round(ab["b_att"] * frac / (t2 - t1) / 1e9, 4),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c5"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-layer-stride", type=int, default=8)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the hot path shards by kv head / layer with no exchange; see DESIGN.md).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from agent_kv_cache_amd import harness as Hn
+    from agent_kv_cache_amd import workloads as W
+    from agent_kv_cache_amd.binding import lib
+
+    lib()
+    torch.cuda.set_device(0)
+    wl = W.WORKLOADS[args.workload]()
+    sh = wl.shape
+    extra = sum(Hn.moved_pages(n, m) for n, m in zip(wl.seq_lens, wl.masks)) + 8
+    cache = Hn.make_cache(sh, wl.seq_lens, extra)
+    cache.reset(None if wl.block_order is None else
+                np.concatenate([wl.block_order, np.arange(len(wl.block_order), cache.NB,
+                                                          dtype=np.int32)]))
+    Hn.fill(cache, sh, wl.seq_lens, wl.data_seed, gen_device="cuda")
+    mask = Hn.mask_tensor(cache, wl.masks)
+    q = W.randn_bf16((wl.n_seqs, sh.n_layers, sh.n_q_heads, sh.head_dim), 202, device="cuda")
+    out = torch.empty_like(q)
+    ws = torch.empty(max(256, cache.decode_workspace_bytes(sh.n_layers, sh.n_q_heads)),
+                     dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    if cache.sync_status() != 0:
+        raise RuntimeError("set-up failed on the device")
+    snap = cache.meta.clone()
+    stream = torch.cuda.current_stream()
+
+    def step():
+        cache.meta.copy_(snap)
+        cache.drop_reposition(mask)
+        cache.decode_attention(q, out, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if cache.sync_status() != 0:
+        raise RuntimeError("device reported an error during warm-up")
+    cache.profile_read("plan", reset=True)
+    cache.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    cache.profile_enable(False)
+    st = cache.sync_status()
+    if st != 0:
+        raise RuntimeError(f"device status {st}")
+    kt = {k: cache.profile_read(k) for k in ("plan", "move", "commit", "attn", "combine")}
+
+    ab = algorithmic_bytes(sh, wl.seq_lens, wl.masks)
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    value = (ab["b_dr"] + ab["b_att"]) / (ms_step * 1e-3) / 1e9
+
+    def avg(k):
+        ms, n = kt[k]
+        return ms / max(n, 1)
+
+    dr_ms = avg("plan") + avg("move") + avg("commit")
+    att_ms = avg("attn") + avg("combine")
+    move_gbps = ab["b_move"] / (avg("move") * 1e-3) / 1e9
+    attn_gbps = (ab["b_att"]) / (avg("attn") * 1e-3) / 1e9
+    dom = "move" if avg("move") >= avg("attn") else "attn"
+    dom_gbps = move_gbps if dom == "move" else attn_gbps
+    traffic = None
+    prof_json = os.path.join(ROOT, "profiles", f"{dom}_kernel_{wl.name}_counters.json")
+    if os.path.exists(prof_json):
+        try:
+            pj = json.load(open(prof_json))
+            traffic = pj.get("hbm_bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wl.name}: {wl.description}",
+            "layers": sh.n_layers, "kv_heads": sh.n_kv_heads, "head_dim": sh.head_dim,
+            "q_heads": sh.n_q_heads, "rope_base": sh.rope_base, "page_tokens": 16,
+            "sequences": wl.n_seqs, "tokens": ab["tokens"], "survivors": ab["survivors"],
+            "moved_tokens": ab["moved"], "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "move_kernel" if dom == "move" else "attn_kernel",
+            "achieved": round(dom_gbps, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(dom_gbps / PEAK_HBM_GBPS, 4),
+            "traffic": traffic,
+        },
+        "parts": {
+            "drop_reposition": {
+                "algorithmic_bytes": ab["b_dr"], "ms": round(dr_ms, 4),
+                "gbps": round(ab["b_dr"] / (dr_ms * 1e-3) / 1e9, 1),
+                "frac_of_peak": round(ab["b_dr"] / (dr_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                "kernel_ms": {k: round(avg(k), 4) for k in ("plan", "move", "commit")},
+                "move_kernel_gbps": round(move_gbps, 1),
+            },
+            "decode_attention": {
+                "algorithmic_bytes": ab["b_att"], "ms": round(att_ms, 4),
+                "gbps": round(ab["b_att"] / (att_ms * 1e-3) / 1e9, 1),
+                "frac_of_peak": round(ab["b_att"] / (att_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                "kernel_ms": {k: round(avg(k), 4) for k in ("attn", "combine")},
+                "attn_kernel_gbps": round(attn_gbps, 1),
+            },
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_layer_stride)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
