@@ -11,7 +11,9 @@ import os
 import re
 from typing import Optional
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libakv.so")
+# AKV_LIBRARY may name another build of the same ABI (e.g. a tuning variant).
+LIB_PATH = os.environ.get("AKV_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libakv.so")
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                       "include", "akv.h")
 

@@ -35,13 +35,16 @@ def common_flags():
             "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-result"]
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, defines=(), out: str = LIB, tag: str = "") -> str:
+    """Compile and link; `defines` are extra -D macros (launch-shape knobs)."""
+    bdir = os.path.join(BUILD, tag) if tag else BUILD
+    os.makedirs(bdir, exist_ok=True)
     hipcc = _hipcc()
+    dflags = [f"-D{x}" for x in defines]
 
     def compile_one(src):
-        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-        cmd = [hipcc, *common_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+        obj = os.path.join(bdir, src.replace(".hip", ".o"))
+        cmd = [hipcc, *common_flags(), *dflags, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)
@@ -51,15 +54,15 @@ def build(verbose: bool = False) -> str:
 
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

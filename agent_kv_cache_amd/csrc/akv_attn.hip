@@ -27,7 +27,13 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int kAttnWaves = 4;
+#ifndef AKV_ATTN_WAVES
+#define AKV_ATTN_WAVES 4       // waves per workgroup (pages interleaved across them)
+#endif
+#ifndef AKV_ATTN_MIN_WAVES
+#define AKV_ATTN_MIN_WAVES 3   // waves per SIMD the register budget must allow
+#endif
+constexpr int kAttnWaves = AKV_ATTN_WAVES;
 
 __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t *p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(p));
@@ -38,7 +44,7 @@ __device__ __forceinline__ short f32_to_bf16_bits(float x) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kAttnWaves * 64) void attn_kernel(
+__global__ __launch_bounds__(kAttnWaves * 64, AKV_ATTN_MIN_WAVES) void attn_kernel(
     Dev d, const uint16_t *__restrict__ q, const int32_t *__restrict__ active_len, int l0,
     int nL, int Hq, uint16_t *__restrict__ out, float *__restrict__ part, int nsplit) {
   constexpr int KC = D / 32;      // QK MFMA steps (K = 32 of d each)
@@ -46,9 +52,14 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_kernel(
   constexpr int VC = D / 32;      // 16-B V chunks per lane per page
   constexpr int C8 = D / 8;       // 16-B chunks per row
   constexpr int VROW = D + 8;     // padded LDS row, elements
-  __shared__ __attribute__((aligned(16))) uint16_t s_v[kAttnWaves][kPage][VROW];
+  // One LDS block serves two phases: per-wave V tiles in the page loop, then
+  // the per-wave (m, l, O) of the final merge.
+  constexpr int kVBytes = kAttnWaves * kPage * VROW * 2;
+  constexpr int kOBytes = kAttnWaves * 16 * D * 4;
+  __shared__ __attribute__((aligned(16))) char s_raw[kVBytes > kOBytes ? kVBytes : kOBytes];
   __shared__ float s_m[kAttnWaves][16], s_l[kAttnWaves][16];
-  __shared__ float s_o[kAttnWaves][16][D];
+  auto s_v = reinterpret_cast<uint16_t (*)[kPage][VROW]>(s_raw);
+  auto s_o = reinterpret_cast<float (*)[16][D]>(s_raw);
 
   const int s = blockIdx.x, g = blockIdx.y, bl = blockIdx.z;
   const int b = bl / nL, li = bl - b * nL, l = l0 + li;
@@ -88,6 +99,9 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_kernel(
   const size_t head_base = ((size_t)l * d.NB * d.H + g) * hstride;
   const size_t page_stride = (size_t)d.H * hstride;
 
+  // Page p's K and V are in registers at the top of an iteration.  Its V goes
+  // to LDS first, which frees the V registers for page p + 4's loads; those
+  // and page p + 4's K loads stay in flight while page p is consumed.
   bf16x8 ka[KC];
   uint4 vv[VC];
   int p = p0 + wave;
@@ -100,14 +114,21 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_kernel(
   }
   while (p < p1) {
     const int pn = p + kAttnWaves;
+    // stage V (rows past the active length are zeroed: never multiply junk)
+#pragma unroll
+    for (int c = 0; c < VC; ++c) {
+      const int ci = lane + 64 * c, row = ci / C8, col = (ci % C8) * 8;
+      uint4 v = vv[c];
+      if (p * kPage + row >= len) v = make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4 *>(&s_v[wave][row][col]) = v;
+    }
     bf16x8 kan[KC];
-    uint4 vvn[VC];
     if (pn < p1) {
       const size_t off = head_base + (size_t)trow[pn] * page_stride;
 #pragma unroll
       for (int c = 0; c < KC; ++c) kan[c] = load_bf16x8(d.k + off + hh * D + 8 * kg + 32 * c);
 #pragma unroll
-      for (int c = 0; c < VC; ++c) vvn[c] = *reinterpret_cast<const uint4 *>(d.v + off + 8 * (lane + 64 * c));
+      for (int c = 0; c < VC; ++c) vv[c] = *reinterpret_cast<const uint4 *>(d.v + off + 8 * (lane + 64 * c));
     }
     // S^T[token 4*kg + j][head hh]
     floatx4 sacc = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -132,14 +153,6 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_kernel(
     m = mnew;
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] *= alpha;
-    // stage V (rows past the active length are zeroed: never multiply junk)
-#pragma unroll
-    for (int c = 0; c < VC; ++c) {
-      const int ci = lane + 64 * c, row = ci / C8, col = (ci % C8) * 8;
-      uint4 v = vv[c];
-      if (p * kPage + row >= len) v = make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4 *>(&s_v[wave][row][col]) = v;
-    }
     const short4v pb = short4v{f32_to_bf16_bits(pj[0]), f32_to_bf16_bits(pj[1]),
                                f32_to_bf16_bits(pj[2]), f32_to_bf16_bits(pj[3])};
 #pragma unroll
@@ -151,12 +164,11 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_kernel(
     }
 #pragma unroll
     for (int c = 0; c < KC; ++c) ka[c] = kan[c];
-#pragma unroll
-    for (int c = 0; c < VC; ++c) vv[c] = vvn[c];
     p = pn;
   }
 
   // ---- merge the four waves ----
+  __syncthreads();  // all V tiles consumed before s_raw is reused
   lsum += __shfl_xor(lsum, 16, 64);
   lsum += __shfl_xor(lsum, 32, 64);
   if (kg == 0) {
@@ -196,22 +208,46 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_kernel(
   }
 }
 
-// Merge split partials of one (sequence, layer, query head) row.
+// Merge split partials of one (sequence, layer, query head) row.  All split
+// records of the row are loaded up front (independent loads in flight).
 template <int D>
 __global__ __launch_bounds__(D) void combine_kernel(const float *__restrict__ part,
                                                     uint16_t *__restrict__ out, int nsplit) {
+  constexpr int kMaxUnroll = 16;
   const size_t row = blockIdx.x;
   const int dim = threadIdx.x;
   const float *pr = part + row * nsplit * (size_t)(D + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pr[s * (D + 2)]);
-  float L = 0.f, o = 0.f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < nsplit; ++s) {
-      const float *ps = pr + s * (D + 2);
-      const float f = exp2f(ps[0] - M);
-      L += f * ps[1];
-      o += f * ps[2 + dim];
+  float M = -INFINITY, L = 0.f, o = 0.f;
+  for (int s0 = 0; s0 < nsplit; s0 += kMaxUnroll) {
+    const int n = min(kMaxUnroll, nsplit - s0);
+    float ms[kMaxUnroll], ls[kMaxUnroll], os[kMaxUnroll];
+#pragma unroll
+    for (int k = 0; k < kMaxUnroll; ++k) {
+      if (k < n) {
+        const float *ps = pr + (size_t)(s0 + k) * (D + 2);
+        ms[k] = ps[0];
+        ls[k] = ps[1];
+        os[k] = ps[2 + dim];
+      } else {
+        ms[k] = -INFINITY;
+        ls[k] = 0.f;
+        os[k] = 0.f;
+      }
+    }
+    float Mn = M;
+#pragma unroll
+    for (int k = 0; k < kMaxUnroll; ++k) Mn = fmaxf(Mn, ms[k]);
+    if (Mn != -INFINITY) {
+      const float a = exp2f(M - Mn);   // M = -inf gives 0
+      L *= a;
+      o *= a;
+#pragma unroll
+      for (int k = 0; k < kMaxUnroll; ++k) {
+        const float f = exp2f(ms[k] - Mn);
+        L += f * ls[k];
+        o += f * os[k];
+      }
+      M = Mn;
     }
   }
   out[row * D + dim] = (uint16_t)f32_to_bf16_bits(L > 0.f ? o / L : 0.f);

@@ -25,8 +25,42 @@
 
 namespace akv {
 
+// Launch-shape knobs of the move kernel (compile-time; defaults are the
+// measured best on MI355X for the configurations of the benchmark).
+#ifndef AKV_MOVE_UNROLL
+#define AKV_MOVE_UNROLL 2      // (layer, head) slices loaded before any store
+#endif
+#ifndef AKV_MOVE_MIN_WAVES
+#define AKV_MOVE_MIN_WAVES 4   // waves per SIMD the register budget must allow
+#endif
+#ifndef AKV_MOVE_NT
+#define AKV_MOVE_NT 1          // nontemporal hint on the streamed KV accesses
+#endif
+#ifndef AKV_MOVE_ITEMS_PER_WG
+#define AKV_MOVE_ITEMS_PER_WG 8
+#endif
+
 constexpr int kPlanThreads = 1024;
 constexpr int kMoveThreads = 256;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming 16-B accesses: every KV byte of a move is read once and written
+// once, so they bypass cache retention (nontemporal hint).
+__device__ __forceinline__ u32x4 ld_stream(const uint16_t *p) {
+#if AKV_MOVE_NT
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+#else
+  return *reinterpret_cast<const u32x4 *>(p);
+#endif
+}
+__device__ __forceinline__ void st_stream(uint16_t *p, u32x4 v) {
+#if AKV_MOVE_NT
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
+#else
+  *reinterpret_cast<u32x4 *>(p) = v;
+#endif
+}
 
 // ---------------------------------------------------------------------------
 // helpers
@@ -96,6 +130,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     const int32_t *__restrict__ old_pos, int mode, int move_grid) {
   __shared__ int s_wave[kPlanThreads / 64 + 1];
   __shared__ int s_fdrop, s_fpos, s_err, s_last, s_gerr;
+  // One round's gather map and deltas are staged here, then written out
+  // with consecutive lanes on consecutive entries (a lane's own survivors
+  // would otherwise hit 16 different cache lines per store instruction).
+  __shared__ int s_src[kPlanThreads * kPage], s_dlt[kPlanThreads * kPage];
   const int b = blockIdx.x, t = threadIdx.x;
   const size_t S = (size_t)d.S;
   const int len = d.lens[b];
@@ -132,27 +170,61 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     int total;
     const int excl = block_exclusive_scan<kPlanThreads>(__popc(keep), s_wave, &total);
     if (keep) {
-      int j = running + excl;
-      const int32_t *prow = d.pos + (size_t)trow[pg] * kPage;
+      // All loads of this page first (positions, old and new positions),
+      // then the stores: keeps the loads in flight together.
+      const int j0 = running + excl;
+      int p[kPage], o[kPage], qn[kPage];
+      int qprev = -1;
+      if (mode & M_REPOS) {
+        const int4 *pp = reinterpret_cast<const int4 *>(d.pos + (size_t)trow[pg] * kPage);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int4 x = pp[k];
+          p[4 * k] = x.x; p[4 * k + 1] = x.y; p[4 * k + 2] = x.z; p[4 * k + 3] = x.w;
+        }
+        if (mode & M_OLDPOS) {
+          const int4 *op = reinterpret_cast<const int4 *>(old_pos + b * S + (size_t)pg * kPage);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int4 x = op[k];
+            o[4 * k] = x.x; o[4 * k + 1] = x.y; o[4 * k + 2] = x.z; o[4 * k + 3] = x.w;
+          }
+        }
+        if (mode & M_NEWPOS) {
+          // slot r's survivor rank is j0 + (kept slots below r)
+#pragma unroll
+          for (int r = 0; r < kPage; ++r)
+            qn[r] = ((keep >> r) & 1u) ? new_pos[b * S + j0 + __popc(keep & ((1u << r) - 1u))] : 0;
+          if (j0 > 0) qprev = new_pos[b * S + j0 - 1];
+        }
+      }
+      int j = j0;
+#pragma unroll
       for (int r = 0; r < kPage; ++r) {
         if (!((keep >> r) & 1u)) continue;
         const int s = pg * kPage + r;
-        if (mode & M_DROP) d.src_map[b * S + j] = s;
+        if (mode & M_DROP) s_src[j - running] = s;
         if (mode & M_REPOS) {
-          const int p = prow[r];
-          if ((mode & M_OLDPOS) && old_pos[b * S + s] != p) err = max(err, (int)AKV_ERR_POS_MISMATCH);
+          if ((mode & M_OLDPOS) && o[r] != p[r]) err = max(err, (int)AKV_ERR_POS_MISMATCH);
           int q = j;
           if (mode & M_NEWPOS) {
-            q = new_pos[b * S + j];
-            if (q < 0 || (j > 0 && new_pos[b * S + j - 1] >= q)) err = max(err, (int)AKV_ERR_ORDER);
+            q = qn[r];
+            if (q < 0 || (j > 0 && qprev >= q)) err = max(err, (int)AKV_ERR_ORDER);
+            qprev = q;
           }
-          const int delta = q - p;
-          d.delta_map[b * S + j] = delta;
+          const int delta = q - p[r];
+          s_dlt[j - running] = delta;
           if (delta != 0 && j < fpos) fpos = j;
         }
         ++j;
       }
     }
+    __syncthreads();
+    for (int i = t; i < total; i += kPlanThreads) {
+      if (mode & M_DROP) d.src_map[b * S + running + i] = s_src[i];
+      if (mode & M_REPOS) d.delta_map[b * S + running + i] = s_dlt[i];
+    }
+    __syncthreads();
     running += total;
   }
   if (err) atomicMax(&s_err, err);
@@ -188,12 +260,18 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     si[SI_OLD_LEN] = len;
   }
   // ---- last workgroup: prefix sums over sequences, pool check, latch ----
-  __threadfence();
-  __syncthreads();
-  if (t == 0) s_last = (atomicAdd(&d.ctl[CTL_DONE], 1) == (int)gridDim.x - 1);
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+  // (device-wide fences and the ticket are only needed with several
+  // workgroups; a single sequence's workgroup is the last one by itself)
+  if (gridDim.x > 1) {
+    __threadfence();
+    __syncthreads();
+    if (t == 0) s_last = (atomicAdd(&d.ctl[CTL_DONE], 1) == (int)gridDim.x - 1);
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+  } else {
+    __syncthreads();
+  }
   if (t == 0) s_gerr = 0;
   __syncthreads();
   int run_m = 0, run_i = 0, run_f = 0;
@@ -239,13 +317,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
       d.ctl[CTL_F_TOTAL] = run_f;
       d.ctl[CTL_FC_OLD] = fc;
       d.ctl[CTL_BASE] = fc - run_m;
-      // Layers per move item: as many as keep ~8 items per workgroup of the
-      // persistent grid, so the cos/sin set-up of an item is amortised over
-      // as many (layer, head) slices as the load balance allows.
+      // Layers per move item: the largest divisor of L that still leaves at
+      // least 8 items per workgroup of the persistent grid, so the cos/sin
+      // set-up of an item is amortised over as many (layer, head) slices as
+      // the load balance allows and all items are the same size.
       const long long pages = (long long)run_m + run_i;
-      const long long target = 8LL * move_grid;
-      long long lpi = pages > 0 ? (pages * d.L) / target : d.L;
-      lpi = lpi < 1 ? 1 : (lpi > d.L ? d.L : lpi);
+      const long long target = (long long)AKV_MOVE_ITEMS_PER_WG * move_grid;
+      int lpi = 1;
+      for (int c = d.L; c >= 1; --c)
+        if (d.L % c == 0 && pages * (d.L / c) >= target) { lpi = c; break; }
       d.ctl[CTL_LPI] = (int)lpi;
     }
     d.ctl[CTL_DONE] = 0;
@@ -257,7 +337,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
 // ---------------------------------------------------------------------------
 // Rotate 8 NeoX pairs: lo holds x_i (8 bf16), hi holds y_i = k[i + d/2].
 // x' = x cos - y sin, y' = y cos + x sin in fp64, one rounding to bf16.
-__device__ __forceinline__ void rotate8(uint4 &lo, uint4 &hi, const double *c, const double *s) {
+__device__ __forceinline__ void rotate8(u32x4 &lo, u32x4 &hi, const double2 *cs) {
   uint32_t a[4] = {lo.x, lo.y, lo.z, lo.w};
   uint32_t bb[4] = {hi.x, hi.y, hi.z, hi.w};
 #pragma unroll
@@ -267,24 +347,25 @@ __device__ __forceinline__ void rotate8(uint4 &lo, uint4 &hi, const double *c, c
     for (int e = 0; e < 2; ++e) {
       const double x = (double)bf16_to_f32((a[q] >> (16 * e)) & 0xFFFFu);
       const double y = (double)bf16_to_f32((bb[q] >> (16 * e)) & 0xFFFFu);
-      const double cc = c[2 * q + e], ss = s[2 * q + e];
+      const double2 v = cs[2 * q + e];
+      const double cc = v.x, ss = v.y;
       xo[e] = f64_to_f32_for_bf16(fma(x, cc, -(y * ss)));
       yo[e] = f64_to_f32_for_bf16(fma(y, cc, x * ss));
     }
     a[q] = f32x2_to_bf16x2(xo[0], xo[1]);
     bb[q] = f32x2_to_bf16x2(yo[0], yo[1]);
   }
-  lo = make_uint4(a[0], a[1], a[2], a[3]);
-  hi = make_uint4(bb[0], bb[1], bb[2], bb[3]);
+  lo = u32x4{a[0], a[1], a[2], a[3]};
+  hi = u32x4{bb[0], bb[1], bb[2], bb[3]};
 }
 
 template <int D>
-__global__ __launch_bounds__(kMoveThreads) void move_kernel(Dev d, int mode) {
+__global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(Dev d, int mode) {
   constexpr int HALF = D / 2;
   constexpr int CH = D / 16;             // 16-B chunks per half row
   constexpr int TPH = kPage * CH;        // threads per (layer, head) slice
   constexpr int NS = kMoveThreads / TPH; // slices per pass
-  constexpr int U = 2;                   // slices loaded before any store
+  constexpr int U = AKV_MOVE_UNROLL;      // slices loaded before any store
   __shared__ int s_b, s_po, s_dst, s_mv;
   __shared__ int s_blk[kPage], s_row[kPage], s_valid[kPage], s_delta[kPage], s_rep[kPage];
   __shared__ int s_repval[kPage], s_nrep;
@@ -375,15 +456,8 @@ __global__ __launch_bounds__(kMoveThreads) void move_kernel(Dev d, int mode) {
     }
     const bool valid = s_valid[r] != 0;
     const int delta = s_delta[r];
-    double cc[8], ss[8];
-    if (rot_any && delta != 0) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const double2 v = s_cs[s_rep[r]][8 * pc + e];
-        cc[e] = v.x;
-        ss[e] = v.y;
-      }
-    }
+    // cos/sin of this thread's 8 pairs stay in LDS and are read per use
+    const double2 *cs_row = &s_cs[(rot_any && delta != 0) ? s_rep[r] : 0][8 * pc];
     const bool do_k = valid ? (mv || delta != 0) : mv;
     const bool do_v = mv;
     const int l0 = lc * lpi, l1 = min(d.L, l0 + lpi);
@@ -392,7 +466,7 @@ __global__ __launch_bounds__(kMoveThreads) void move_kernel(Dev d, int mode) {
     const size_t dst_row = (size_t)dst * d.H * hstride + (size_t)r * D + 8 * pc;
     if (!do_k) continue;
     for (int i0 = slot; i0 < nsl; i0 += NS * U) {
-      uint4 klo[U], khi[U], vlo[U], vhi[U];
+      u32x4 klo[U], khi[U], vlo[U], vhi[U];
       size_t dofs[U];
       bool on[U];
 #pragma unroll
@@ -402,26 +476,26 @@ __global__ __launch_bounds__(kMoveThreads) void move_kernel(Dev d, int mode) {
         const int l = l0 + idx / d.H, h = idx % d.H;
         const size_t off = (size_t)l * lstride + (size_t)h * hstride;
         dofs[u] = dst_row + off;
-        klo[u] = khi[u] = vlo[u] = vhi[u] = make_uint4(0, 0, 0, 0);
+        klo[u] = khi[u] = vlo[u] = vhi[u] = u32x4{0u, 0u, 0u, 0u};
         if (on[u] && valid) {
           const size_t so = src_row + off;
-          klo[u] = *reinterpret_cast<const uint4 *>(d.k + so);
-          khi[u] = *reinterpret_cast<const uint4 *>(d.k + so + HALF);
+          klo[u] = ld_stream(d.k + so);
+          khi[u] = ld_stream(d.k + so + HALF);
           if (do_v) {
-            vlo[u] = *reinterpret_cast<const uint4 *>(d.v + so);
-            vhi[u] = *reinterpret_cast<const uint4 *>(d.v + so + HALF);
+            vlo[u] = ld_stream(d.v + so);
+            vhi[u] = ld_stream(d.v + so + HALF);
           }
         }
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (!on[u]) continue;
-        if (valid && delta != 0) rotate8(klo[u], khi[u], cc, ss);
-        *reinterpret_cast<uint4 *>(d.k + dofs[u]) = klo[u];
-        *reinterpret_cast<uint4 *>(d.k + dofs[u] + HALF) = khi[u];
+        if (valid && delta != 0) rotate8(klo[u], khi[u], cs_row);
+        st_stream(d.k + dofs[u], klo[u]);
+        st_stream(d.k + dofs[u] + HALF, khi[u]);
         if (do_v) {
-          *reinterpret_cast<uint4 *>(d.v + dofs[u]) = vlo[u];
-          *reinterpret_cast<uint4 *>(d.v + dofs[u] + HALF) = vhi[u];
+          st_stream(d.v + dofs[u], vlo[u]);
+          st_stream(d.v + dofs[u] + HALF, vhi[u]);
         }
       }
     }
@@ -595,6 +669,14 @@ hipError_t launch_move(const Dev &d, int mode, int grid, hipStream_t st) {
   else
     hipLaunchKernelGGL(move_kernel<64>, dim3(grid), dim3(kMoveThreads), 0, st, d, mode);
   return hipGetLastError();
+}
+
+int move_blocks_per_cu(int D) {
+  int n = 0;
+  const hipError_t e = (D == 128)
+      ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, move_kernel<128>, kMoveThreads, 0)
+      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, move_kernel<64>, kMoveThreads, 0);
+  return (e == hipSuccess && n > 0) ? n : 2;
 }
 
 hipError_t launch_commit(const Dev &d, hipStream_t st) {

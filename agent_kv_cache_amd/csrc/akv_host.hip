@@ -71,9 +71,13 @@ struct Timed {
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+#ifndef AKV_ATTN_WG_PER_CU
+#define AKV_ATTN_WG_PER_CU 8   // decode workgroups per CU the split count aims for
+#endif
+
 int nsplit_for(const akv_cache *c, int nL) {
   const long long base = (long long)c->desc.n_seqs * nL * c->desc.n_kv_heads;
-  const long long target = 8LL * c->n_cu;
+  const long long target = (long long)AKV_ATTN_WG_PER_CU * c->n_cu;
   long long ns = (target + base - 1) / base;
   const long long cap = std::max(1, c->desc.max_blocks_per_seq / 4);
   ns = std::min(ns, cap);
@@ -161,7 +165,7 @@ akv_status akv_cache_init(const akv_cache_desc *d, akv_cache **out) {
     delete c;
     return AKV_ERR_HIP;
   }
-  c->move_grid = 8 * c->n_cu;
+  c->move_grid = akv::move_blocks_per_cu(d->head_dim) * c->n_cu;
 
   // theta_i = base^(-2i/d), double, uploaded once.
   double theta[akv::kMaxHalf] = {};
@@ -223,7 +227,8 @@ akv_status akv_drop(akv_cache *c, const uint8_t *drop_mask, void *stream) {
 
 akv_status akv_reposition(akv_cache *c, const int32_t *old_pos, const int32_t *new_pos,
                           void *stream) {
-  if (!c) return AKV_ERR_ARG;
+  if (!c || (old_pos && !aligned(old_pos, 16)) || (new_pos && !aligned(new_pos, 16)))
+    return AKV_ERR_ARG;
   int mode = akv::M_REPOS;
   if (new_pos) mode |= akv::M_NEWPOS;
   if (old_pos) mode |= akv::M_OLDPOS;
@@ -232,7 +237,8 @@ akv_status akv_reposition(akv_cache *c, const int32_t *old_pos, const int32_t *n
 
 akv_status akv_drop_reposition(akv_cache *c, const uint8_t *drop_mask, const int32_t *new_pos,
                                void *stream) {
-  if (!c || !drop_mask || !aligned(drop_mask, 16)) return AKV_ERR_ARG;
+  if (!c || !drop_mask || !aligned(drop_mask, 16) || (new_pos && !aligned(new_pos, 16)))
+    return AKV_ERR_ARG;
   int mode = akv::M_DROP | akv::M_REPOS;
   if (new_pos) mode |= akv::M_NEWPOS;
   return run_compaction(c, drop_mask, new_pos, nullptr, mode, stream);

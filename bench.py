@@ -108,6 +108,33 @@ def cpu_baseline(wl, layer_stride: int, time_budget_s: float = 25.0):
     }
 
 
+def calibrate(nbytes: int, reps: int):
+    """Achieved GB/s of torch's device copy (read+write), fill (write) and a
+    max-reduction (read) over `nbytes`: the plain streaming kernels that bound
+    what a copy-shaped or read-shaped kernel can reach on this GPU."""
+    import torch
+    n = nbytes // 4
+    a = torch.ones(n, dtype=torch.int32, device="cuda")
+    b = torch.empty_like(a)
+    out = {}
+    for name, fn, moved in (("copy", lambda: b.copy_(a), 2 * n * 4),
+                            ("fill", lambda: b.fill_(7), n * 4),
+                            ("read_max", lambda: torch.amax(a), n * 4)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(reps):
+            fn()
+        ev1.record()
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / reps
+        out[name] = {"bytes": moved, "ms": round(ms, 4), "gbps": round(moved / ms / 1e6, 1),
+                     "frac_of_peak": round(moved / ms / 1e6 / PEAK_HBM_GBPS, 4)}
+    return {"calibration": out, "buffer_bytes": nbytes}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,6 +143,10 @@ def main():
     ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layer-stride", type=int, default=8)
+    ap.add_argument("--calibrate", type=int, default=0, metavar="BYTES",
+                    help="instead of the workload, time plain device copy / fill / read "
+                         "kernels over BYTES (the reference kernels whose counter readings "
+                         "scale the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -129,8 +160,11 @@ def main():
     from agent_kv_cache_amd import workloads as W
     from agent_kv_cache_amd.binding import lib
 
-    lib()
     torch.cuda.set_device(0)
+    if args.calibrate:
+        print(json.dumps(calibrate(args.calibrate, args.steps)), flush=True)
+        return
+    lib()
     wl = W.WORKLOADS[args.workload]()
     sh = wl.shape
     extra = sum(Hn.moved_pages(n, m) for n, m in zip(wl.seq_lens, wl.masks)) + 8
