@@ -49,34 +49,46 @@ def make_cache(shape: Shape, seq_lens: Sequence[int], extra_pages: int,
 
 
 def fill(cache: AkvCache, shape: Shape, seq_lens: Sequence[int], data_seed: int,
-         gen_device: str = "cuda", token_base: Optional[List[int]] = None):
+         gen_device: str = "cuda", token_base: Optional[List[int]] = None,
+         max_tokens_per_call: int = 16384, progress=None):
     """Append every sequence's tokens chunk by chunk (seeded per chunk).
 
     Token ids of sequence b are token_base[b] + 0, 1, ... (default b * 2^24).
+    Each akv_append call carries at most `max_tokens_per_call` tokens so the
+    set-up temporaries stay small next to a large pool.
     """
     import torch
     dev = cache.device
     B = len(seq_lens)
     nchunks = max((int(n) + CHUNK - 1) // CHUNK for n in seq_lens) if B else 0
     for c in range(nchunks):
-        counts, ks, vs, toks = [], [], [], []
+        group = []
         for b, n in enumerate(seq_lens):
             m = max(0, min(CHUNK, int(n) - c * CHUNK))
-            counts.append(m)
             if m:
+                group.append((b, m))
+        while group:
+            take, tot = [], 0
+            while group and (not take or tot + group[0][1] <= max_tokens_per_call):
+                take.append(group.pop(0))
+                tot += take[-1][1]
+            counts = [0] * B
+            ks, vs, toks = [], [], []
+            for b, m in take:
+                counts[b] = m
                 ks.append(seq_chunk(shape, data_seed, b, c, m, "k", gen_device).to(dev))
                 vs.append(seq_chunk(shape, data_seed, b, c, m, "v", gen_device).to(dev))
                 base = (b << 24) if token_base is None else token_base[b]
                 toks.append(torch.arange(base + c * CHUNK, base + c * CHUNK + m,
                                          dtype=torch.int32, device=dev))
-        n_new = sum(counts)
-        cnt = torch.tensor(counts, dtype=torch.int32, device=dev)
-        if n_new == 0:
-            continue
-        k = torch.cat(ks, dim=1).contiguous()
-        v = torch.cat(vs, dim=1).contiguous()
-        cache.append(cnt, n_new, k, v, torch.cat(toks))
-        del k, v, ks, vs
+            k = torch.cat(ks, dim=1).contiguous() if len(ks) > 1 else ks[0]
+            v = torch.cat(vs, dim=1).contiguous() if len(vs) > 1 else vs[0]
+            del ks, vs
+            cache.append(torch.tensor(counts, dtype=torch.int32, device=dev), tot, k, v,
+                         torch.cat(toks))
+            del k, v
+        if progress:
+            progress(c + 1, nchunks)
 
 
 def mask_tensor(cache: AkvCache, masks: Sequence[Optional[np.ndarray]]):

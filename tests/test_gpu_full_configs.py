@@ -1,0 +1,136 @@
+"""Full-size GPU parity for the long-history, ragged-batch and 70B-shaped
+configurations.  Indices, positions, lengths and next positions are compared
+for every sequence; K/V and attention on sampled (sequence, layer) pairs that
+the fp64 oracle can hold."""
+import time
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+from agent_kv_cache_amd import harness as Hn  # noqa: E402
+from agent_kv_cache_amd import workloads as W  # noqa: E402
+from oracle import akv_oracle as O  # noqa: E402
+
+from gpu_util import (bits, check_attention, check_kv, check_meta, oracle_for,  # noqa: E402
+                      q_tensor, say, to_f64)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from agent_kv_cache_amd.binding import lib
+    lib()
+
+
+def _decode(cache, q):
+    out = torch.empty_like(q)
+    ws = torch.empty(max(256, cache.decode_workspace_bytes(q.shape[1], q.shape[2])),
+                     dtype=torch.uint8, device=cache.device)
+    cache.decode_attention(q, out, ws)
+    return out
+
+
+def _batch_config(wl, seqs, layers):
+    sh = wl.shape
+    t0 = time.time()
+    extra = sum(Hn.moved_pages(n, m) for n, m in zip(wl.seq_lens, wl.masks)) + 8
+    cache = Hn.make_cache(sh, wl.seq_lens, extra)
+    order = None
+    if wl.block_order is not None:
+        order = np.concatenate([wl.block_order,
+                                np.arange(len(wl.block_order), cache.NB, dtype=np.int32)])
+    cache.reset(order)
+    Hn.fill(cache, sh, wl.seq_lens, wl.data_seed, gen_device="cuda",
+            progress=lambda c, n: say(f"  fill chunk {c}/{n} ({time.time() - t0:.0f}s)"))
+    assert cache.sync_status() == 0
+    say(f"{wl.name}: filled {wl.total_tokens} tokens, {cache.NB} pages")
+    meta = oracle_for(sh, wl.seq_lens, wl.data_seed, with_kv=False)
+    kvo = oracle_for(sh, wl.seq_lens, wl.data_seed, layers=layers, gen_device="cuda", seqs=seqs)
+    cache.drop_reposition(Hn.mask_tensor(cache, wl.masks))
+    assert cache.sync_status() == 0
+    for b in range(wl.n_seqs):
+        meta.drop_reposition(b, wl.masks[b])
+    for i, b in enumerate(seqs):
+        kvo.drop_reposition(i, wl.masks[b])
+    say(f"{wl.name}: drop+reposition done ({time.time() - t0:.0f}s)")
+    check_meta(cache, meta)
+    worst = check_kv(cache, kvo, layers=layers, k_ulp=1, seqs=seqs)
+    say(f"{wl.name}: meta exact for {wl.n_seqs} seqs; worst K ulp on samples {worst}")
+    q = q_tensor(sh, wl.n_seqs, sh.n_layers, 202, device="cuda")
+    out = _decode(cache, q)
+    err = check_attention(cache, kvo, q, out, layers=layers, seqs=seqs)
+    say(f"{wl.name}: attention max abs err {err:.2e} ({time.time() - t0:.0f}s)")
+    return worst, err
+
+
+@pytest.mark.timeout(600)
+def test_c5_llama70b_shape_full():
+    _batch_config(W.c5(), seqs=[0, 3], layers=[0, 40, 79])
+
+
+@pytest.mark.timeout(900)
+def test_c3_ragged_batch_full():
+    _batch_config(W.c3(), seqs=[0, 21, 63], layers=[0, 31])
+
+
+@pytest.mark.timeout(600)
+def test_c4_long_history_replay():
+    """50-turn history (131072 tokens appended, 47 drops, 16 repositions):
+    GPU replay vs oracle replay after every op; final decode with 64 heads."""
+    sh = W.SHAPES["c4"]
+    hist = W.c4_history()
+    layers = [0, 35]
+    t0 = time.time()
+    cache = Hn.make_cache(sh, [1], 4096, max_blocks_per_seq=4096)
+    cache.reset()
+    meta = O.OracleCache(sh.n_layers, sh.n_kv_heads, sh.head_dim, sh.rope_base, with_kv=False)
+    kvo = O.OracleCache(len(layers), sh.n_kv_heads, sh.head_dim, sh.rope_base)
+    n_rot = 0
+    dev = cache.device
+    for step, op in enumerate(hist.ops):
+        if op[0] == "append":
+            mid, n = op[1], op[2]
+            k = W.randn_bf16((sh.n_layers, n, sh.n_kv_heads, sh.head_dim), 104_000 + 2 * mid, dev)
+            v = W.randn_bf16((sh.n_layers, n, sh.n_kv_heads, sh.head_dim), 104_001 + 2 * mid, dev)
+            tid = np.arange(hist.msg_start[mid], hist.msg_start[mid] + n)
+            cache.append(torch.tensor([n], dtype=torch.int32, device=dev), n, k, v,
+                         torch.tensor(tid, dtype=torch.int32, device=dev))
+            meta.append(0, tid)
+            kvo.append(0, tid, to_f64(k[layers].permute(1, 0, 2, 3)),
+                       to_f64(v[layers].permute(1, 0, 2, 3)))
+        else:
+            gtok, _, _ = cache.seq_state(0)
+            if op[0] == "repos":
+                cache.reposition()
+                meta.reposition(0)
+                kvo.reposition(0)
+            else:
+                gm = W.mask_for_messages(gtok, hist, op[1])
+                om = W.mask_for_messages(meta.seqs[0].token_ids, hist, op[1])
+                if op[0] == "drop":
+                    cache.drop(Hn.mask_tensor(cache, [gm]))
+                    meta.drop(0, om)
+                    kvo.drop(0, om)
+                else:
+                    cache.drop_reposition(Hn.mask_tensor(cache, [gm]))
+                    meta.drop_reposition(0, om)
+                    kvo.drop_reposition(0, om)
+            n_rot += op[0] != "drop"
+        assert cache.sync_status() == 0, (step, op)
+        if op[0] != "append" or step == len(hist.ops) - 1:
+            check_meta(cache, meta)
+            worst = check_kv(cache, kvo, layers=layers, k_ulp=max(1, n_rot))
+        if step % 20 == 0:
+            say(f"c4 op {step}/{len(hist.ops)} {op[0]} active {len(meta.seqs[0])} "
+                f"next_pos {meta.seqs[0].next_pos} ({time.time() - t0:.0f}s)")
+    say(f"c4 final: active {len(meta.seqs[0])}, next_pos {meta.seqs[0].next_pos}, "
+        f"worst K ulp {worst}")
+    q = q_tensor(sh, 1, sh.n_layers, 204, device="cuda")
+    out = _decode(cache, q)
+    err = check_attention(cache, kvo, q, out, layers=layers)
+    say(f"c4 attention max abs err {err:.2e}")
