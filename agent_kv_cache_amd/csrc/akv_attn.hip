@@ -266,6 +266,14 @@ hipError_t launch_attention(const Dev &d, const uint16_t *q, const int32_t *acti
   return hipGetLastError();
 }
 
+int attn_blocks_per_cu(int D) {
+  int n = 0;
+  const hipError_t e = (D == 128)
+      ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_kernel<128>, kAttnWaves * 64, 0)
+      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_kernel<64>, kAttnWaves * 64, 0);
+  return (e == hipSuccess && n > 0) ? n : 2;
+}
+
 hipError_t launch_combine(const float *part, uint16_t *out, int rows, int nsplit, int D,
                           hipStream_t st) {
   if (D == 128)

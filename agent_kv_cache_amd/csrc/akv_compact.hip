@@ -36,9 +36,6 @@ namespace akv {
 #ifndef AKV_MOVE_NT
 #define AKV_MOVE_NT 1          // nontemporal hint on the streamed KV accesses
 #endif
-#ifndef AKV_MOVE_ITEMS_PER_WG
-#define AKV_MOVE_ITEMS_PER_WG 8
-#endif
 
 constexpr int kPlanThreads = 1024;
 constexpr int kMoveThreads = 256;
@@ -127,7 +124,7 @@ __device__ __forceinline__ float f64_to_f32_for_bf16(double x) {
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     Dev d, const uint8_t *__restrict__ mask, const int32_t *__restrict__ new_pos,
-    const int32_t *__restrict__ old_pos, int mode, int move_grid) {
+    const int32_t *__restrict__ old_pos, int mode) {
   __shared__ int s_wave[kPlanThreads / 64 + 1];
   __shared__ int s_fdrop, s_fpos, s_err, s_last, s_gerr;
   // One round's gather map and deltas are staged here, then written out
@@ -202,8 +199,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
 #pragma unroll
       for (int r = 0; r < kPage; ++r) {
         if (!((keep >> r) & 1u)) continue;
-        const int s = pg * kPage + r;
-        if (mode & M_DROP) s_src[j - running] = s;
+        if (mode & M_DROP) s_src[j - running] = trow[pg] * kPage + r;   // physical slot
         if (mode & M_REPOS) {
           if ((mode & M_OLDPOS) && o[r] != p[r]) err = max(err, (int)AKV_ERR_POS_MISMATCH);
           int q = j;
@@ -317,16 +313,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
       d.ctl[CTL_F_TOTAL] = run_f;
       d.ctl[CTL_FC_OLD] = fc;
       d.ctl[CTL_BASE] = fc - run_m;
-      // Layers per move item: the largest divisor of L that still leaves at
-      // least 8 items per workgroup of the persistent grid, so the cos/sin
-      // set-up of an item is amortised over as many (layer, head) slices as
-      // the load balance allows and all items are the same size.
-      const long long pages = (long long)run_m + run_i;
-      const long long target = (long long)AKV_MOVE_ITEMS_PER_WG * move_grid;
-      int lpi = 1;
-      for (int c = d.L; c >= 1; --c)
-        if (d.L % c == 0 && pages * (d.L / c) >= target) { lpi = c; break; }
-      d.ctl[CTL_LPI] = (int)lpi;
     }
     d.ctl[CTL_DONE] = 0;
   }
@@ -359,6 +345,12 @@ __device__ __forceinline__ void rotate8(u32x4 &lo, u32x4 &hi, const double2 *cs)
   hi = u32x4{bb[0], bb[1], bb[2], bb[3]};
 }
 
+// Work split: the rebuilt pages (moved first, then in-place) times the L
+// layers form U = pages * L (page, layer) units, ordered page-major.  Workgroup
+// w takes the contiguous units [w*U/G, (w+1)*U/G), so every workgroup moves
+// the same number of (layer, page) slices whatever the page count, and the
+// per-page set-up (row sources, deltas, cos/sin) is done once per page it
+// touches.
 template <int D>
 __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(Dev d, int mode) {
   constexpr int HALF = D / 2;
@@ -367,27 +359,30 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
   constexpr int NS = kMoveThreads / TPH; // slices per pass
   constexpr int U = AKV_MOVE_UNROLL;      // slices loaded before any store
   __shared__ int s_b, s_po, s_dst, s_mv;
-  __shared__ int s_blk[kPage], s_row[kPage], s_valid[kPage], s_delta[kPage], s_rep[kPage];
+  __shared__ int s_src[kPage], s_valid[kPage], s_delta[kPage], s_rep[kPage];
   __shared__ int s_repval[kPage], s_nrep;
   __shared__ double2 s_cs[kPage][HALF];
 
   if (d.ctl[CTL_OP_OK] == 0) return;
   const int Tm = d.ctl[CTL_T_MOVE], Ti = d.ctl[CTL_T_INPLACE];
-  const int npages = Tm + Ti;
+  const long long npages = (long long)Tm + Ti;
   if (npages == 0) return;
-  const int lpi = d.ctl[CTL_LPI];
   const int fc_old = d.ctl[CTL_FC_OLD];
-  const int nlc = (d.L + lpi - 1) / lpi;
-  const int nitems = npages * nlc;
+  const long long units = npages * d.L;
+  const long long u0 = units * blockIdx.x / gridDim.x;
+  const long long u1 = units * (blockIdx.x + 1) / gridDim.x;
   const int t = threadIdx.x;
   const int r = (t % TPH) / CH, pc = t % CH, slot = t / TPH;
   const size_t S = (size_t)d.S;
   const size_t hstride = (size_t)kPage * D;
   const size_t lstride = (size_t)d.NB * d.H * hstride;
+  const bool rot_any = (mode & M_REPOS) != 0;
 
-  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
-    const int lc = item / npages, pg = item - lc * npages;
-    __syncthreads();  // LDS of the previous item is no longer read
+  for (long long pgl = u0 / d.L; pgl * d.L < u1; ++pgl) {
+    const int pg = (int)pgl;
+    const int l0 = (int)(max(u0, pgl * d.L) - pgl * d.L);
+    const int l1 = (int)(min(u1, (pgl + 1) * d.L) - pgl * d.L);
+    __syncthreads();  // LDS of the previous page is no longer read
     if (t == 0) {
       const bool mv = pg < Tm;
       const int key = mv ? pg : pg - Tm;
@@ -403,7 +398,7 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
       s_po = po;
       s_mv = mv;
       s_dst = mv ? d.free_stack[fc_old - 1 - pg] : d.table[(size_t)lo * d.maxpg + po];
-      if (mv && lc == 0) d.stage[pg] = s_dst;
+      if (mv && l0 == 0) d.stage[pg] = s_dst;
     }
     __syncthreads();
     const int b = s_b, po = s_po, dst = s_dst;
@@ -412,25 +407,25 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
       const int rnew = d.seq_info[(size_t)b * kSeqInfo + SI_NEW_LEN];
       const int j = po * kPage + t;
       const bool valid = j < rnew;
-      const int i = !valid ? 0 : ((mv && (mode & M_DROP)) ? d.src_map[b * S + j] : j);
+      // physical source slot (page * 16 + row); in place: the slot itself
+      const int src = !valid ? 0
+                      : ((mv && (mode & M_DROP)) ? d.src_map[b * S + j]
+                                                 : d.table[(size_t)b * d.maxpg + po] * kPage + t);
       const int delta = (valid && (mode & M_REPOS)) ? d.delta_map[b * S + j] : 0;
-      const int blk = valid ? d.table[(size_t)b * d.maxpg + (i >> 4)] : 0;
-      s_blk[t] = blk;
-      s_row[t] = i & 15;
+      s_src[t] = src;
       s_valid[t] = valid;
       s_delta[t] = delta;
-      if (lc == 0) {
-        const size_t so = (size_t)blk * kPage + (i & 15), dn = (size_t)dst * kPage + t;
+      if (l0 == 0) {
+        const size_t dn = (size_t)dst * kPage + t;
         if (mv) {
-          d.pos[dn] = valid ? d.pos[so] + delta : -1;
-          d.tok[dn] = valid ? d.tok[so] : -1;
+          d.pos[dn] = valid ? d.pos[src] + delta : -1;
+          d.tok[dn] = valid ? d.tok[src] : -1;
         } else if (valid && delta != 0) {
           d.pos[dn] += delta;
         }
       }
     }
     __syncthreads();
-    const bool rot_any = (mode & M_REPOS) != 0;
     if (rot_any) {
       if (t == 0) {
         int n = 0;
@@ -460,11 +455,11 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
     const double2 *cs_row = &s_cs[(rot_any && delta != 0) ? s_rep[r] : 0][8 * pc];
     const bool do_k = valid ? (mv || delta != 0) : mv;
     const bool do_v = mv;
-    const int l0 = lc * lpi, l1 = min(d.L, l0 + lpi);
-    const int nsl = (l1 - l0) * d.H;
-    const size_t src_row = (size_t)s_blk[r] * d.H * hstride + (size_t)s_row[r] * D + 8 * pc;
-    const size_t dst_row = (size_t)dst * d.H * hstride + (size_t)r * D + 8 * pc;
     if (!do_k) continue;
+    const int nsl = (l1 - l0) * d.H;
+    const int sp = s_src[r];
+    const size_t src_row = (size_t)(sp >> 4) * d.H * hstride + (size_t)(sp & 15) * D + 8 * pc;
+    const size_t dst_row = (size_t)dst * d.H * hstride + (size_t)r * D + 8 * pc;
     for (int i0 = slot; i0 < nsl; i0 += NS * U) {
       u32x4 klo[U], khi[U], vlo[U], vhi[U];
       size_t dofs[U];
@@ -657,9 +652,9 @@ __global__ void reset_kernel(Dev d, const int32_t *order) {
 // launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_plan(const Dev &d, const uint8_t *mask, const int32_t *new_pos,
-                       const int32_t *old_pos, int mode, int move_grid, hipStream_t st) {
+                       const int32_t *old_pos, int mode, hipStream_t st) {
   hipLaunchKernelGGL(plan_kernel, dim3(d.B), dim3(kPlanThreads), 0, st, d, mask, new_pos,
-                     old_pos, mode, move_grid);
+                     old_pos, mode);
   return hipGetLastError();
 }
 

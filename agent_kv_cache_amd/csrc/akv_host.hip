@@ -19,6 +19,7 @@ struct akv_cache {
   int device = 0;
   int n_cu = 256;
   int move_grid = 2048;
+  int attn_per_cu = 2;
   bool profile = false;
   struct Rec {
     int kernel;
@@ -71,17 +72,29 @@ struct Timed {
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-#ifndef AKV_ATTN_WG_PER_CU
-#define AKV_ATTN_WG_PER_CU 8   // decode workgroups per CU the split count aims for
-#endif
-
+// Split count of the decode grid.  The host never reads device lengths, so
+// the choice uses only (sequences x layers x kv heads) rows and the resident
+// capacity (workgroups per CU from the occupancy API x CUs): at least one
+// full round, and among up to 4x that many splits the one whose last round of
+// workgroups is fullest (ties: fewer splits, less combine work).  Each split's
+// page range is then cut on the device from the actual length.
 int nsplit_for(const akv_cache *c, int nL) {
-  const long long base = (long long)c->desc.n_seqs * nL * c->desc.n_kv_heads;
-  const long long target = (long long)AKV_ATTN_WG_PER_CU * c->n_cu;
-  long long ns = (target + base - 1) / base;
-  const long long cap = std::max(1, c->desc.max_blocks_per_seq / 4);
-  ns = std::min(ns, cap);
-  return (int)std::max(1LL, ns);
+  const long long rows = (long long)c->desc.n_seqs * nL * c->desc.n_kv_heads;
+  const long long cap = (long long)c->attn_per_cu * c->n_cu;
+  const long long max_ns = std::max(1, c->desc.max_blocks_per_seq / 4);
+  const long long ns_min = std::min(max_ns, std::max(1LL, (cap + rows - 1) / rows));
+  long long best = ns_min;
+  double best_eff = 0.0;
+  for (long long ns = ns_min; ns <= std::min(max_ns, 4 * ns_min); ++ns) {
+    const long long wg = rows * ns;
+    const long long rounds = (wg + cap - 1) / cap;
+    const double eff = (double)wg / (double)(rounds * cap);
+    if (eff > best_eff + 1e-9) {
+      best_eff = eff;
+      best = ns;
+    }
+  }
+  return (int)best;
 }
 
 akv_status run_compaction(akv_cache *c, const uint8_t *mask, const int32_t *new_pos,
@@ -89,7 +102,7 @@ akv_status run_compaction(akv_cache *c, const uint8_t *mask, const int32_t *new_
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   {
     Timed tm(c, AKV_KERNEL_PLAN, st);
-    AKV_HIP(akv::launch_plan(c->dev, mask, new_pos, old_pos, mode, c->move_grid, st));
+    AKV_HIP(akv::launch_plan(c->dev, mask, new_pos, old_pos, mode, st));
   }
   {
     Timed tm(c, AKV_KERNEL_MOVE, st);
@@ -166,6 +179,7 @@ akv_status akv_cache_init(const akv_cache_desc *d, akv_cache **out) {
     return AKV_ERR_HIP;
   }
   c->move_grid = akv::move_blocks_per_cu(d->head_dim) * c->n_cu;
+  c->attn_per_cu = akv::attn_blocks_per_cu(d->head_dim);
 
   // theta_i = base^(-2i/d), double, uploaded once.
   double theta[akv::kMaxHalf] = {};

@@ -22,7 +22,6 @@ enum Ctl : int {
   CTL_F_TOTAL = 5,    // pages returned to the free stack
   CTL_BASE = 6,       // free_count before the op minus CTL_T_MOVE
   CTL_FC_OLD = 7,     // free_count before the op
-  CTL_LPI = 8,        // layers per move item chosen by the plan
   CTL_COUNT = 64
 };
 
@@ -84,7 +83,7 @@ inline ScratchLayout scratch_layout(int B, int S, int NB) {
 
 // Launchers (each in the .hip file that defines its kernels).
 hipError_t launch_plan(const Dev &d, const uint8_t *mask, const int32_t *new_pos,
-                       const int32_t *old_pos, int mode, int move_grid, hipStream_t st);
+                       const int32_t *old_pos, int mode, hipStream_t st);
 hipError_t launch_move(const Dev &d, int mode, int grid, hipStream_t st);
 hipError_t launch_commit(const Dev &d, hipStream_t st);
 int move_blocks_per_cu(int D);
@@ -96,6 +95,7 @@ hipError_t launch_reset(const Dev &d, const int32_t *order_dev, hipStream_t st);
 hipError_t launch_attention(const Dev &d, const uint16_t *q, const int32_t *active_len,
                             int l0, int nL, int Hq, uint16_t *out, float *part,
                             int nsplit, hipStream_t st);
+int attn_blocks_per_cu(int D);
 hipError_t launch_combine(const float *part, uint16_t *out, int rows, int nsplit,
                           int D, hipStream_t st);
 

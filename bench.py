@@ -108,6 +108,92 @@ def cpu_baseline(wl, layer_stride: int, time_budget_s: float = 25.0):
     }
 
 
+def run_history(args):
+    """The 50-turn agent history (configuration 4): appends are the model's
+    work and are not timed; every drop / drop+reposition / reposition op is
+    timed with the library's kernel events (plan + move + commit), and its
+    algorithmic bytes are counted from the device state read back around it.
+    Ends with one decode step over the final state."""
+    import torch
+
+    from agent_kv_cache_amd import harness as Hn
+    from agent_kv_cache_amd import workloads as W
+
+    sh = W.SHAPES["c4"]
+    hist = W.c4_history()
+    row = sh.n_layers * sh.n_kv_heads * sh.head_dim * 2
+    cache = Hn.make_cache(sh, [1], 4096, max_blocks_per_seq=4096)
+    cache.reset()
+    dev = cache.device
+    tot_bytes = tot_ms = 0.0
+    n_ops = 0
+    per_op = []
+    for op in hist.ops:
+        if op[0] == "append":
+            mid, n = op[1], op[2]
+            k = W.randn_bf16((sh.n_layers, n, sh.n_kv_heads, sh.head_dim), 104_000 + 2 * mid, "cuda")
+            v = W.randn_bf16((sh.n_layers, n, sh.n_kv_heads, sh.head_dim), 104_001 + 2 * mid, "cuda")
+            tid = torch.arange(hist.msg_start[mid], hist.msg_start[mid] + n, dtype=torch.int32,
+                               device=dev)
+            cache.append(torch.tensor([n], dtype=torch.int32, device=dev), n, k, v, tid)
+            continue
+        tok0, pos0, _ = cache.seq_state(0)
+        mask = (W.mask_for_messages(tok0, hist, op[1]) if op[0] != "repos"
+                else np.zeros(len(tok0), np.uint8))
+        mt = Hn.mask_tensor(cache, [mask])
+        torch.cuda.synchronize()
+        cache.profile_read("plan", reset=True)
+        cache.profile_enable(True)
+        if op[0] == "drop":
+            cache.drop(mt)
+        elif op[0] == "repos":
+            cache.reposition()
+        else:
+            cache.drop_reposition(mt)
+        cache.profile_enable(False)
+        if cache.sync_status() != 0:
+            raise RuntimeError(f"device status after {op}")
+        ms = sum(cache.profile_read(k)[0] for k in ("plan", "move", "commit"))
+        keep = mask == 0
+        r = int(keep.sum())
+        f = int(np.flatnonzero(mask)[0]) if mask.any() else len(mask)
+        moved = int(keep[f:].sum())
+        new_pos = np.arange(r) if op[0] != "drop" else pos0[keep]
+        inplace = int((new_pos[:int(keep[:f].sum())] != pos0[:f][keep[:f]]).sum())
+        b = moved * 4 * row + 12 * moved + inplace * 2 * row + len(mask) + 4 * r
+        tot_bytes += b
+        tot_ms += ms
+        n_ops += 1
+        per_op.append((op[0], len(mask), r, moved, inplace, round(ms, 4)))
+    tok, _, _ = cache.seq_state(0)
+    q = W.randn_bf16((1, sh.n_layers, sh.n_q_heads, sh.head_dim), 204, device="cuda")
+    out = torch.empty_like(q)
+    ws = torch.empty(max(256, cache.decode_workspace_bytes(sh.n_layers, sh.n_q_heads)),
+                     dtype=torch.uint8, device="cuda")
+    for _ in range(args.warmup):
+        cache.decode_attention(q, out, ws)
+    torch.cuda.synchronize()
+    cache.profile_read("attn", reset=True)
+    cache.profile_enable(True)
+    for _ in range(args.steps):
+        cache.decode_attention(q, out, ws)
+    cache.profile_enable(False)
+    att_ms = (cache.profile_read("attn")[0] + cache.profile_read("combine")[0]) / args.steps
+    b_att = len(tok) * 2 * row + 2 * sh.n_layers * sh.n_q_heads * sh.head_dim * 2
+    return {
+        "metric": METRIC, "workload": "c4: 50-turn history, 131072 tokens appended, "
+        "L=36 Hkv=8 d=64, 47 drops / 16 repositions, decode 64 q heads",
+        "ops": n_ops, "ops_ms_total": round(tot_ms, 4), "ops_bytes_total": int(tot_bytes),
+        "drop_reposition_gbps": round(tot_bytes / (tot_ms * 1e-3) / 1e9, 1),
+        "drop_reposition_frac_of_peak": round(tot_bytes / (tot_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "decode_ms": round(att_ms, 4), "decode_bytes": b_att,
+        "decode_gbps": round(b_att / (att_ms * 1e-3) / 1e9, 1),
+        "decode_frac_of_peak": round(b_att / (att_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "final_active": len(tok),
+        "per_op": per_op[-6:],
+    }
+
+
 def calibrate(nbytes: int, reps: int):
     """Achieved GB/s of torch's device copy (read+write), fill (write) and a
     max-reduction (read) over `nbytes`: the plain streaming kernels that bound
@@ -140,7 +226,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c5"])
+    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layer-stride", type=int, default=8)
     ap.add_argument("--calibrate", type=int, default=0, metavar="BYTES",
@@ -165,6 +251,9 @@ def main():
         print(json.dumps(calibrate(args.calibrate, args.steps)), flush=True)
         return
     lib()
+    if args.workload == "c4":
+        print(json.dumps(run_history(args)), flush=True)
+        return
     wl = W.WORKLOADS[args.workload]()
     sh = wl.shape
     extra = sum(Hn.moved_pages(n, m) for n, m in zip(wl.seq_lens, wl.masks)) + 8
