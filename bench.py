@@ -311,14 +311,19 @@ def main():
     attn_gbps = (ab["b_att"]) / (avg("attn") * 1e-3) / 1e9
     dom = "move" if avg("move") >= avg("attn") else "attn"
     dom_gbps = move_gbps if dom == "move" else attn_gbps
+    # HBM bytes per launch from the committed rocprofv3 counter record of this
+    # kernel and workload (FETCH_SIZE and WRITE_SIZE scaled by what they read
+    # for a plain copy of known size), used only while the kernel source is
+    # unchanged since the counters were taken.
     traffic = None
     prof_json = os.path.join(ROOT, "profiles", f"{dom}_kernel_{wl.name}_counters.json")
     if os.path.exists(prof_json):
-        try:
-            pj = json.load(open(prof_json))
+        import hashlib
+        pj = json.load(open(prof_json))
+        src = os.path.join(ROOT, pj.get("source_file", ""))
+        if os.path.exists(src) and hashlib.sha256(open(src, "rb").read()).hexdigest() == \
+                pj.get("source_sha256"):
             traffic = pj.get("hbm_bytes_per_launch")
-        except Exception:
-            traffic = None
 
     res = {
         "metric": METRIC,
