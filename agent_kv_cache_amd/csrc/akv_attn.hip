@@ -4,8 +4,8 @@
 // sequence (the active cache of [CE] sec. 3.1/3.3: dropped entries are no
 // longer present after compaction, so only surviving KV is read).
 //
-// Grid (split, kv head, sequence*layer); 4 waves per workgroup, wave w takes
-// pages w, w+4, ... of the split.  Per 16-token page a wave
+// Grid (split, kv head, sequence*layer); 8 waves per workgroup, wave w takes
+// pages w, w+8, ... of the split.  Per 16-token page a wave
 //   - loads K straight into MFMA A-operand registers (lane = token row,
 //     16-B loads) and computes S^T[16 tok x 16 q-head] with
 //     v_mfma_f32_16x16x32_bf16 (the GQA group is padded to 16 columns),
@@ -28,10 +28,10 @@ typedef short short4v __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 #ifndef AKV_ATTN_WAVES
-#define AKV_ATTN_WAVES 4       // waves per workgroup (pages interleaved across them)
+#define AKV_ATTN_WAVES 8       // waves per workgroup (pages interleaved across them)
 #endif
 #ifndef AKV_ATTN_MIN_WAVES
-#define AKV_ATTN_MIN_WAVES 3   // waves per SIMD the register budget must allow
+#define AKV_ATTN_MIN_WAVES 2   // waves per SIMD the register budget must allow
 #endif
 constexpr int kAttnWaves = AKV_ATTN_WAVES;
 
@@ -100,8 +100,8 @@ __global__ __launch_bounds__(kAttnWaves * 64, AKV_ATTN_MIN_WAVES) void attn_kern
   const size_t page_stride = (size_t)d.H * hstride;
 
   // Page p's K and V are in registers at the top of an iteration.  Its V goes
-  // to LDS first, which frees the V registers for page p + 4's loads; those
-  // and page p + 4's K loads stay in flight while page p is consumed.
+  // to LDS first, which frees the V registers for the next page's loads;
+  // those and the next page's K loads stay in flight while page p is consumed.
   bf16x8 ka[KC];
   uint4 vv[VC];
   int p = p0 + wave;
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(kAttnWaves * 64, AKV_ATTN_MIN_WAVES) void attn_kern
     p = pn;
   }
 
-  // ---- merge the four waves ----
+  // ---- merge the waves ----
   __syncthreads();  // all V tiles consumed before s_raw is reused
   lsum += __shfl_xor(lsum, 16, 64);
   lsum += __shfl_xor(lsum, 32, 64);

@@ -122,69 +122,115 @@ __device__ __forceinline__ float f64_to_f32_for_bf16(double x) {
 // ---------------------------------------------------------------------------
 // plan
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(
+// A sequence's pages are cut into chunks of kChunkPages pages, one 256-thread
+// workgroup per (chunk, sequence) and one page per thread, so a long sequence
+// is planned by many CUs.  plan_count: keep counts and the first dropped slot
+// of every chunk.  plan_write: the chunk's first survivor rank (sum of the
+// earlier chunks' counts), an in-chunk prefix sum, the gather map src[j]
+// (physical slot) and the rotation delta q_j - p, staged in LDS and written
+// coalesced; the last workgroup finalizes every sequence and the op.
+constexpr int kChunkPages = kPlanChunkPages;
+
+__device__ __forceinline__ unsigned page_drop_bits(const uint4 m) {
+  const uint32_t w[4] = {m.x, m.y, m.z, m.w};
+  unsigned bits = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) bits |= (((w[q] >> (8 * e)) & 0xFFu) != 0u) << (4 * q + e);
+  return bits;
+}
+
+__device__ __forceinline__ unsigned page_valid_bits(int len, int pg) {
+  const int nvalid = min(kPage, len - pg * kPage);
+  return nvalid >= kPage ? 0xFFFFu : (nvalid <= 0 ? 0u : ((1u << nvalid) - 1u));
+}
+
+__global__ __launch_bounds__(kChunkPages) void plan_count_kernel(Dev d, const uint8_t *__restrict__ mask,
+                                                                 int mode) {
+  __shared__ int s_wave[kChunkPages / 64 + 1];
+  __shared__ int s_fdrop;
+  const int c = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+  const int len = d.lens[b];
+  const int pg = c * kChunkPages + t;
+  if (t == 0) s_fdrop = INT_MAX;
+  __syncthreads();
+  unsigned keep = page_valid_bits(len, pg);
+  if (keep && (mode & M_DROP)) {
+    const unsigned dropbits =
+        page_drop_bits(*reinterpret_cast<const uint4 *>(mask + (size_t)b * d.S + (size_t)pg * kPage)) & keep;
+    keep &= ~dropbits;
+    if (dropbits) atomicMin(&s_fdrop, pg * kPage + __ffs(dropbits) - 1);
+  }
+  int total;
+  block_exclusive_scan<kChunkPages>(__popc(keep), s_wave, &total);
+  if (t == 0) {
+    int *ci = d.chunk_info + ((size_t)b * d.nchunk + c) * 2;
+    ci[0] = total;
+    ci[1] = s_fdrop;
+    if (c == 0) {
+      int *si = d.seq_info + (size_t)b * kSeqInfo;
+      si[SI_FPOS] = INT_MAX;
+      si[SI_ERR] = 0;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kChunkPages) void plan_write_kernel(
     Dev d, const uint8_t *__restrict__ mask, const int32_t *__restrict__ new_pos,
     const int32_t *__restrict__ old_pos, int mode) {
-  __shared__ int s_wave[kPlanThreads / 64 + 1];
-  __shared__ int s_fdrop, s_fpos, s_err, s_last, s_gerr;
-  // One round's gather map and deltas are staged here, then written out
-  // with consecutive lanes on consecutive entries (a lane's own survivors
-  // would otherwise hit 16 different cache lines per store instruction).
-  __shared__ int s_src[kPlanThreads * kPage], s_dlt[kPlanThreads * kPage];
-  const int b = blockIdx.x, t = threadIdx.x;
+  __shared__ int s_wave[kChunkPages / 64 + 1];
+  __shared__ int s_base, s_last, s_gerr;
+  __shared__ int s_src[kChunkPages * kPage], s_dlt[kChunkPages * kPage];
+  const int c = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
   const size_t S = (size_t)d.S;
   const int len = d.lens[b];
   const int P = (len + kPage - 1) / kPage;
-  if (t == 0) {
-    s_fdrop = len;
-    s_fpos = INT_MAX;
-    s_err = 0;
-  }
-  __syncthreads();
-  const int32_t *trow = d.table + (size_t)b * d.maxpg;
-  int running = 0, err = 0, fpos = INT_MAX;
-  for (int base = 0; base < P; base += kPlanThreads) {
-    const int pg = base + t;
-    unsigned keep = 0;
-    if (pg < P) {
-      const int nvalid = min(kPage, len - pg * kPage);
-      const unsigned valid = (nvalid == kPage) ? 0xFFFFu : ((1u << nvalid) - 1u);
-      keep = valid;
-      if (mode & M_DROP) {
-        const uint4 m = *reinterpret_cast<const uint4 *>(mask + b * S + (size_t)pg * kPage);
-        const uint32_t w[4] = {m.x, m.y, m.z, m.w};
-        unsigned dropbits = 0;
+  const int pg = c * kChunkPages + t;
+  if (c * kChunkPages < P) {
+    // all loads of this thread's page first
+    const int32_t *trow = d.table + (size_t)b * d.maxpg;
+    unsigned keep = page_valid_bits(len, pg);
+    uint4 m = make_uint4(0, 0, 0, 0);
+    int tb = 0;
+    int4 pp[4], oo[4];
+    if (keep) {
+      if (mode & M_DROP) m = *reinterpret_cast<const uint4 *>(mask + b * S + (size_t)pg * kPage);
+      tb = trow[pg];
+      if (mode & M_REPOS) {
+        const int4 *ps = reinterpret_cast<const int4 *>(d.pos + (size_t)tb * kPage);
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int k = 0; k < 4; ++k) pp[k] = ps[k];
+        if (mode & M_OLDPOS) {
+          const int4 *os = reinterpret_cast<const int4 *>(old_pos + b * S + (size_t)pg * kPage);
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            dropbits |= (((w[q] >> (8 * e)) & 0xFFu) != 0u) << (4 * q + e);
-        dropbits &= valid;
-        keep = valid & ~dropbits;
-        if (dropbits) atomicMin(&s_fdrop, pg * kPage + __ffs(dropbits) - 1);
+          for (int k = 0; k < 4; ++k) oo[k] = os[k];
+        }
       }
     }
+    // survivor rank of the chunk's first page: earlier chunks' counts
+    if (t < 64) {
+      int acc = 0;
+      for (int cc = t; cc < c; cc += 64) acc += d.chunk_info[((size_t)b * d.nchunk + cc) * 2];
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+      if (t == 0) s_base = acc;
+    }
+    if (keep && (mode & M_DROP)) keep &= ~page_drop_bits(m);
     int total;
-    const int excl = block_exclusive_scan<kPlanThreads>(__popc(keep), s_wave, &total);
+    const int excl = block_exclusive_scan<kChunkPages>(__popc(keep), s_wave, &total);
+    const int base = s_base;
+    int err = 0, fpos = INT_MAX;
     if (keep) {
-      // All loads of this page first (positions, old and new positions),
-      // then the stores: keeps the loads in flight together.
-      const int j0 = running + excl;
+      const int j0 = base + excl;
       int p[kPage], o[kPage], qn[kPage];
       int qprev = -1;
       if (mode & M_REPOS) {
-        const int4 *pp = reinterpret_cast<const int4 *>(d.pos + (size_t)trow[pg] * kPage);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const int4 x = pp[k];
-          p[4 * k] = x.x; p[4 * k + 1] = x.y; p[4 * k + 2] = x.z; p[4 * k + 3] = x.w;
-        }
-        if (mode & M_OLDPOS) {
-          const int4 *op = reinterpret_cast<const int4 *>(old_pos + b * S + (size_t)pg * kPage);
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const int4 x = op[k];
-            o[4 * k] = x.x; o[4 * k + 1] = x.y; o[4 * k + 2] = x.z; o[4 * k + 3] = x.w;
+          p[4 * k] = pp[k].x; p[4 * k + 1] = pp[k].y; p[4 * k + 2] = pp[k].z; p[4 * k + 3] = pp[k].w;
+          if (mode & M_OLDPOS) {
+            o[4 * k] = oo[k].x; o[4 * k + 1] = oo[k].y; o[4 * k + 2] = oo[k].z; o[4 * k + 3] = oo[k].w;
           }
         }
         if (mode & M_NEWPOS) {
@@ -199,7 +245,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
 #pragma unroll
       for (int r = 0; r < kPage; ++r) {
         if (!((keep >> r) & 1u)) continue;
-        if (mode & M_DROP) s_src[j - running] = trow[pg] * kPage + r;   // physical slot
+        if (mode & M_DROP) s_src[j - base] = tb * kPage + r;   // physical slot
         if (mode & M_REPOS) {
           if ((mode & M_OLDPOS) && o[r] != p[r]) err = max(err, (int)AKV_ERR_POS_MISMATCH);
           int q = j;
@@ -209,59 +255,27 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
             qprev = q;
           }
           const int delta = q - p[r];
-          s_dlt[j - running] = delta;
+          s_dlt[j - base] = delta;
           if (delta != 0 && j < fpos) fpos = j;
         }
         ++j;
       }
     }
     __syncthreads();
-    for (int i = t; i < total; i += kPlanThreads) {
-      if (mode & M_DROP) d.src_map[b * S + running + i] = s_src[i];
-      if (mode & M_REPOS) d.delta_map[b * S + running + i] = s_dlt[i];
+    for (int i = t; i < total; i += kChunkPages) {
+      if (mode & M_DROP) d.src_map[b * S + base + i] = s_src[i];
+      if (mode & M_REPOS) d.delta_map[b * S + base + i] = s_dlt[i];
     }
-    __syncthreads();
-    running += total;
-  }
-  if (err) atomicMax(&s_err, err);
-  if (fpos != INT_MAX) atomicMin(&s_fpos, fpos);
-  __syncthreads();
-  if (t == 0) {
     int *si = d.seq_info + (size_t)b * kSeqInfo;
-    const int rnew = running;
-    const int Pn = (rnew + kPage - 1) / kPage;
-    int fbd = P, nmove = 0, nfreed = 0;
-    if ((mode & M_DROP) && s_fdrop < len) {
-      fbd = s_fdrop / kPage;
-      nmove = max(0, Pn - fbd);
-      nfreed = P - fbd;
-    }
-    int fip = P, ninp = 0;
-    int nnext = d.next_pos[b];
-    if (mode & M_REPOS) {
-      if (s_fpos < rnew) {
-        fip = s_fpos / kPage;
-        ninp = max(0, min(fbd, Pn) - fip);
-      }
-      nnext = rnew == 0 ? 0 : ((mode & M_NEWPOS) ? new_pos[b * S + rnew - 1] + 1 : rnew);
-    }
-    si[SI_NEW_LEN] = rnew;
-    si[SI_FBD] = fbd;
-    si[SI_FIP] = fip;
-    si[SI_N_MOVE] = nmove;
-    si[SI_N_INPLACE] = ninp;
-    si[SI_N_FREED] = nfreed;
-    si[SI_NEW_NEXT] = nnext;
-    si[SI_ERR] = s_err;
-    si[SI_OLD_LEN] = len;
+    if (err) atomicMax(&si[SI_ERR], err);
+    if (fpos != INT_MAX) atomicMin(&si[SI_FPOS], fpos);
   }
-  // ---- last workgroup: prefix sums over sequences, pool check, latch ----
-  // (device-wide fences and the ticket are only needed with several
-  // workgroups; a single sequence's workgroup is the last one by itself)
-  if (gridDim.x > 1) {
+  // ---- last workgroup: finalize every sequence, prefix sums, pool check ----
+  if (gridDim.x * gridDim.y > 1) {
     __threadfence();
     __syncthreads();
-    if (t == 0) s_last = (atomicAdd(&d.ctl[CTL_DONE], 1) == (int)gridDim.x - 1);
+    if (t == 0)
+      s_last = (atomicAdd(&d.ctl[CTL_DONE], 1) == (int)(gridDim.x * gridDim.y) - 1);
     __syncthreads();
     if (!s_last) return;
     __threadfence();
@@ -271,26 +285,57 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
   if (t == 0) s_gerr = 0;
   __syncthreads();
   int run_m = 0, run_i = 0, run_f = 0;
-  for (int base = 0; base < d.B; base += kPlanThreads) {
-    const int bb = base + t;
-    int nm = 0, ni = 0, nf = 0, e = 0;
+  for (int b0 = 0; b0 < d.B; b0 += kChunkPages) {
+    const int bb = b0 + t;
+    int nm = 0, ni = 0, nf = 0;
     int *si = d.seq_info + (size_t)bb * kSeqInfo;
     if (bb < d.B) {
-      nm = __atomic_load_n(&si[SI_N_MOVE], __ATOMIC_RELAXED);
-      ni = __atomic_load_n(&si[SI_N_INPLACE], __ATOMIC_RELAXED);
-      nf = __atomic_load_n(&si[SI_N_FREED], __ATOMIC_RELAXED);
-      e = __atomic_load_n(&si[SI_ERR], __ATOMIC_RELAXED);
+      const int L0 = d.lens[bb];
+      const int P0 = (L0 + kPage - 1) / kPage;
+      const int nch = (P0 + kChunkPages - 1) / kChunkPages;
+      int rnew = 0, fdrop = INT_MAX;
+      for (int cc = 0; cc < nch; ++cc) {
+        const int *ci = d.chunk_info + ((size_t)bb * d.nchunk + cc) * 2;
+        rnew += __atomic_load_n(&ci[0], __ATOMIC_RELAXED);
+        fdrop = min(fdrop, __atomic_load_n(&ci[1], __ATOMIC_RELAXED));
+      }
+      const int fpos = nch ? __atomic_load_n(&si[SI_FPOS], __ATOMIC_RELAXED) : INT_MAX;
+      const int e = nch ? __atomic_load_n(&si[SI_ERR], __ATOMIC_RELAXED) : 0;
+      const int Pn = (rnew + kPage - 1) / kPage;
+      int fbd = P0;
+      if ((mode & M_DROP) && fdrop < L0) {
+        fbd = fdrop / kPage;
+        nm = max(0, Pn - fbd);
+        nf = P0 - fbd;
+      }
+      int fip = P0;
+      int nnext = d.next_pos[bb];
+      if (mode & M_REPOS) {
+        if (fpos < rnew) {
+          fip = fpos / kPage;
+          ni = max(0, min(fbd, Pn) - fip);
+        }
+        nnext = rnew == 0 ? 0 : ((mode & M_NEWPOS) ? new_pos[(size_t)bb * S + rnew - 1] + 1 : rnew);
+      }
+      si[SI_NEW_LEN] = rnew;
+      si[SI_FBD] = fbd;
+      si[SI_FIP] = fip;
+      si[SI_N_MOVE] = nm;
+      si[SI_N_INPLACE] = ni;
+      si[SI_N_FREED] = nf;
+      si[SI_NEW_NEXT] = nnext;
+      si[SI_OLD_LEN] = L0;
+      if (e) atomicMax(&s_gerr, e);
     }
     int tm, ti, tf;
-    const int em = block_exclusive_scan<kPlanThreads>(nm, s_wave, &tm);
-    const int ei = block_exclusive_scan<kPlanThreads>(ni, s_wave, &ti);
-    const int ef = block_exclusive_scan<kPlanThreads>(nf, s_wave, &tf);
+    const int em = block_exclusive_scan<kChunkPages>(nm, s_wave, &tm);
+    const int ei = block_exclusive_scan<kChunkPages>(ni, s_wave, &ti);
+    const int ef = block_exclusive_scan<kChunkPages>(nf, s_wave, &tf);
     if (bb < d.B) {
       si[SI_MOVE_OFF] = run_m + em;
       si[SI_INPLACE_OFF] = run_i + ei;
       si[SI_FREED_OFF] = run_f + ef;
     }
-    if (e) atomicMax(&s_gerr, e);
     run_m += tm;
     run_i += ti;
     run_f += tf;
@@ -653,8 +698,12 @@ __global__ void reset_kernel(Dev d, const int32_t *order) {
 // ---------------------------------------------------------------------------
 hipError_t launch_plan(const Dev &d, const uint8_t *mask, const int32_t *new_pos,
                        const int32_t *old_pos, int mode, hipStream_t st) {
-  hipLaunchKernelGGL(plan_kernel, dim3(d.B), dim3(kPlanThreads), 0, st, d, mask, new_pos,
-                     old_pos, mode);
+  const dim3 grid(d.nchunk, d.B);
+  hipLaunchKernelGGL(plan_count_kernel, grid, dim3(kChunkPages), 0, st, d, mask, mode);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(plan_write_kernel, grid, dim3(kChunkPages), 0, st, d, mask, new_pos, old_pos,
+                     mode);
   return hipGetLastError();
 }
 

@@ -59,12 +59,12 @@ struct Timed {
     if (c->profile) {
       a = take_event(c);
       b = take_event(c);
-      if (a && b) hipEventRecord(a, st);
+      if (a && b) (void)hipEventRecord(a, st);
     }
   }
   ~Timed() {
     if (a && b) {
-      hipEventRecord(b, st);
+      (void)hipEventRecord(b, st);
       c->pending.push_back({kernel, a, b});
     }
   }
@@ -164,6 +164,7 @@ akv_status akv_cache_init(const akv_cache_desc *d, akv_cache **out) {
   v.src_map = reinterpret_cast<int32_t *>(sb + c->layout.src_map);
   v.delta_map = reinterpret_cast<int32_t *>(sb + c->layout.delta_map);
   v.stage = reinterpret_cast<int32_t *>(sb + c->layout.stage);
+  v.chunk_info = reinterpret_cast<int32_t *>(sb + c->layout.chunk_info);
   v.L = d->n_layers;
   v.H = d->n_kv_heads;
   v.D = d->head_dim;
@@ -171,6 +172,7 @@ akv_status akv_cache_init(const akv_cache_desc *d, akv_cache **out) {
   v.B = d->n_seqs;
   v.maxpg = d->max_blocks_per_seq;
   v.S = S;
+  v.nchunk = akv::plan_chunks(d->max_blocks_per_seq);
 
   if (hipGetDevice(&c->device) != hipSuccess ||
       hipDeviceGetAttribute(&c->n_cu, hipDeviceAttributeMultiprocessorCount, c->device) !=
@@ -196,10 +198,10 @@ akv_status akv_cache_init(const akv_cache_desc *d, akv_cache **out) {
 void akv_cache_free(akv_cache *c) {
   if (!c) return;
   for (auto &r : c->pending) {
-    hipEventDestroy(r.a);
-    hipEventDestroy(r.b);
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
   }
-  for (auto e : c->spare) hipEventDestroy(e);
+  for (auto e : c->spare) (void)hipEventDestroy(e);
   delete c;
 }
 

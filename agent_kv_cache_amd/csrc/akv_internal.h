@@ -41,6 +41,7 @@ enum SeqInfo : int {
   SI_OLD_LEN = 11,
   SI_OLD_NEXT = 12,
   SI_APP_OFF = 13,   // append: offset of this sequence's tokens in the input
+  SI_FPOS = 14,      // first survivor rank whose position changes (atomic min)
   kSeqInfo = 16
 };
 
@@ -56,17 +57,21 @@ enum Mode : int {
 struct Dev {
   uint16_t *k, *v;
   int32_t *table, *lens, *next_pos, *pos, *tok, *free_stack, *free_count;
-  int32_t *ctl, *seq_info, *src_map, *delta_map, *stage;
+  int32_t *ctl, *seq_info, *src_map, *delta_map, *stage, *chunk_info;
   const double *theta;        // [d/2]
-  int L, H, D, NB, B, maxpg, S;
+  int L, H, D, NB, B, maxpg, S, nchunk;   // nchunk: plan chunks per sequence
 };
 
 // Scratch layout (byte offsets from the scratch base, each 256-B aligned).
 struct ScratchLayout {
-  size_t ctl, theta, seq_info, src_map, delta_map, stage, total;
+  size_t ctl, theta, seq_info, src_map, delta_map, stage, chunk_info, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+constexpr int kPlanChunkPages = 256;   // pages per plan workgroup
+
+inline int plan_chunks(int maxpg) { return (maxpg + kPlanChunkPages - 1) / kPlanChunkPages; }
 
 inline ScratchLayout scratch_layout(int B, int S, int NB) {
   ScratchLayout s;
@@ -77,6 +82,7 @@ inline ScratchLayout scratch_layout(int B, int S, int NB) {
   s.src_map = o;   o = align256(o + size_t(B) * S * 4);
   s.delta_map = o; o = align256(o + size_t(B) * S * 4);
   s.stage = o;     o = align256(o + size_t(NB) * 4);
+  s.chunk_info = o; o = align256(o + size_t(B) * plan_chunks(S / kPage) * 2 * 4);
   s.total = o;
   return s;
 }
