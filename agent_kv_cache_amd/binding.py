@@ -115,7 +115,9 @@ class AkvCache:
 
     def __init__(self, n_layers: int, n_kv_heads: int, head_dim: int, n_blocks: int,
                  n_seqs: int, max_blocks_per_seq: int, rope_base: float,
-                 device: str = "cuda"):
+                 device: str = "cuda", k_pool=None, v_pool=None):
+        """k_pool / v_pool: optional caller-placed bf16 tensors of shape
+        [L][NB][Hkv][16][d] (e.g. views of one larger buffer)."""
         import torch
         self.L, self.H, self.D = n_layers, n_kv_heads, head_dim
         self.NB, self.B, self.maxpg = n_blocks, n_seqs, max_blocks_per_seq
@@ -123,8 +125,14 @@ class AkvCache:
         self.rope_base = float(rope_base)
         self.device = torch.device(device)
         shape = (n_layers, n_blocks, n_kv_heads, PAGE, head_dim)
-        self.k_pool = torch.empty(shape, dtype=torch.bfloat16, device=self.device)
-        self.v_pool = torch.empty(shape, dtype=torch.bfloat16, device=self.device)
+        for t in (k_pool, v_pool):
+            if t is not None and (tuple(t.shape) != shape or t.dtype != torch.bfloat16
+                                  or not t.is_contiguous()):
+                raise ValueError(f"pool tensors must be contiguous bf16 {shape}")
+        self.k_pool = k_pool if k_pool is not None else torch.empty(
+            shape, dtype=torch.bfloat16, device=self.device)
+        self.v_pool = v_pool if v_pool is not None else torch.empty(
+            shape, dtype=torch.bfloat16, device=self.device)
         self.positions = torch.empty((n_blocks, PAGE), dtype=torch.int32, device=self.device)
         self.token_ids = torch.empty((n_blocks, PAGE), dtype=torch.int32, device=self.device)
         nt = n_seqs * max_blocks_per_seq

@@ -36,6 +36,12 @@ namespace akv {
 #ifndef AKV_MOVE_NT
 #define AKV_MOVE_NT 1          // nontemporal hint on the streamed KV accesses
 #endif
+#ifndef AKV_MOVE_SPLIT_KV
+#define AKV_MOVE_SPLIT_KV 1    // stream a unit's K slices, then its V slices
+#endif
+#ifndef AKV_MOVE_ROTATE
+#define AKV_MOVE_ROTATE 0      // start each page's layer walk at a page-dependent layer
+#endif
 
 constexpr int kPlanThreads = 1024;
 constexpr int kMoveThreads = 256;
@@ -502,9 +508,47 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
     const bool do_v = mv;
     if (!do_k) continue;
     const int nsl = (l1 - l0) * d.H;
+#if AKV_MOVE_ROTATE
+    // the k-th unit of page pg is layer (k + rot) mod L: concurrently
+    // running workgroups then stream different layers' regions
+    const int rot = (int)((pgl * 7) % d.L);
+#endif
     const int sp = s_src[r];
     const size_t src_row = (size_t)(sp >> 4) * d.H * hstride + (size_t)(sp & 15) * D + 8 * pc;
     const size_t dst_row = (size_t)dst * d.H * hstride + (size_t)r * D + 8 * pc;
+#if AKV_MOVE_SPLIT_KV
+    // K slices of the unit range first, then V slices: each pass streams one
+    // pool (two concurrent streams per workgroup instead of four)
+    for (int plane = 0; plane < (do_v ? 2 : 1); ++plane) {
+      uint16_t *pool = plane ? d.v : d.k;
+      const bool rot_plane = plane == 0 && valid && delta != 0;
+      for (int i0 = slot; i0 < nsl; i0 += NS * U) {
+        u32x4 lo[U], hi[U];
+        size_t dofs[U];
+        bool on[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int idx = i0 + u * NS;
+          on[u] = idx < nsl;
+          const int l = l0 + idx / d.H, h = idx % d.H;
+          const size_t off = (size_t)l * lstride + (size_t)h * hstride;
+          dofs[u] = dst_row + off;
+          lo[u] = hi[u] = u32x4{0u, 0u, 0u, 0u};
+          if (on[u] && valid) {
+            lo[u] = ld_stream(pool + src_row + off);
+            hi[u] = ld_stream(pool + src_row + off + HALF);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (!on[u]) continue;
+          if (rot_plane) rotate8(lo[u], hi[u], cs_row);
+          st_stream(pool + dofs[u], lo[u]);
+          st_stream(pool + dofs[u] + HALF, hi[u]);
+        }
+      }
+    }
+#else
     for (int i0 = slot; i0 < nsl; i0 += NS * U) {
       u32x4 klo[U], khi[U], vlo[U], vhi[U];
       size_t dofs[U];
@@ -513,7 +557,13 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
       for (int u = 0; u < U; ++u) {
         const int idx = i0 + u * NS;
         on[u] = idx < nsl;
-        const int l = l0 + idx / d.H, h = idx % d.H;
+#if AKV_MOVE_ROTATE
+        int l = l0 + idx / d.H + rot;
+        if (l >= d.L) l -= d.L;
+#else
+        const int l = l0 + idx / d.H;
+#endif
+        const int h = idx % d.H;
         const size_t off = (size_t)l * lstride + (size_t)h * hstride;
         dofs[u] = dst_row + off;
         klo[u] = khi[u] = vlo[u] = vhi[u] = u32x4{0u, 0u, 0u, 0u};
@@ -539,6 +589,7 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
         }
       }
     }
+#endif
   }
 }
 
