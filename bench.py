@@ -228,6 +228,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured once in a HIP graph and replayed "
+                         "(reported as graph_ms_per_step; per-kernel times stay eager)")
     ap.add_argument("--cpu-layer-stride", type=int, default=8)
     ap.add_argument("--calibrate", type=int, default=0, metavar="BYTES",
                     help="instead of the workload, time plain device copy / fill / read "
@@ -371,6 +374,28 @@ def main():
             },
         },
     }
+    if args.graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step()
+        torch.cuda.current_stream().wait_stream(s)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        tg0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        tg1 = time.perf_counter()
+        if cache.sync_status() != 0:
+            raise RuntimeError("device status after graph replays")
+        gms = (tg1 - tg0) * 1e3 / args.steps
+        res["graph_ms_per_step"] = round(gms, 4)
+        res["graph_value"] = round((ab["b_dr"] + ab["b_att"]) / (gms * 1e-3) / 1e9, 2)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_layer_stride)
     print(json.dumps(res), flush=True)

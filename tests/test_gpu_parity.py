@@ -302,3 +302,109 @@ def test_c2_full_size_sampled():
     out = _decode(cache, q)
     err = check_attention(cache, oc, q, out, layers=layers)
     say("c2 attention max abs err (sampled layers)", err)
+
+
+def test_degenerate_masks_and_positions():
+    """Drop everything, drop nothing, reposition non-canonical positions in
+    place, refill an emptied sequence, and decode over empty sequences."""
+    sh = W.Shape(2, 2, 128, 4, 5.0e5)
+    lens = [40, 37, 0]
+    say("case degenerate masks")
+    c = _setup(sh, lens, seed=41, extra=20, maxpg=8)
+    oc = oracle_for(sh, lens, 41)
+    # seq 0: drop nothing; seq 1: drop everything; seq 2: empty
+    masks = [np.zeros(40, np.uint8), np.ones(37, np.uint8), np.zeros(0, np.uint8)]
+    c.drop(Hn.mask_tensor(c, masks))
+    for b in range(3):
+        oc.drop(b, masks[b])
+    assert c.sync_status() == 0
+    check_meta(c, oc)
+    assert int(c.seq_lens[1]) == 0 and int(c.next_pos[1]) == 37   # drop keeps next_pos
+    # positions with gaps, then a reposition with nothing dropped: in place
+    m0 = np.zeros(40, np.uint8); m0[5:9] = 1
+    c.drop(Hn.mask_tensor(c, [m0, None, None]))
+    oc.drop(0, m0)
+    c.drop_reposition(Hn.mask_tensor(c, [np.zeros(36, np.uint8), None, None]))
+    for b in range(3):
+        oc.drop_reposition(b, np.zeros(len(oc.seqs[b]), np.uint8))
+    assert c.sync_status() == 0
+    check_meta(c, oc)
+    check_kv(c, oc, k_ulp=1)
+    assert int(c.next_pos[1]) == 0                                   # empty after repos
+    # refill the emptied sequence and decode everything
+    k = W.randn_bf16((2, 5, 2, 128), 42)
+    v = W.randn_bf16((2, 5, 2, 128), 43)
+    tid = np.arange(5) + (1 << 27)
+    c.append(torch.tensor([0, 5, 0], dtype=torch.int32, device=c.device), 5, k.to(c.device),
+             v.to(c.device), torch.tensor(tid, dtype=torch.int32, device=c.device))
+    oc.append(1, tid, k.permute(1, 0, 2, 3).double().numpy(), v.permute(1, 0, 2, 3).double().numpy())
+    assert c.sync_status() == 0
+    check_meta(c, oc)
+    q = q_tensor(sh, 3, 2, 44).to(c.device)
+    out = _decode(c, q)
+    check_attention(c, oc, q, out)
+    assert not out[2].float().abs().sum().item()                     # empty sequence -> 0
+
+
+def test_active_len_out_of_range_is_latched():
+    sh = W.Shape(1, 2, 64, 4, 1.0e4)
+    lens = [50, 20]
+    say("case active_len out of range")
+    c = _setup(sh, lens, seed=51)
+    oc = oracle_for(sh, lens, 51)
+    q = q_tensor(sh, 2, 1, 52).to(c.device)
+    out = _decode(c, q, [60, 20])          # 60 > 50: clamped to 50, error latched
+    assert c.sync_status() == 1
+    check_attention(c, oc, q, out, active=[50, 20])
+    out = _decode(c, q, [-3, 20])          # negative: clamped to 0
+    assert c.sync_status() == 1
+    assert not out[0].float().abs().sum().item()
+
+
+def test_graph_capture_replays_match_eager():
+    """One step (state restore, fused drop+reposition, decode) captured in a
+    HIP graph and replayed several times with eager work and host syncs in
+    between; every replay must equal the eager step bit for bit."""
+    sh = W.Shape(4, 8, 128, 32, 5.0e5)
+    lens = [3000, 1777]
+    rng = np.random.default_rng(61)
+    masks = [(rng.uniform(size=n) < 0.3).astype(np.uint8) for n in lens]
+    say("case graph capture")
+    c = _setup(sh, lens, seed=61)
+    mask = Hn.mask_tensor(c, masks)
+    q = q_tensor(sh, 2, 4, 62).to(c.device)
+    out = torch.empty_like(q)
+    ws = torch.empty(max(256, c.decode_workspace_bytes(4, 32)), dtype=torch.uint8, device=c.device)
+    snap = c.meta.clone()
+
+    def step():
+        c.meta.copy_(snap)
+        c.drop_reposition(mask)
+        c.decode_attention(q, out, ws)
+
+    step()
+    torch.cuda.synchronize()
+    assert c.sync_status() == 0
+    ref_meta = c.meta.clone()
+    ref_out = out.clone()
+    ref_k = [c.gather_rows(b, l, "k").clone() for b in range(2) for l in range(4)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()                              # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        out.zero_()
+        junk = torch.randn(1 << 20, device=c.device).sum()      # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(c.meta, ref_meta), rep
+        assert torch.equal(out, ref_out), rep
+        got_k = [c.gather_rows(b, l, "k") for b in range(2) for l in range(4)]
+        assert all(torch.equal(x, y) for x, y in zip(got_k, ref_k)), rep
+        del junk
+    assert c.sync_status() == 0
