@@ -95,9 +95,9 @@ __global__ __launch_bounds__(kAttnWaves * 64, AKV_ATTN_MIN_WAVES) void attn_kern
   for (int t = 0; t < NT; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   const int32_t *trow = d.table + (size_t)b * d.maxpg;
-  const size_t hstride = (size_t)kPage * D;
-  const size_t head_base = ((size_t)l * d.NB * d.H + g) * hstride;
-  const size_t page_stride = (size_t)d.H * hstride;
+  const PoolStrides ps = pool_strides(d.NB, d.H, D);
+  const size_t head_base = (size_t)l * ps.layer + (size_t)g * ps.head;
+  const size_t page_stride = ps.page;
 
   // Page p's K and V are in registers at the top of an iteration.  Its V goes
   // to LDS first, which frees the V registers for the next page's loads;

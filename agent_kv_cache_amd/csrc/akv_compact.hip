@@ -425,8 +425,8 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
   const int t = threadIdx.x;
   const int r = (t % TPH) / CH, pc = t % CH, slot = t / TPH;
   const size_t S = (size_t)d.S;
-  const size_t hstride = (size_t)kPage * D;
-  const size_t lstride = (size_t)d.NB * d.H * hstride;
+  const PoolStrides ps = pool_strides(d.NB, d.H, D);
+  const size_t hstride = ps.head, lstride = ps.layer;
   const bool rot_any = (mode & M_REPOS) != 0;
 
   for (long long pgl = u0 / d.L; pgl * d.L < u1; ++pgl) {
@@ -514,8 +514,8 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
     const int rot = (int)((pgl * 7) % d.L);
 #endif
     const int sp = s_src[r];
-    const size_t src_row = (size_t)(sp >> 4) * d.H * hstride + (size_t)(sp & 15) * D + 8 * pc;
-    const size_t dst_row = (size_t)dst * d.H * hstride + (size_t)r * D + 8 * pc;
+    const size_t src_row = (size_t)(sp >> 4) * ps.page + (size_t)(sp & 15) * D + 8 * pc;
+    const size_t dst_row = (size_t)dst * ps.page + (size_t)r * D + 8 * pc;
 #if AKV_MOVE_SPLIT_KV
     // K slices of the unit range first, then V slices: each pass streams one
     // pool (two concurrent streams per workgroup instead of four)
@@ -720,7 +720,9 @@ __global__ __launch_bounds__(256) void append_copy_kernel(Dev d, int64_t n_new,
   for (int c = threadIdx.x; c < nchunk; c += blockDim.x) {
     const int e8 = c % C8, lh = c / C8, h = lh % d.H, l = lh / d.H;
     const size_t src = (((size_t)l * n_new + tk) * d.H + h) * D + 8 * e8;
-    const size_t dst = (((size_t)l * d.NB + page) * d.H + h) * (size_t)(kPage * D) + (size_t)row * D + 8 * e8;
+    const PoolStrides ps = pool_strides(d.NB, d.H, D);
+    const size_t dst = (size_t)l * ps.layer + (size_t)page * ps.page + (size_t)h * ps.head +
+                       (size_t)row * D + 8 * e8;
     *reinterpret_cast<uint4 *>(d.k + dst) = *reinterpret_cast<const uint4 *>(k_new + src);
     *reinterpret_cast<uint4 *>(d.v + dst) = *reinterpret_cast<const uint4 *>(v_new + src);
   }

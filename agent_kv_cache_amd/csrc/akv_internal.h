@@ -62,6 +62,23 @@ struct Dev {
   int L, H, D, NB, B, maxpg, S, nchunk;   // nchunk: plan chunks per sequence
 };
 
+// Element strides of the K/V pools: page, kv head, layer.  One (layer, page,
+// head) chunk is 16*D contiguous values.
+#ifndef AKV_HEAD_MAJOR
+#define AKV_HEAD_MAJOR 0
+#endif
+struct PoolStrides {
+  size_t page, head, layer;
+};
+__host__ __device__ inline PoolStrides pool_strides(int NB, int H, int D) {
+  const size_t chunk = (size_t)kPage * D;
+#if AKV_HEAD_MAJOR
+  return PoolStrides{chunk, (size_t)NB * chunk, (size_t)H * NB * chunk};   // [L][H][NB][16][D]
+#else
+  return PoolStrides{(size_t)H * chunk, chunk, (size_t)NB * H * chunk};    // [L][NB][H][16][D]
+#endif
+}
+
 // Scratch layout (byte offsets from the scratch base, each 256-B aligned).
 struct ScratchLayout {
   size_t ctl, theta, seq_info, src_map, delta_map, stage, chunk_info, total;
