@@ -35,6 +35,13 @@ What is computed (every function below is the plain definition):
   entries, GQA head h reads kv head floor(h / G).
 * replay (eq. 6):  the state is the result of applying the op list in order
   from the empty cache.
+* fork ([CE] sec. 4.2.3, Appendix A.1.1): a new position version of a
+  sequence -- its entries copied (K re-rotated when positions change, V
+  copied), then drop / reposition applied to the copy only; the source
+  version is unchanged.
+* segment attention ([CE] Appendix A.1.1): a restore forward splits its
+  queries into segments; each segment applies standard causal attention over
+  its own KV list, whose last n entries are the segment's own tokens.
 
 Readings where the pages are silent (each listed in the design doc):
   pairing/sign of RoPE (NeoX half split, +p*theta), theta_i without scaling,
@@ -63,6 +70,7 @@ __all__ = [
     "attend",
     "SeqState",
     "OracleCache",
+    "segment_attention",
     "replay",
 ]
 
@@ -289,6 +297,24 @@ class OracleCache:
         delta = self.reposition(b, new_pos)
         return src, delta
 
+    # -- position versions ([CE] sec. 4.2.3, A.1.1) ------------------------
+    def fork(self, src: int, dst: int, mask=None, reposition: bool = False, new_pos=None):
+        """dst (empty) becomes a copy of src; then drop(mask) and, if asked,
+        reposition(new_pos) are applied to dst only.  src is unchanged."""
+        s, d = self.seqs[src], self.seqs[dst]
+        if len(d) or src == dst:
+            raise ValueError("fork: destination must be empty and differ from the source")
+        d.token_ids = s.token_ids.copy()
+        d.pos = s.pos.copy()
+        d.next_pos = s.next_pos
+        if self.with_kv:
+            d.k = s.k.copy()
+            d.v = s.v.copy()
+        if mask is not None:
+            self.drop(dst, mask)
+        if reposition:
+            self.reposition(dst, new_pos)
+
     # -- decode attention over the active KV ------------------------------
     def decode_attention(self, b: int, q, active_len: Optional[int] = None) -> np.ndarray:
         """o[l, h] = attend(q[l, h], K[:n, l, h // G], V[:n, l, h // G]).
@@ -308,6 +334,32 @@ class OracleCache:
                 g = h // G
                 out[l, h] = attend(q[l, h], s.k[:n, l, g], s.v[:n, l, g])
         return out
+
+
+def segment_attention(cache: "OracleCache", segments) -> list:
+    """Causal attention of restore segments ([CE] Appendix A.1.1).
+
+    segments: list of (b, q) with q [n, L, Hq, d]: the n query rows are the
+    last n entries of sequence b (the segment's own tokens); row i attends to
+    entries [0, len_b - n + i].  Returns one [n, L, Hq, d] array per segment.
+    """
+    out = []
+    for b, q in segments:
+        q = np.asarray(q, dtype=np.float64)
+        n = q.shape[0]
+        s = cache.seqs[b]
+        if n > len(s):
+            raise ValueError("segment_attention: more queries than entries")
+        L, Hq, d = q.shape[1:]
+        G = Hq // cache.n_kv_heads
+        o = np.zeros_like(q)
+        for i in range(n):
+            vis = len(s) - n + i + 1
+            for l in range(L):
+                for h in range(Hq):
+                    o[i, l, h] = attend(q[i, l, h], s.k[:vis, l, h // G], s.v[:vis, l, h // G])
+        out.append(o)
+    return out
 
 
 # ---------------------------------------------------------------------------

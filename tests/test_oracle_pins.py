@@ -502,3 +502,148 @@ def test_planted_mistakes_are_caught(monkeypatch):
     monkeypatch.setattr(O, "attend", attend_bad_scale)
     with pytest.raises(AssertionError):
         test_attention_matches_torch_sdpa_gqa()
+
+
+# ---------------------------------------------------------------------------
+# position versions and segment-batch restore attention
+# ---------------------------------------------------------------------------
+def _fig10_versions(with_kv=True, seed=12):
+    """Build the Figure 10 request as four position versions (sequences 0..3)."""
+    rng = np.random.default_rng(seed)
+    L, H, d = 1, 2, 8
+    c = O.OracleCache(L, H, d, 1e4, n_seqs=4, with_kv=with_kv)
+    names = "ABCDEF"
+    kv = {n: (O.bf16_round(rng.standard_normal((1, L, H, d))),
+              O.bf16_round(rng.standard_normal((1, L, H, d)))) for n in names}
+
+    def app(b, n):
+        c.append(b, [names.index(n)], *(kv[n] if with_kv else (None, None)))
+
+    def mask(b, drop):
+        return np.array([names[t] in drop for t in c.seqs[b].token_ids], np.uint8)
+
+    for n in "ABC":
+        app(0, n)
+    c.fork(0, 1, mask(0, "B"), reposition=True)
+    app(1, "D")
+    c.fork(1, 2, mask(1, "D"))
+    app(2, "E")
+    c.fork(2, 3, None, reposition=True)
+    app(3, "F")
+    return c, kv, names
+
+
+def test_fig10_segment_visible_sets():
+    g = json.load(open(os.path.join(GOLDEN, "fig10_positions.json")))
+    c, _, names = _fig10_versions(with_kv=False)
+    for b, seg in enumerate(g["segments"]):
+        s = c.seqs[b]
+        got = {names[t]: int(p) for t, p in zip(s.token_ids, s.pos)}
+        assert got == seg["visible"], (b, got)
+        own = [names[t] for t in s.token_ids[len(s) - len(seg["queries"]):]]
+        assert own == seg["queries"]
+    # the source versions are untouched by later forks
+    assert [names[t] for t in c.seqs[0].token_ids] == ["A", "B", "C"]
+    assert list(c.seqs[0].pos) == [0, 1, 2]
+
+
+def test_fig10_segment_attention_uses_rotated_versions():
+    """Segment rows attend over the explicit visible sets; C1 and E2 are the
+    originals turned by (new - old) position, V copied."""
+    c, kv, names = _fig10_versions()
+    th = c.theta
+    rng = np.random.default_rng(13)
+    segs = [(b, O.bf16_round(rng.standard_normal((n, 1, 4, 8))))
+            for b, n in enumerate([3, 1, 1, 1])]
+    outs = O.segment_attention(c, segs)
+
+    def k_at(n, old, new):
+        k = kv[n][0][0]
+        return k if old == new else O.bf16_round(O.rotate_pairs(k, new - old, th))
+
+    vis = {0: [("A", 0, 0), ("B", 1, 1), ("C", 2, 2)],
+           1: [("A", 0, 0), ("C", 2, 1), ("D", 2, 2)],
+           2: [("A", 0, 0), ("C", 2, 1), ("E", 3, 3)],
+           3: [("A", 0, 0), ("C", 2, 1), ("E", 3, 2), ("F", 3, 3)]}
+    for b, (_, q) in enumerate(segs):
+        ents = vis[b]
+        n = q.shape[0]
+        for i in range(n):
+            upto = len(ents) - n + i + 1
+            kk = np.stack([k_at(nm, o, p) for nm, o, p in ents[:upto]])     # [m, 1, H, d]
+            vv = np.stack([kv[nm][1][0] for nm, _, _ in ents[:upto]])
+            for h in range(4):
+                want = O.attend(q[i, 0, h], kk[:, 0, h // 2], vv[:, 0, h // 2])
+                assert np.allclose(outs[b][i, 0, h], want, rtol=0, atol=1e-14), (b, i, h)
+
+
+def test_segment_attention_is_per_row_causal_decode():
+    """Row i of an n-row segment equals a decode over the first len-n+i+1 entries."""
+    rng = np.random.default_rng(14)
+    c = O.OracleCache(2, 2, 16, 1e4)
+    n_all = 23
+    c.append(0, np.arange(n_all), O.bf16_round(rng.standard_normal((n_all, 2, 2, 16))),
+             O.bf16_round(rng.standard_normal((n_all, 2, 2, 16))))
+    q = O.bf16_round(rng.standard_normal((7, 2, 8, 16)))
+    (out,) = O.segment_attention(c, [(0, q)])
+    for i in range(7):
+        ref = c.decode_attention(0, q[i], active_len=n_all - 7 + i + 1)
+        assert np.array_equal(out[i], ref)
+
+
+def test_fork_leaves_source_and_matches_in_place_ops():
+    c, k, v = _filled_cache(20)
+    c.seqs.append(O.SeqState(k=np.zeros((0, 1, 2, 8)), v=np.zeros((0, 1, 2, 8))))
+    before = (c.seqs[0].token_ids.copy(), c.seqs[0].pos.copy(), c.seqs[0].k.copy())
+    mask = np.zeros(20, np.uint8); mask[3:9] = 1
+    c.fork(0, 1, mask, reposition=True)
+    s0 = c.seqs[0]
+    assert np.array_equal(s0.token_ids, before[0]) and np.array_equal(s0.pos, before[1])
+    assert np.array_equal(s0.k, before[2])
+    ref, _, _ = _filled_cache(20)
+    ref.drop_reposition(0, mask)
+    assert np.array_equal(c.seqs[1].k, ref.seqs[0].k)
+    assert np.array_equal(c.seqs[1].pos, ref.seqs[0].pos)
+    assert c.seqs[1].next_pos == ref.seqs[0].next_pos
+    with pytest.raises(ValueError):
+        c.fork(0, 1)                                      # destination not empty
+
+
+def test_planted_mistakes_in_versions_are_caught(monkeypatch):
+    # a causal window one entry too short: the per-row decode pin fails
+    orig = O.segment_attention
+
+    def short_window(cache, segments):
+        out = []
+        for b, q in segments:
+            n = q.shape[0]
+            s = cache.seqs[b]
+            o = np.zeros_like(np.asarray(q, np.float64))
+            G = q.shape[2] // cache.n_kv_heads
+            for i in range(n):
+                vis = len(s) - n + i
+                for l in range(q.shape[1]):
+                    for h in range(q.shape[2]):
+                        o[i, l, h] = O.attend(q[i, l, h], s.k[:vis, l, h // G], s.v[:vis, l, h // G])
+            out.append(o)
+        return out
+
+    monkeypatch.setattr(O, "segment_attention", short_window)
+    with pytest.raises(AssertionError):
+        test_segment_attention_is_per_row_causal_decode()
+    monkeypatch.setattr(O, "segment_attention", orig)
+    # a fork that shares the source's arrays: the source changes, the pin fails
+    orig_fork = O.OracleCache.fork
+
+    def aliasing_fork(self, src, dst, mask=None, reposition=False, new_pos=None):
+        s, d = self.seqs[src], self.seqs[dst]
+        self.seqs[dst] = s
+        if mask is not None:
+            self.drop(dst, mask)
+        if reposition:
+            self.reposition(dst, new_pos)
+
+    monkeypatch.setattr(O.OracleCache, "fork", aliasing_fork)
+    with pytest.raises(AssertionError):
+        test_fork_leaves_source_and_matches_in_place_ops()
+    monkeypatch.setattr(O.OracleCache, "fork", orig_fork)
