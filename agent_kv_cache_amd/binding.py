@@ -19,7 +19,8 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 
 STATUS = {0: "AKV_OK", 1: "AKV_ERR_ARG", 2: "AKV_ERR_ORDER", 3: "AKV_ERR_POS_MISMATCH",
           4: "AKV_ERR_NO_BLOCKS", 5: "AKV_ERR_CAPACITY", 6: "AKV_ERR_HIP"}
-KERNELS = {"plan": 0, "move": 1, "commit": 2, "attn": 3, "combine": 4, "append": 5}
+KERNELS = {"plan": 0, "move": 1, "commit": 2, "attn": 3, "combine": 4, "append": 5,
+           "segment": 6}
 PAGE = 16
 
 
@@ -63,9 +64,12 @@ def lib() -> C.CDLL:
         "akv_drop": (C.c_int, [_P, _P, _P]),
         "akv_reposition": (C.c_int, [_P, _P, _P, _P]),
         "akv_drop_reposition": (C.c_int, [_P, _P, _P, _P]),
+        "akv_fork": (C.c_int, [_P, _P, _P, C.c_int, _P, _P]),
         "akv_decode_workspace_bytes": (C.c_size_t, [_P, C.c_int32, C.c_int32]),
         "akv_decode_attention": (C.c_int, [_P, _P, _P, C.c_int32, C.c_int32, C.c_int32, _P,
                                            _P, C.c_size_t, _P]),
+        "akv_segment_attention": (C.c_int, [_P, _P, _P, _P, C.c_int32, C.c_int32, C.c_int32,
+                                            C.c_int32, C.c_int32, _P, _P]),
         "akv_sync_status": (C.c_int, [_P, _P]),
         "akv_status_string": (C.c_char_p, [C.c_int]),
         "akv_profile_enable": (C.c_int, [_P, C.c_int]),
@@ -194,6 +198,17 @@ class AkvCache:
         _check(lib().akv_drop_reposition(self.handle, _ptr(drop_mask), _ptr(new_pos),
                                          _stream(stream)), "akv_drop_reposition")
 
+    def fork(self, dst_of, drop_mask=None, reposition: bool = False, new_pos=None,
+             stream=None):
+        """New position versions: dst_of[b] = destination sequence of source b
+        or -1 (host list)."""
+        import numpy as np
+        arr = np.ascontiguousarray(dst_of, dtype=np.int32)
+        if arr.shape != (self.B,):
+            raise ValueError("dst_of needs one entry per sequence")
+        _check(lib().akv_fork(self.handle, arr.ctypes.data_as(_P), _ptr(drop_mask),
+                              int(bool(reposition)), _ptr(new_pos), _stream(stream)), "akv_fork")
+
     def decode_workspace_bytes(self, n_layers: int, n_q_heads: int) -> int:
         return int(lib().akv_decode_workspace_bytes(self.handle, n_layers, n_q_heads))
 
@@ -206,6 +221,19 @@ class AkvCache:
                                           workspace.numel() * workspace.element_size()
                                           if workspace is not None else 0, _stream(stream)),
                "akv_decode_attention")
+
+    def segment_attention(self, q, seg_seq, seg_q_off, max_q: int, out, layer_begin: int = 0,
+                          n_layers: Optional[int] = None, stream=None):
+        """q/out [n_q][n_layers][Hq][d] bf16; seg_seq [n_seg], seg_q_off
+        [n_seg + 1] int32 device arrays; max_q >= every segment's rows."""
+        nL = self.L - layer_begin if n_layers is None else n_layers
+        n_seg = seg_seq.numel()
+        if seg_q_off.numel() != n_seg + 1:
+            raise ValueError("seg_q_off needs n_segments + 1 entries")
+        _check(lib().akv_segment_attention(self.handle, _ptr(q), _ptr(seg_seq), _ptr(seg_q_off),
+                                           n_seg, int(max_q), layer_begin, nL, q.shape[-2],
+                                           _ptr(out), _stream(stream)),
+               "akv_segment_attention")
 
     def sync_status(self, stream=None) -> int:
         return int(lib().akv_sync_status(self.handle, _stream(stream)))

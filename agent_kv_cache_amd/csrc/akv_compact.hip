@@ -157,7 +157,8 @@ __global__ __launch_bounds__(kChunkPages) void plan_count_kernel(Dev d, const ui
   __shared__ int s_wave[kChunkPages / 64 + 1];
   __shared__ int s_fdrop;
   const int c = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
-  const int len = d.lens[b];
+  // in fork mode only sources with a destination take part
+  const int len = ((mode & M_FORK) && d.fork_dst[b] < 0) ? 0 : d.lens[b];
   const int pg = c * kChunkPages + t;
   if (t == 0) s_fdrop = INT_MAX;
   __syncthreads();
@@ -190,7 +191,7 @@ __global__ __launch_bounds__(kChunkPages) void plan_write_kernel(
   __shared__ int s_src[kChunkPages * kPage], s_dlt[kChunkPages * kPage];
   const int c = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
   const size_t S = (size_t)d.S;
-  const int len = d.lens[b];
+  const int len = ((mode & M_FORK) && d.fork_dst[b] < 0) ? 0 : d.lens[b];
   const int P = (len + kPage - 1) / kPage;
   const int pg = c * kChunkPages + t;
   if (c * kChunkPages < P) {
@@ -251,7 +252,7 @@ __global__ __launch_bounds__(kChunkPages) void plan_write_kernel(
 #pragma unroll
       for (int r = 0; r < kPage; ++r) {
         if (!((keep >> r) & 1u)) continue;
-        if (mode & M_DROP) s_src[j - base] = tb * kPage + r;   // physical slot
+        if (mode & (M_DROP | M_FORK)) s_src[j - base] = tb * kPage + r;   // physical slot
         if (mode & M_REPOS) {
           if ((mode & M_OLDPOS) && o[r] != p[r]) err = max(err, (int)AKV_ERR_POS_MISMATCH);
           int q = j;
@@ -269,7 +270,7 @@ __global__ __launch_bounds__(kChunkPages) void plan_write_kernel(
     }
     __syncthreads();
     for (int i = t; i < total; i += kChunkPages) {
-      if (mode & M_DROP) d.src_map[b * S + base + i] = s_src[i];
+      if (mode & (M_DROP | M_FORK)) d.src_map[b * S + base + i] = s_src[i];
       if (mode & M_REPOS) d.delta_map[b * S + base + i] = s_dlt[i];
     }
     int *si = d.seq_info + (size_t)b * kSeqInfo;
@@ -296,7 +297,8 @@ __global__ __launch_bounds__(kChunkPages) void plan_write_kernel(
     int nm = 0, ni = 0, nf = 0;
     int *si = d.seq_info + (size_t)bb * kSeqInfo;
     if (bb < d.B) {
-      const int L0 = d.lens[bb];
+      const int dst = (mode & M_FORK) ? d.fork_dst[bb] : -1;
+      const int L0 = ((mode & M_FORK) && dst < 0) ? 0 : d.lens[bb];
       const int P0 = (L0 + kPage - 1) / kPage;
       const int nch = (P0 + kChunkPages - 1) / kChunkPages;
       int rnew = 0, fdrop = INT_MAX;
@@ -309,15 +311,21 @@ __global__ __launch_bounds__(kChunkPages) void plan_write_kernel(
       const int e = nch ? __atomic_load_n(&si[SI_ERR], __ATOMIC_RELAXED) : 0;
       const int Pn = (rnew + kPage - 1) / kPage;
       int fbd = P0;
-      if ((mode & M_DROP) && fdrop < L0) {
+      int ee = e;
+      if (mode & M_FORK) {
+        // every survivor goes to fresh pages of the (empty) destination
+        fbd = 0;
+        nm = dst >= 0 ? Pn : 0;
+        if (dst >= 0 && d.lens[dst] != 0) ee = max(ee, (int)AKV_ERR_ARG);
+      } else if ((mode & M_DROP) && fdrop < L0) {
         fbd = fdrop / kPage;
         nm = max(0, Pn - fbd);
         nf = P0 - fbd;
       }
       int fip = P0;
-      int nnext = d.next_pos[bb];
+      int nnext = (mode & M_FORK) && dst < 0 ? 0 : d.next_pos[bb];
       if (mode & M_REPOS) {
-        if (fpos < rnew) {
+        if (fpos < rnew && !(mode & M_FORK)) {
           fip = fpos / kPage;
           ni = max(0, min(fbd, Pn) - fip);
         }
@@ -331,7 +339,8 @@ __global__ __launch_bounds__(kChunkPages) void plan_write_kernel(
       si[SI_N_FREED] = nf;
       si[SI_NEW_NEXT] = nnext;
       si[SI_OLD_LEN] = L0;
-      if (e) atomicMax(&s_gerr, e);
+      si[SI_DST] = dst;
+      if (ee) atomicMax(&s_gerr, ee);
     }
     int tm, ti, tf;
     const int em = block_exclusive_scan<kChunkPages>(nm, s_wave, &tm);
@@ -364,6 +373,7 @@ __global__ __launch_bounds__(kChunkPages) void plan_write_kernel(
       d.ctl[CTL_F_TOTAL] = run_f;
       d.ctl[CTL_FC_OLD] = fc;
       d.ctl[CTL_BASE] = fc - run_m;
+      d.ctl[CTL_MODE] = mode;
     }
     d.ctl[CTL_DONE] = 0;
   }
@@ -460,7 +470,7 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
       const bool valid = j < rnew;
       // physical source slot (page * 16 + row); in place: the slot itself
       const int src = !valid ? 0
-                      : ((mv && (mode & M_DROP)) ? d.src_map[b * S + j]
+                      : ((mv && (mode & (M_DROP | M_FORK))) ? d.src_map[b * S + j]
                                                  : d.table[(size_t)b * d.maxpg + po] * kPage + t);
       const int delta = (valid && (mode & M_REPOS)) ? d.delta_map[b * S + j] : 0;
       s_src[t] = src;
@@ -603,6 +613,22 @@ __global__ __launch_bounds__(256) void commit_kernel(Dev d) {
   const int fbd = si[SI_FBD], nmove = si[SI_N_MOVE], nfreed = si[SI_N_FREED];
   const int moff = si[SI_MOVE_OFF], foff = si[SI_FREED_OFF];
   const int base = d.ctl[CTL_BASE];
+  const int dst = si[SI_DST];
+  if (dst >= 0) {
+    // fork: the new version takes the fresh pages; the source is untouched
+    int32_t *drow = d.table + (size_t)dst * d.maxpg;
+    for (int k = threadIdx.x; k < nmove; k += blockDim.x) drow[k] = d.stage[moff + k];
+    if (threadIdx.x == 0) {
+      d.lens[dst] = si[SI_NEW_LEN];
+      d.next_pos[dst] = si[SI_NEW_NEXT];
+    }
+    if (b == 0 && threadIdx.x == 0) *d.free_count = base + d.ctl[CTL_F_TOTAL];
+    return;
+  }
+  if (d.ctl[CTL_MODE] & M_FORK) {
+    if (b == 0 && threadIdx.x == 0) *d.free_count = base + d.ctl[CTL_F_TOTAL];
+    return;
+  }
   int32_t *trow = d.table + (size_t)b * d.maxpg;
   for (int k = threadIdx.x; k < nfreed; k += blockDim.x) {
     const int po = fbd + k;

@@ -165,6 +165,7 @@ akv_status akv_cache_init(const akv_cache_desc *d, akv_cache **out) {
   v.delta_map = reinterpret_cast<int32_t *>(sb + c->layout.delta_map);
   v.stage = reinterpret_cast<int32_t *>(sb + c->layout.stage);
   v.chunk_info = reinterpret_cast<int32_t *>(sb + c->layout.chunk_info);
+  v.fork_dst = reinterpret_cast<int32_t *>(sb + c->layout.fork_dst);
   v.L = d->n_layers;
   v.H = d->n_kv_heads;
   v.D = d->head_dim;
@@ -260,6 +261,37 @@ akv_status akv_drop_reposition(akv_cache *c, const uint8_t *drop_mask, const int
   return run_compaction(c, drop_mask, new_pos, nullptr, mode, stream);
 }
 
+akv_status akv_fork(akv_cache *c, const int32_t *dst_of, const uint8_t *drop_mask, int reposition,
+                    const int32_t *new_pos, void *stream) {
+  if (!c || !dst_of) return AKV_ERR_ARG;
+  if ((drop_mask && !aligned(drop_mask, 16)) || (new_pos && !aligned(new_pos, 16)))
+    return AKV_ERR_ARG;
+  if (new_pos && !reposition) return AKV_ERR_ARG;
+  const int B = c->desc.n_seqs;
+  std::vector<char> is_dst(B, 0), is_src(B, 0);
+  int n = 0;
+  for (int b = 0; b < B; ++b) {
+    const int e = dst_of[b];
+    if (e < -1 || e >= B || e == b) return AKV_ERR_ARG;
+    if (e >= 0) {
+      if (is_dst[e]) return AKV_ERR_ARG;
+      is_dst[e] = 1;
+      is_src[b] = 1;
+      ++n;
+    }
+  }
+  for (int b = 0; b < B; ++b)
+    if (is_dst[b] && is_src[b]) return AKV_ERR_ARG;   // a destination may not be forked from
+  if (n == 0) return AKV_OK;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  AKV_HIP(hipMemcpyAsync(c->dev.fork_dst, dst_of, sizeof(int32_t) * B, hipMemcpyHostToDevice, st));
+  int mode = akv::M_FORK;
+  if (drop_mask) mode |= akv::M_DROP;
+  if (reposition) mode |= akv::M_REPOS;
+  if (new_pos) mode |= akv::M_NEWPOS;
+  return run_compaction(c, drop_mask, new_pos, nullptr, mode, stream);
+}
+
 size_t akv_decode_workspace_bytes(const akv_cache *c, int32_t n_layers, int32_t n_q_heads) {
   if (!c || n_layers < 1 || n_q_heads < 1) return 0;
   const int ns = nsplit_for(c, n_layers);
@@ -294,6 +326,31 @@ akv_status akv_decode_attention(akv_cache *c, const uint16_t *q, const int32_t *
     AKV_HIP(akv::launch_combine(static_cast<float *>(workspace), out,
                                 c->desc.n_seqs * n_layers * n_q_heads, ns, c->desc.head_dim, st));
   }
+  return AKV_OK;
+}
+
+akv_status akv_segment_attention(akv_cache *c, const uint16_t *q, const int32_t *seg_seq,
+                                 const int32_t *seg_q_off, int32_t n_segments, int32_t max_q,
+                                 int32_t layer_begin, int32_t n_layers, int32_t n_q_heads,
+                                 uint16_t *out, void *stream) {
+  if (!c || n_segments < 0) return AKV_ERR_ARG;
+  if (n_segments == 0) return AKV_OK;
+  if (!q || !out || !seg_seq || !seg_q_off || max_q < 1) return AKV_ERR_ARG;
+  if (layer_begin < 0 || n_layers < 1 || layer_begin + n_layers > c->desc.n_layers)
+    return AKV_ERR_ARG;
+  if (n_q_heads < 1 || n_q_heads % c->desc.n_kv_heads != 0 ||
+      n_q_heads / c->desc.n_kv_heads > 16)
+    return AKV_ERR_ARG;
+  if (!aligned(q, 16) || !aligned(out, 2) || !aligned(seg_seq, 4) || !aligned(seg_q_off, 4))
+    return AKV_ERR_ARG;
+  const int tb = 16 / (n_q_heads / c->desc.n_kv_heads);
+  if (n_segments > 65535 || (long long)n_layers * c->desc.n_kv_heads > 65535 ||
+      (max_q + (long long)tb - 1) / tb > 0x7fffffff)
+    return AKV_ERR_ARG;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  Timed tm(c, AKV_KERNEL_SEGMENT, st);
+  AKV_HIP(akv::launch_segment_attention(c->dev, q, seg_seq, seg_q_off, n_segments, max_q,
+                                        layer_begin, n_layers, n_q_heads, out, st));
   return AKV_OK;
 }
 

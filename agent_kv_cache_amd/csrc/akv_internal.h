@@ -22,6 +22,7 @@ enum Ctl : int {
   CTL_F_TOTAL = 5,    // pages returned to the free stack
   CTL_BASE = 6,       // free_count before the op minus CTL_T_MOVE
   CTL_FC_OLD = 7,     // free_count before the op
+  CTL_MODE = 8,       // mode bits of the planned op
   CTL_COUNT = 64
 };
 
@@ -42,6 +43,7 @@ enum SeqInfo : int {
   SI_OLD_NEXT = 12,
   SI_APP_OFF = 13,   // append: offset of this sequence's tokens in the input
   SI_FPOS = 14,      // first survivor rank whose position changes (atomic min)
+  SI_DST = 15,       // fork: destination sequence (-1 = none)
   kSeqInfo = 16
 };
 
@@ -51,13 +53,14 @@ enum Mode : int {
   M_REPOS = 2,       // positions change (canonical unless M_NEWPOS)
   M_NEWPOS = 4,      // explicit new positions
   M_OLDPOS = 8,      // validate old positions
+  M_FORK = 16,       // write a new position version into an empty sequence
 };
 
 // Device view of one cache, passed by value to every kernel.
 struct Dev {
   uint16_t *k, *v;
   int32_t *table, *lens, *next_pos, *pos, *tok, *free_stack, *free_count;
-  int32_t *ctl, *seq_info, *src_map, *delta_map, *stage, *chunk_info;
+  int32_t *ctl, *seq_info, *src_map, *delta_map, *stage, *chunk_info, *fork_dst;
   const double *theta;        // [d/2]
   int L, H, D, NB, B, maxpg, S, nchunk;   // nchunk: plan chunks per sequence
 };
@@ -81,7 +84,7 @@ __host__ __device__ inline PoolStrides pool_strides(int NB, int H, int D) {
 
 // Scratch layout (byte offsets from the scratch base, each 256-B aligned).
 struct ScratchLayout {
-  size_t ctl, theta, seq_info, src_map, delta_map, stage, chunk_info, total;
+  size_t ctl, theta, seq_info, src_map, delta_map, stage, chunk_info, fork_dst, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -100,6 +103,7 @@ inline ScratchLayout scratch_layout(int B, int S, int NB) {
   s.delta_map = o; o = align256(o + size_t(B) * S * 4);
   s.stage = o;     o = align256(o + size_t(NB) * 4);
   s.chunk_info = o; o = align256(o + size_t(B) * plan_chunks(S / kPage) * 2 * 4);
+  s.fork_dst = o;  o = align256(o + size_t(B) * 4);
   s.total = o;
   return s;
 }
@@ -121,5 +125,8 @@ hipError_t launch_attention(const Dev &d, const uint16_t *q, const int32_t *acti
 int attn_blocks_per_cu(int D);
 hipError_t launch_combine(const float *part, uint16_t *out, int rows, int nsplit,
                           int D, hipStream_t st);
+hipError_t launch_segment_attention(const Dev &d, const uint16_t *q, const int32_t *seg_seq,
+                                    const int32_t *seg_q_off, int n_seg, int max_q, int l0,
+                                    int nL, int Hq, uint16_t *out, hipStream_t st);
 
 }  // namespace akv

@@ -154,6 +154,24 @@ akv_status akv_reposition(akv_cache *c, const int32_t *old_pos,
 akv_status akv_drop_reposition(akv_cache *c, const uint8_t *drop_mask,
                                const int32_t *new_pos, void *stream);
 
+/* New position versions ([CE] sec. 4.2.3, Appendix A.1.1): for every
+ * source sequence b with dst_of[b] >= 0, the empty sequence dst_of[b]
+ * becomes a copy of b's active entries with drop_mask applied (optional)
+ * and, if reposition != 0, its positions moved to new_pos (NULL = canonical
+ * 0..r-1): K re-rotated, V and token ids copied into fresh pages.  The
+ * source sequence is not modified (copy on transform).
+ *   dst_of    : HOST int32 [B]; -1 = no fork.  Host-checked: destinations
+ *               in range, distinct, not equal to their source, and not
+ *               themselves sources.
+ *   drop_mask : DEVICE uint8 [B][S] (row b applies to source b) or NULL
+ *   new_pos   : DEVICE int32 [B][S] by survivor rank of source b, or NULL;
+ *               only with reposition != 0
+ * next_pos of the copy: the source's (no reposition) or last new position
+ * + 1.  Device-checked: a destination that is not empty (AKV_ERR_ARG),
+ * new positions (AKV_ERR_ORDER), free pages (AKV_ERR_NO_BLOCKS). */
+akv_status akv_fork(akv_cache *c, const int32_t *dst_of, const uint8_t *drop_mask,
+                    int reposition, const int32_t *new_pos, void *stream);
+
 /* Decode attention over the active KV for layers
  * [layer_begin, layer_begin + n_layers):
  *   q          : DEVICE bf16 [B][n_layers][n_q_heads][d], already rotated at
@@ -175,6 +193,30 @@ akv_status akv_decode_attention(akv_cache *c, const uint16_t *q,
                                 uint16_t *out, void *workspace,
                                 size_t workspace_bytes, void *stream);
 
+/* Segment-batch attention ([CE] Appendix A.1.1, Figure 10; Section 4.2.2):
+ * the queries of a restore forward, split at drop / reposition boundaries
+ * into segments, each attending causally over its own sequence of the cache
+ * (the original or a position version made by akv_fork), all segments in
+ * one launch, for layers [layer_begin, layer_begin + n_layers).
+ *   q         : DEVICE bf16 [n_q][n_layers][n_q_heads][d], rotated at each
+ *               query token's own position by the caller; segment s owns
+ *               rows [seg_q_off[s], seg_q_off[s+1])
+ *   seg_seq   : DEVICE int32 [n_segments], the sequence segment s reads
+ *   seg_q_off : DEVICE int32 [n_segments + 1], non-decreasing, from 0
+ *   max_q     : HOST, >= every segment's row count n_s (sets the grid)
+ *   out       : DEVICE bf16, same layout as q
+ * The last n_s entries of sequence seg_seq[s] are the segment's own tokens
+ * (already appended): row i of the segment attends to entries
+ * [0, len - n_s + i] of that sequence.  Several segments may read one
+ * sequence.  Host-checked: n_q_heads multiple of n_kv_heads with ratio
+ * <= 16, layer range, 1 <= max_q.  Device-checked (AKV_ERR_ARG latched):
+ * n_s > max_q or n_s < 0 (rows of that segment left unwritten), sequence
+ * out of range or shorter than n_s (rows of that segment set to zero). */
+akv_status akv_segment_attention(akv_cache *c, const uint16_t *q, const int32_t *seg_seq,
+                                 const int32_t *seg_q_off, int32_t n_segments, int32_t max_q,
+                                 int32_t layer_begin, int32_t n_layers, int32_t n_q_heads,
+                                 uint16_t *out, void *stream);
+
 /* Synchronise `stream`, return the latched device error (AKV_OK if none)
  * and clear it. */
 akv_status akv_sync_status(akv_cache *c, void *stream);
@@ -189,7 +231,8 @@ enum {
   AKV_KERNEL_ATTN = 3,     /* split-K decode attention */
   AKV_KERNEL_COMBINE = 4,  /* split-K merge */
   AKV_KERNEL_APPEND = 5,   /* append plan + copy */
-  AKV_KERNEL_COUNT = 6
+  AKV_KERNEL_SEGMENT = 6,  /* segment-batch attention */
+  AKV_KERNEL_COUNT = 7
 };
 akv_status akv_profile_enable(akv_cache *c, int on);
 /* Synchronises the recorded events; *total_ms and *launches accumulate
