@@ -341,7 +341,7 @@ akv_status akv_segment_attention(akv_cache *c, const uint16_t *q, const int32_t 
   if (n_q_heads < 1 || n_q_heads % c->desc.n_kv_heads != 0 ||
       n_q_heads / c->desc.n_kv_heads > 16)
     return AKV_ERR_ARG;
-  if (!aligned(q, 16) || !aligned(out, 2) || !aligned(seg_seq, 4) || !aligned(seg_q_off, 4))
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(seg_seq, 4) || !aligned(seg_q_off, 4))
     return AKV_ERR_ARG;
   const int tb = 16 / (n_q_heads / c->desc.n_kv_heads);
   if (n_segments > 65535 || (long long)n_layers * c->desc.n_kv_heads > 65535 ||

@@ -67,7 +67,7 @@ __global__ __launch_bounds__(kSegWaves * 64, 2) void segment_attn_kernel(
   if (bad && threadIdx.x == 0 && blockIdx.x == 0 && blockIdx.z == 0)
     atomicCAS(&d.ctl[CTL_ERR], 0, (int)AKV_ERR_ARG);
   const int i_col = i0 + tq;                   // row of this column inside the segment
-  const bool col_ok = !bad && i_col < n;
+  const bool col_ok = !bad && tq < TB && i_col < n;
   const int lim = col_ok ? len - n + i_col : -1;          // last visible entry
   const int i_last = min(i0 + TB, n) - 1;
   const int P = bad ? 0 : (len - n + i_last + 1 + kPage - 1) / kPage;
@@ -169,7 +169,7 @@ __global__ __launch_bounds__(kSegWaves * 64, 2) void segment_attn_kernel(
   for (int e = threadIdx.x; e < 16 * D; e += kSegWaves * 64) {
     const int c = e / D, dim = e - c * D;
     const int ti = i0 + c / G;
-    if (ti >= n) continue;
+    if (c / G >= TB || ti >= n) continue;      // columns past 16/G tokens belong to no row
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kSegWaves; ++w) M = fmaxf(M, s_m[w][c]);
@@ -187,12 +187,267 @@ __global__ __launch_bounds__(kSegWaves * 64, 2) void segment_attn_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Long segments: a prefill-shaped kernel.  A workgroup owns 256 columns
+// (256/G query tokens x G heads of one kv head); each of its 8 waves owns 32
+// of them (two MFMA column tiles) and keeps their Q fragments, running max,
+// running sum and O^T accumulators in registers.  The workgroup sweeps the
+// causal KV range in 64-token tiles staged in LDS (K as rows, V transposed)
+// and double-buffered: the next tile's global loads are in flight while the
+// current one is multiplied, so every KV byte is fetched once per workgroup
+// and reused by 256 columns.
+//   S^T tile (16 tokens x 16 columns) = K (16 x 32 dims) * Q^T, 16x16x32 MFMA.
+//   O^T (16 dims x 16 columns) += V^T (16 dims x 32 tokens) * P^T: the 32
+//   tokens of one MFMA step are ordered so that a lane's 8 k-values are the
+//   4 + 4 probabilities it already holds from two S^T tiles.
+// ---------------------------------------------------------------------------
+constexpr int kFaWaves = 8, kFaKT = 64, kFaCols = 256;
+
+template <int D>
+__global__ __launch_bounds__(kFaWaves * 64, 1) void segment_fa_kernel(
+    Dev d, const uint16_t *__restrict__ q, const int32_t *__restrict__ seg_seq,
+    const int32_t *__restrict__ seg_q_off, int max_q, int l0, int nL, int Hq,
+    uint16_t *__restrict__ out) {
+  constexpr int KC = D / 32, NT = D / 16, C8 = D / 8;
+  constexpr int KROW = D + 8, VROW = kFaKT + 8;
+  constexpr int NTH = kFaWaves * 64;
+  constexpr int KPT = kFaKT * C8 / NTH;                  // K chunks per thread
+  constexpr int VPAIRS = (kFaKT / 2) * C8;               // V token-pair chunks per tile
+  constexpr int VPT = (VPAIRS + NTH - 1) / NTH;
+  static_assert(KPT * NTH == kFaKT * C8, "K tile must split evenly");
+  __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kFaKT][KROW];
+  __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][D][VROW];
+
+  const int G = Hq / d.H;
+  const int TBW = kFaCols / G;                            // query tokens per workgroup
+  const int sg = blockIdx.y;
+  const int li = blockIdx.z / d.H, g = blockIdx.z - li * d.H, l = l0 + li;
+  const int q0 = seg_q_off[sg];
+  const int n = seg_q_off[sg + 1] - q0;
+  if (n < 0 || n > max_q) {
+    if (threadIdx.x == 0 && blockIdx.x == 0 && blockIdx.z == 0)
+      atomicCAS(&d.ctl[CTL_ERR], 0, (int)AKV_ERR_ARG);
+    return;
+  }
+  const int i0 = blockIdx.x * TBW;
+  if (i0 >= n) return;
+  const int seq = seg_seq[sg];
+  const int len = (seq >= 0 && seq < d.B) ? d.lens[seq] : -1;
+  const bool bad = len < n;
+  if (bad && threadIdx.x == 0 && blockIdx.x == 0 && blockIdx.z == 0)
+    atomicCAS(&d.ctl[CTL_ERR], 0, (int)AKV_ERR_ARG);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int cl = lane & 15, kg = lane >> 4;
+
+  // this lane's column in each of the wave's two column tiles
+  int lim[2];
+  bool rok[2], cok[2];   // the column is a row of the segment / and the segment is valid
+  size_t qrow[2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const int c = 32 * wave + 16 * ct + cl;
+    const int tq = c / G, hh = c - tq * G, i = i0 + tq;
+    rok[ct] = tq < TBW && i < n;
+    cok[ct] = !bad && rok[ct];
+    lim[ct] = cok[ct] ? len - n + i : -1;
+    qrow[ct] = ((size_t)(q0 + (rok[ct] ? i : 0)) * nL + li) * Hq + (size_t)g * G + hh;
+  }
+  // last entry any valid column of this wave sees
+  int wave_lim = -1;
+  {
+    const int tlo = (32 * wave) / G, thi = min((32 * wave + 31) / G, TBW - 1);
+    if (!bad && tlo < TBW && i0 + tlo < n) wave_lim = len - n + min(i0 + thi, n - 1);
+  }
+  const int last = bad ? -1 : len - n + min(i0 + TBW, n) - 1;
+  const int ntile = (last + kFaKT) / kFaKT;
+
+  bf16x8s qf[2][KC];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+    for (int c = 0; c < KC; ++c)
+      qf[ct][c] = cok[ct] ? seg_load8(q + qrow[ct] * D + 8 * kg + 32 * c)
+                          : __builtin_bit_cast(bf16x8s, make_uint4(0, 0, 0, 0));
+
+  const float scale = 1.4426950408889634f / sqrtf((float)D);
+  float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
+  floatx4s acc[2][NT];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[ct][t] = floatx4s{0.f, 0.f, 0.f, 0.f};
+
+  const int32_t *trow = d.table + (size_t)(bad ? 0 : seq) * d.maxpg;
+  const PoolStrides ps = pool_strides(d.NB, d.H, D);
+  const uint16_t *kb = d.k + (size_t)l * ps.layer + (size_t)g * ps.head;
+  const uint16_t *vb = d.v + (size_t)l * ps.layer + (size_t)g * ps.head;
+  const uint4 z4 = make_uint4(0, 0, 0, 0);
+
+  uint4 rk[KPT], rv[2 * VPT];
+  auto gload = [&](int t) {
+    const int T0 = t * kFaKT;
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) {
+      const int idx = tid + NTH * r, tok = idx / C8, ch = idx - tok * C8, e = T0 + tok;
+      rk[r] = e < len ? *reinterpret_cast<const uint4 *>(kb + (size_t)trow[e >> 4] * ps.page +
+                                                          (e & 15) * D + 8 * ch)
+                      : z4;
+    }
+#pragma unroll
+    for (int r = 0; r < VPT; ++r) {
+      const int idx = tid + NTH * r;
+      const int a = idx & 31, ch = idx >> 5, e = T0 + 2 * a;
+      const bool on = idx < VPAIRS;
+      rv[2 * r] = (on && e < len) ? *reinterpret_cast<const uint4 *>(
+                                        vb + (size_t)trow[e >> 4] * ps.page + (e & 15) * D + 8 * ch)
+                                  : z4;
+      rv[2 * r + 1] = (on && e + 1 < len)
+                          ? *reinterpret_cast<const uint4 *>(vb + (size_t)trow[(e + 1) >> 4] * ps.page +
+                                                             ((e + 1) & 15) * D + 8 * ch)
+                          : z4;
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) {
+      const int idx = tid + NTH * r, tok = idx / C8, ch = idx - tok * C8;
+      *reinterpret_cast<uint4 *>(&s_k[buf][tok][8 * ch]) = rk[r];
+    }
+#pragma unroll
+    for (int r = 0; r < VPT; ++r) {
+      const int idx = tid + NTH * r;
+      if (idx < VPAIRS) {
+        const int a = idx & 31, ch = idx >> 5;
+        const uint32_t *x0 = reinterpret_cast<const uint32_t *>(&rv[2 * r]);
+        const uint32_t *x1 = reinterpret_cast<const uint32_t *>(&rv[2 * r + 1]);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          // dims 8ch+2w (low halves) and 8ch+2w+1 (high halves) of tokens 2a, 2a+1
+          *reinterpret_cast<uint32_t *>(&s_vt[buf][8 * ch + 2 * w][2 * a]) =
+              (x0[w] & 0xffffu) | (x1[w] << 16);
+          *reinterpret_cast<uint32_t *>(&s_vt[buf][8 * ch + 2 * w + 1][2 * a]) =
+              (x0[w] >> 16) | (x1[w] & 0xffff0000u);
+        }
+      }
+    }
+  };
+
+  if (ntile > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+  for (int t = 0; t < ntile; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < ntile) gload(t + 1);
+    const int T0 = t * kFaKT;
+    if (T0 <= wave_lim) {
+      floatx4s sacc[2][4];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        bf16x8s kf[KC];
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+          kf[c] = __builtin_bit_cast(bf16x8s,
+                                     *reinterpret_cast<const uint4 *>(&s_k[buf][16 * tt + cl][32 * c + 8 * kg]));
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          floatx4s sa = floatx4s{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int c = 0; c < KC; ++c) sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[c], qf[ct][c], sa, 0, 0, 0);
+          sacc[ct][tt] = sa;
+        }
+      }
+      bf16x8s pb[2][2];
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        float sv[4][4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int e = T0 + 16 * tt + 4 * kg + j;
+            sv[tt][j] = (e <= lim[ct]) ? sacc[ct][tt][j] * scale : -INFINITY;
+            mx = fmaxf(mx, sv[tt][j]);
+          }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mnew = fmaxf(m[ct], mx);
+        const float alpha = (m[ct] == -INFINITY) ? 0.f : exp2f(m[ct] - mnew);
+        float psum = 0.f;
+        float pj[4][4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            pj[tt][j] = (sv[tt][j] == -INFINITY) ? 0.f : exp2f(sv[tt][j] - mnew);
+            psum += pj[tt][j];
+          }
+        lsum[ct] = lsum[ct] * alpha + psum;
+        m[ct] = mnew;
+#pragma unroll
+        for (int dt = 0; dt < NT; ++dt) acc[ct][dt] *= alpha;
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc)
+          pb[ct][kc] = bf16x8s{(__bf16)pj[2 * kc][0], (__bf16)pj[2 * kc][1], (__bf16)pj[2 * kc][2],
+                               (__bf16)pj[2 * kc][3], (__bf16)pj[2 * kc + 1][0], (__bf16)pj[2 * kc + 1][1],
+                               (__bf16)pj[2 * kc + 1][2], (__bf16)pj[2 * kc + 1][3]};
+      }
+#pragma unroll
+      for (int dt = 0; dt < NT; ++dt)
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+          const uint2 lo = *reinterpret_cast<const uint2 *>(&s_vt[buf][16 * dt + cl][32 * kc + 4 * kg]);
+          const uint2 hi = *reinterpret_cast<const uint2 *>(&s_vt[buf][16 * dt + cl][32 * kc + 16 + 4 * kg]);
+          const bf16x8s vf = __builtin_bit_cast(bf16x8s, make_uint4(lo.x, lo.y, hi.x, hi.y));
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct)
+            acc[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[ct][kc], acc[ct][dt], 0, 0, 0);
+        }
+    }
+    if (t + 1 < ntile) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    float ls = lsum[ct];
+    ls += __shfl_xor(ls, 16, 64);
+    ls += __shfl_xor(ls, 32, 64);
+    if (!rok[ct]) continue;
+    const float inv = cok[ct] ? 1.f / ls : 0.f;   // an invalid segment's rows are zero
+    uint16_t *orow = out + qrow[ct] * D + 4 * kg;
+#pragma unroll
+    for (int dt = 0; dt < NT; ++dt) {
+      const uint32_t w0 = (uint16_t)seg_bf16(acc[ct][dt][0] * inv) |
+                          ((uint32_t)(uint16_t)seg_bf16(acc[ct][dt][1] * inv) << 16);
+      const uint32_t w1 = (uint16_t)seg_bf16(acc[ct][dt][2] * inv) |
+                          ((uint32_t)(uint16_t)seg_bf16(acc[ct][dt][3] * inv) << 16);
+      *reinterpret_cast<uint2 *>(orow + 16 * dt) = make_uint2(w0, w1);
+    }
+  }
+}
+
 hipError_t launch_segment_attention(const Dev &d, const uint16_t *q, const int32_t *seg_seq,
                                     const int32_t *seg_q_off, int n_seg, int max_q, int l0,
                                     int nL, int Hq, uint16_t *out, hipStream_t st) {
   const int G = Hq / d.H;
   const int TB = 16 / G;
-  const dim3 grid((max_q + TB - 1) / TB, n_seg, nL * d.H), block(kSegWaves * 64);
+  const dim3 block(kSegWaves * 64);
+  if (max_q > TB) {
+    // more rows than one 16-column tile holds: the prefill-shaped kernel
+    const int TBW = kFaCols / G;
+    const dim3 grid((max_q + TBW - 1) / TBW, n_seg, nL * d.H), fblock(kFaWaves * 64);
+    if (d.D == 128)
+      hipLaunchKernelGGL(segment_fa_kernel<128>, grid, fblock, 0, st, d, q, seg_seq, seg_q_off,
+                         max_q, l0, nL, Hq, out);
+    else
+      hipLaunchKernelGGL(segment_fa_kernel<64>, grid, fblock, 0, st, d, q, seg_seq, seg_q_off,
+                         max_q, l0, nL, Hq, out);
+    return hipGetLastError();
+  }
+  const dim3 grid((max_q + TB - 1) / TB, n_seg, nL * d.H);
   if (d.D == 128)
     hipLaunchKernelGGL(segment_attn_kernel<128>, grid, block, 0, st, d, q, seg_seq, seg_q_off,
                        max_q, l0, nL, Hq, out);

@@ -224,6 +224,45 @@ def mask_for_messages(token_ids: np.ndarray, hist: History, msg_ids) -> np.ndarr
 WORKLOADS = {"c1": c1, "c2": c2, "c3": c3, "c5": c5}
 
 
+@dataclass
+class Restore:
+    """A request re-run after eviction as segments ([CE] Appendix A.1.1).
+
+    versions[j] = (drop mask over the source sequence, rows of segment j):
+    version j is the source with that mask dropped and its survivors moved
+    to canonical positions; its last `rows` entries are segment j's tokens.
+    """
+    name: str
+    shape: Shape
+    n_tokens: int
+    versions: List[Tuple[np.ndarray, int]]
+    data_seed: int
+    description: str = ""
+
+
+def restore_c2() -> Restore:
+    """The c2 request (32768 tokens, six tool spans) recomputed in seven
+    segments.  Segment 0 is the text before the first span; segment j >= 1
+    is tool span j plus the text up to the next span.  Span j stays visible
+    to its own segment and is dropped (with reposition) before the next one,
+    so segment j attends over: the text of segments 0..j-1 without their
+    spans, then its own tokens."""
+    wl = c2()
+    n = wl.seq_lens[0]
+    sp = sorted(wl.spans[0])
+    starts = [0] + [s for s, _ in sp] + [n]
+    versions = []
+    for j in range(len(sp) + 1):
+        lo, hi = starts[j], starts[j + 1]
+        m = np.zeros(n, dtype=np.uint8)
+        for s, ln in sp[:max(0, j - 1)]:
+            m[s:s + ln] = 1
+        m[hi:] = 1
+        versions.append((m, hi - lo))
+    return Restore("restore_c2", wl.shape, n, versions, wl.data_seed,
+                   "c2 request restored in 7 segments over 7 position versions")
+
+
 # ---------------------------------------------------------------------------
 # bf16 ~N(0,1) tensors
 # ---------------------------------------------------------------------------

@@ -194,6 +194,183 @@ def run_history(args):
     }
 
 
+def restore_counts(rs):
+    """Per-version survivors, rows, attention flops and fork bytes."""
+    sh = rs.shape
+    row = sh.n_layers * sh.n_kv_heads * sh.head_dim * 2
+    out = []
+    for m, n in rs.versions:
+        ln = int((m == 0).sum())
+        pairs = n * (ln - n) + n * (n + 1) // 2          # (row, visible entry) pairs
+        flops = 4 * pairs * sh.head_dim * sh.n_q_heads * sh.n_layers
+        # fork: every survivor's K and V read and written, its position and
+        # token id moved, the mask and positions read
+        fork_b = ln * (2 * row) * 2 + ln * 12 + len(m) + 4 * ln
+        kv_b = ln * 2 * row
+        out.append(dict(len=ln, rows=n, pairs=pairs, flops=flops, fork_bytes=fork_b, kv_bytes=kv_b))
+    return out
+
+
+def restore_cpu_baseline(rs, rows_per_segment: int):
+    """The oracle on one layer: fork every version, then the last
+    `rows_per_segment` rows of each segment (the rows with the longest
+    prefixes; a segment's last k rows form a valid segment on their own)."""
+    from threadpoolctl import threadpool_limits
+
+    from agent_kv_cache_amd import harness as Hn
+    from agent_kv_cache_amd.workloads import randn_bf16
+    from oracle import akv_oracle as O
+    import torch
+
+    sh = rs.shape
+    nv = len(rs.versions)
+    G = sh.n_q_heads // sh.n_kv_heads
+    oc = O.OracleCache(1, 1, sh.head_dim, sh.rope_base, n_seqs=1 + nv)
+    gen = "cuda" if torch.cuda.is_available() else "cpu"
+    n = rs.n_tokens
+    for c in range((n + Hn.CHUNK - 1) // Hn.CHUNK):
+        m = min(Hn.CHUNK, n - c * Hn.CHUNK)
+        k = Hn.seq_chunk(sh, rs.data_seed, 0, c, m, "k", gen)[:1, :, :1]
+        v = Hn.seq_chunk(sh, rs.data_seed, 0, c, m, "v", gen)[:1, :, :1]
+        oc.append(0, c * Hn.CHUNK + np.arange(m), k.permute(1, 0, 2, 3).cpu().double().numpy(),
+                  v.permute(1, 0, 2, 3).cpu().double().numpy())
+    cnt = restore_counts(rs)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for j, (mask, _) in enumerate(rs.versions):
+            oc.fork(0, 1 + j, mask, reposition=True)
+        t1 = time.perf_counter()
+        segs, flops = [], 0
+        for j, (_, rows) in enumerate(rs.versions):
+            k = min(rows_per_segment, rows)
+            q = randn_bf16((k, 1, G, sh.head_dim), 300 + j).double().numpy()
+            segs.append((1 + j, q))
+            ln = cnt[j]["len"]
+            flops += 4 * sum(ln - k + i + 1 for i in range(k)) * sh.head_dim * G
+        t2 = time.perf_counter()
+        O.segment_attention(oc, segs)
+        t3 = time.perf_counter()
+    fork_b = sum(c["fork_bytes"] for c in cnt) / (sh.n_layers * sh.n_kv_heads)
+    return {
+        "value": round(flops / (t3 - t2) / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"layer 0 of {sh.n_layers}, kv head 0 of {sh.n_kv_heads} and its {G} "
+                  f"query heads; segment attention of the last {rows_per_segment} rows of "
+                  f"each of the {nv} segments ({t3 - t2:.2f} s); the {nv} forks of that "
+                  f"layer and head ({t1 - t0:.2f} s); bytes and flops scaled to the sample",
+        "fork_gbps": round(fork_b / (t1 - t0) / 1e9, 4),
+    }
+
+
+def run_restore(args):
+    """Restore of the c2 request after eviction: one step = reset the cache
+    metadata, make the 7 position versions with akv_fork (drop + canonical
+    reposition, source untouched), then one segment-batch attention launch
+    over all 32 layers for the 7 segments (32768 query rows)."""
+    import torch
+
+    from agent_kv_cache_amd import harness as Hn
+    from agent_kv_cache_amd import workloads as W
+
+    rs = W.restore_c2()
+    sh = rs.shape
+    nv = len(rs.versions)
+    cnt = restore_counts(rs)
+    lens = [rs.n_tokens] + [0] * nv
+    extra = sum(Hn.pages_for(c["len"]) for c in cnt) + 8
+    cache = Hn.make_cache(sh, lens, extra, max_blocks_per_seq=Hn.pages_for(rs.n_tokens))
+    cache.reset()
+    Hn.fill(cache, sh, lens, rs.data_seed, gen_device="cuda")
+    dev = cache.device
+    masks = [Hn.mask_tensor(cache, [m]) for m, _ in rs.versions]
+    rows = [c["rows"] for c in cnt]
+    nq = sum(rows)
+    seg_seq = torch.arange(1, 1 + nv, dtype=torch.int32, device=dev)
+    seg_off = torch.tensor(np.concatenate([[0], np.cumsum(rows)]).astype(np.int32), device=dev)
+    max_q = max(rows)
+    q = W.randn_bf16((nq, sh.n_layers, sh.n_q_heads, sh.head_dim), 203, device="cuda")
+    out = torch.empty_like(q)
+    torch.cuda.synchronize()
+    if cache.sync_status() != 0:
+        raise RuntimeError("set-up failed on the device")
+    snap = cache.meta.clone()
+
+    def step():
+        cache.meta.copy_(snap)
+        for j in range(nv):
+            dst = [-1] * (1 + nv)
+            dst[0] = 1 + j
+            cache.fork(dst, masks[j], reposition=True)
+        cache.segment_attention(q, seg_seq, seg_off, max_q, out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if cache.sync_status() != 0:
+        raise RuntimeError("device reported an error during warm-up")
+    cache.profile_read("plan", reset=True)
+    cache.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    cache.profile_enable(False)
+    if cache.sync_status() != 0:
+        raise RuntimeError("device status after the timed steps")
+    kt = {k: cache.profile_read(k) for k in ("plan", "move", "commit", "segment")}
+
+    def tot(k):
+        return kt[k][0] / args.steps
+
+    flops = sum(c["flops"] for c in cnt)
+    fork_b = sum(c["fork_bytes"] for c in cnt)
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    seg_ms = tot("segment")
+    fork_ms = tot("plan") + tot("move") + tot("commit")
+    move_b = sum(c["len"] * 2 * (sh.n_layers * sh.n_kv_heads * sh.head_dim * 2) * 2 for c in cnt)
+    seg_tf = flops / (seg_ms * 1e-3) / 1e12
+    peak_tf = 2500.0
+    res = {
+        "metric": "restore: segment-batch attention TFLOP/s (bf16 MFMA) and fork GB/s, 1 GPU",
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {
+            "workload": f"{rs.name}: {rs.description}",
+            "layers": sh.n_layers, "kv_heads": sh.n_kv_heads, "head_dim": sh.head_dim,
+            "q_heads": sh.n_q_heads, "rope_base": sh.rope_base, "page_tokens": 16,
+            "tokens": rs.n_tokens, "segments": nv, "query_rows": nq,
+            "version_lens": [c["len"] for c in cnt], "segment_rows": rows,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "mfma", "kernel": "segment_fa_kernel",
+            "achieved": round(seg_tf, 1), "peak": peak_tf, "unit": "TFLOP/s",
+            "frac": round(seg_tf / peak_tf, 4), "traffic": None,
+        },
+        "parts": {
+            "segment_attention": {"flops": flops, "ms": round(seg_ms, 4),
+                                  "tflops": round(seg_tf, 1),
+                                  "unique_kv_bytes": sum(c["kv_bytes"] for c in cnt)},
+            "fork": {"algorithmic_bytes": fork_b, "ms": round(fork_ms, 4),
+                     "gbps": round(fork_b / (fork_ms * 1e-3) / 1e9, 1),
+                     "frac_of_peak": round(fork_b / (fork_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                     "kernel_ms": {k: round(tot(k), 4) for k in ("plan", "move", "commit")},
+                     "move_kernel_gbps": round(move_b / (tot("move") * 1e-3) / 1e9, 1),
+                     "launches_per_step": nv},
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = restore_cpu_baseline(rs, args.cpu_rows)
+    return res
+
+
 def calibrate(nbytes: int, reps: int):
     """Achieved GB/s of torch's device copy (read+write), fill (write) and a
     max-reduction (read) over `nbytes`: the plain streaming kernels that bound
@@ -226,7 +403,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--workload", default="c2",
+                    choices=["c1", "c2", "c3", "c4", "c5", "restore"])
+    ap.add_argument("--cpu-rows", type=int, default=256,
+                    help="restore: rows per segment in the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured once in a HIP graph and replayed "
@@ -256,6 +436,9 @@ def main():
     lib()
     if args.workload == "c4":
         print(json.dumps(run_history(args)), flush=True)
+        return
+    if args.workload == "restore":
+        print(json.dumps(run_restore(args)), flush=True)
         return
     wl = W.WORKLOADS[args.workload]()
     sh = wl.shape

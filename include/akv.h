@@ -204,7 +204,7 @@ akv_status akv_decode_attention(akv_cache *c, const uint16_t *q,
  *   seg_seq   : DEVICE int32 [n_segments], the sequence segment s reads
  *   seg_q_off : DEVICE int32 [n_segments + 1], non-decreasing, from 0
  *   max_q     : HOST, >= every segment's row count n_s (sets the grid)
- *   out       : DEVICE bf16, same layout as q
+ *   out       : DEVICE bf16, same layout as q; q and out 16-byte aligned
  * The last n_s entries of sequence seg_seq[s] are the segment's own tokens
  * (already appended): row i of the segment attends to entries
  * [0, len - n_s + i] of that sequence.  Several segments may read one

@@ -281,7 +281,7 @@ def test_fork_errors():
 # ---------------------------------------------------------------------------
 # segment attention on its own
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 8, 16])
 @pytest.mark.parametrize("d", [64, 128])
 def test_segment_attention_gqa(G, d):
     H = 2
@@ -304,6 +304,30 @@ def test_segment_attention_gqa(G, d):
     q1 = q[:, 1:2].contiguous()
     out1 = _segments(cache, q1, segs, layer_begin=1, n_layers=1)
     assert torch.equal(out1, out[:, 1:2])
+
+
+@pytest.mark.parametrize("G", [1, 3, 4, 16])
+def test_segment_attention_short_segments(G):
+    """Every segment within one 16-column tile (16 // G rows): the split-KV
+    kernel; many segments over few sequences, ragged lengths."""
+    H, d = 2, 128
+    sh = W.Shape(3, H, d, H * G, 5.0e5)
+    lens = [5, 16, 17, 300, 1111]
+    tb = 16 // G
+    say(f"case short segments G={G}")
+    cache = Hn.make_cache(sh, lens, 0)
+    cache.reset(np.random.default_rng(40 + G).permutation(cache.NB).astype(np.int32))
+    Hn.fill(cache, sh, lens, 60 + G, gen_device="cpu")
+    oc = oracle_for(sh, lens, 60 + G)
+    rng = np.random.default_rng(G)
+    segs = [(b, int(rng.integers(0, tb + 1))) for b in range(len(lens)) for _ in range(3)]
+    segs = [(b, min(n, lens[b])) for b, n in segs]
+    nq = sum(n for _, n in segs)
+    q = W.randn_bf16((max(nq, 1), sh.n_layers, sh.n_q_heads, d), 700 + G).to(cache.device)
+    out = _segments(cache, q, segs, max_q=tb)
+    assert cache.sync_status() == 0
+    err = _check_segments(oc, q, out, segs)
+    say("short segments max abs err", err)
 
 
 def test_segment_attention_sharp_and_errors():
