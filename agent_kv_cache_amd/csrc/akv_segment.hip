@@ -31,6 +31,9 @@ __device__ __forceinline__ bf16x8s seg_load8(const uint16_t *p) {
   return __builtin_bit_cast(bf16x8s, *reinterpret_cast<const uint4 *>(p));
 }
 __device__ __forceinline__ short seg_bf16(float x) { return __builtin_bit_cast(short, (__bf16)x); }
+// 2^x as the single hardware instruction (no denormal range reduction:
+// results below 2^-126 flush to zero, which softmax weights can afford).
+__device__ __forceinline__ float seg_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <int D>
 __global__ __launch_bounds__(kSegWaves * 64, 2) void segment_attn_kernel(
@@ -130,11 +133,11 @@ __global__ __launch_bounds__(kSegWaves * 64, 2) void segment_attn_kernel(
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float mnew = fmaxf(m, mx);
     // a column may see a page with nothing visible before any visible entry
-    const float alpha = (m == -INFINITY) ? 0.f : exp2f(m - mnew);
+    const float alpha = (m == -INFINITY) ? 0.f : seg_exp2(m - mnew);
     float pj[4], psum = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      pj[j] = (sv[j] == -INFINITY) ? 0.f : exp2f(sv[j] - mnew);
+      pj[j] = (sv[j] == -INFINITY) ? 0.f : seg_exp2(sv[j] - mnew);
       psum += pj[j];
     }
     lsum = lsum * alpha + psum;
@@ -177,7 +180,7 @@ __global__ __launch_bounds__(kSegWaves * 64, 2) void segment_attn_kernel(
     if (M != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < kSegWaves; ++w) {
-        const float f = s_m[w][c] == -INFINITY ? 0.f : exp2f(s_m[w][c] - M);
+        const float f = s_m[w][c] == -INFINITY ? 0.f : seg_exp2(s_m[w][c] - M);
         Lsum += f * s_l[w][c];
         o += f * s_o[w][c][dim];
       }
@@ -201,6 +204,12 @@ __global__ __launch_bounds__(kSegWaves * 64, 2) void segment_attn_kernel(
 //   tokens of one MFMA step are ordered so that a lane's 8 k-values are the
 //   4 + 4 probabilities it already holds from two S^T tiles.
 // ---------------------------------------------------------------------------
+#ifndef AKV_FA_VPAD
+#define AKV_FA_VPAD 4      // halfwords of padding per transposed-V row in LDS
+#endif
+#ifndef AKV_FA_KPAD
+#define AKV_FA_KPAD 8      // halfwords of padding per K row in LDS (keeps 16-B alignment)
+#endif
 constexpr int kFaWaves = 8, kFaKT = 64, kFaCols = 256;
 
 template <int D>
@@ -209,7 +218,7 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void segment_fa_kernel(
     const int32_t *__restrict__ seg_q_off, int max_q, int l0, int nL, int Hq,
     uint16_t *__restrict__ out) {
   constexpr int KC = D / 32, NT = D / 16, C8 = D / 8;
-  constexpr int KROW = D + 8, VROW = kFaKT + 8;
+  constexpr int KROW = D + AKV_FA_KPAD, VROW = kFaKT + AKV_FA_VPAD;
   constexpr int NTH = kFaWaves * 64;
   constexpr int KPT = kFaKT * C8 / NTH;                  // K chunks per thread
   constexpr int VPAIRS = (kFaKT / 2) * C8;               // V token-pair chunks per tile
@@ -253,10 +262,15 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void segment_fa_kernel(
     qrow[ct] = ((size_t)(q0 + (rok[ct] ? i : 0)) * nL + li) * Hq + (size_t)g * G + hh;
   }
   // last entry any valid column of this wave sees
-  int wave_lim = -1;
+  // last entry any valid column of this wave sees, and the first entry some
+  // valid column cannot see (tiles wholly before it need no causal mask)
+  int wave_lim = -1, wave_lo = -1;
   {
     const int tlo = (32 * wave) / G, thi = min((32 * wave + 31) / G, TBW - 1);
-    if (!bad && tlo < TBW && i0 + tlo < n) wave_lim = len - n + min(i0 + thi, n - 1);
+    if (!bad && tlo < TBW && i0 + tlo < n) {
+      wave_lim = len - n + min(i0 + thi, n - 1);
+      wave_lo = len - n + i0 + tlo;
+    }
   }
   const int last = bad ? -1 : len - n + min(i0 + TBW, n) - 1;
   const int ntile = (last + kFaKT) / kFaKT;
@@ -281,45 +295,65 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void segment_fa_kernel(
   const PoolStrides ps = pool_strides(d.NB, d.H, D);
   const uint16_t *kb = d.k + (size_t)l * ps.layer + (size_t)g * ps.head;
   const uint16_t *vb = d.v + (size_t)l * ps.layer + (size_t)g * ps.head;
-  const uint4 z4 = make_uint4(0, 0, 0, 0);
 
+  // Page ids of the tile fetched next are loaded one tile ahead, so a
+  // tile's K/V loads never wait on a table lookup.  Entries past the end of
+  // the sequence read the last entry (always a valid address) and are zeroed
+  // by value, so every load is unconditional.  Only called when len >= 1.
+  int pk[KPT], pv[VPT];
+  auto pidx = [&](int t) {
+    const int T0 = t * kFaKT;
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) {
+      const int tok = (tid + NTH * r) / C8;
+      pk[r] = trow[min(T0 + tok, len - 1) >> 4];
+    }
+#pragma unroll
+    for (int r = 0; r < VPT; ++r) {
+      const int idx = tid + NTH * r;
+      const int a = idx < VPAIRS ? (idx & 31) : 0;
+      pv[r] = trow[min(T0 + 2 * a, len - 1) >> 4];
+    }
+  };
   uint4 rk[KPT], rv[2 * VPT];
   auto gload = [&](int t) {
     const int T0 = t * kFaKT;
 #pragma unroll
     for (int r = 0; r < KPT; ++r) {
       const int idx = tid + NTH * r, tok = idx / C8, ch = idx - tok * C8, e = T0 + tok;
-      rk[r] = e < len ? *reinterpret_cast<const uint4 *>(kb + (size_t)trow[e >> 4] * ps.page +
-                                                          (e & 15) * D + 8 * ch)
-                      : z4;
+      const int ec = min(e, len - 1);
+      rk[r] = *reinterpret_cast<const uint4 *>(kb + (size_t)pk[r] * ps.page + (ec & 15) * D + 8 * ch);
     }
 #pragma unroll
     for (int r = 0; r < VPT; ++r) {
       const int idx = tid + NTH * r;
-      const int a = idx & 31, ch = idx >> 5, e = T0 + 2 * a;
       const bool on = idx < VPAIRS;
-      rv[2 * r] = (on && e < len) ? *reinterpret_cast<const uint4 *>(
-                                        vb + (size_t)trow[e >> 4] * ps.page + (e & 15) * D + 8 * ch)
-                                  : z4;
-      rv[2 * r + 1] = (on && e + 1 < len)
-                          ? *reinterpret_cast<const uint4 *>(vb + (size_t)trow[(e + 1) >> 4] * ps.page +
-                                                             ((e + 1) & 15) * D + 8 * ch)
-                          : z4;
+      const int a = on ? (idx & 31) : 0, ch = on ? (idx >> 5) : 0, e = T0 + 2 * a;
+      // e is even, so e and e + 1 (each clamped to len - 1) share a page
+      const uint16_t *pg = vb + (size_t)pv[r] * ps.page;
+      rv[2 * r] = *reinterpret_cast<const uint4 *>(pg + (min(e, len - 1) & 15) * D + 8 * ch);
+      rv[2 * r + 1] = *reinterpret_cast<const uint4 *>(pg + (min(e + 1, len - 1) & 15) * D + 8 * ch);
     }
   };
-  auto lstore = [&](int buf) {
+  // registers -> LDS; entries past the end of the sequence become zeros here
+  auto lstore = [&](int t, int buf) {
+    const int T0 = t * kFaKT;
 #pragma unroll
     for (int r = 0; r < KPT; ++r) {
       const int idx = tid + NTH * r, tok = idx / C8, ch = idx - tok * C8;
-      *reinterpret_cast<uint4 *>(&s_k[buf][tok][8 * ch]) = rk[r];
+      uint4 x = rk[r];
+      if (T0 + tok >= len) x = make_uint4(0u, 0u, 0u, 0u);
+      *reinterpret_cast<uint4 *>(&s_k[buf][tok][8 * ch]) = x;
     }
 #pragma unroll
     for (int r = 0; r < VPT; ++r) {
       const int idx = tid + NTH * r;
       if (idx < VPAIRS) {
-        const int a = idx & 31, ch = idx >> 5;
-        const uint32_t *x0 = reinterpret_cast<const uint32_t *>(&rv[2 * r]);
-        const uint32_t *x1 = reinterpret_cast<const uint32_t *>(&rv[2 * r + 1]);
+        const int a = idx & 31, ch = idx >> 5, e = T0 + 2 * a;
+        uint4 v0 = rv[2 * r], v1 = rv[2 * r + 1];
+        if (e >= len) v0 = make_uint4(0u, 0u, 0u, 0u);
+        if (e + 1 >= len) v1 = make_uint4(0u, 0u, 0u, 0u);
+        const uint32_t x0[4] = {v0.x, v0.y, v0.z, v0.w}, x1[4] = {v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           // dims 8ch+2w (low halves) and 8ch+2w+1 (high halves) of tokens 2a, 2a+1
@@ -333,13 +367,19 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void segment_fa_kernel(
   };
 
   if (ntile > 0) {
+    pidx(0);
     gload(0);
-    lstore(0);
+    if (ntile > 1) pidx(1);
+    lstore(0, 0);
   }
+  // Q and the first tile are in registers / LDS before the loop: no wait on
+  // the loop's own prefetches inside it
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int t = 0; t < ntile; ++t) {
     const int buf = t & 1;
     if (t + 1 < ntile) gload(t + 1);
+    if (t + 2 < ntile) pidx(t + 2);
     const int T0 = t * kFaKT;
     if (T0 <= wave_lim) {
       floatx4s sacc[2][4];
@@ -359,35 +399,45 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void segment_fa_kernel(
         }
       }
       bf16x8s pb[2][2];
+      const bool diag = T0 + kFaKT - 1 > wave_lo;            // wave-uniform
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
-        float sv[4][4];
-        float mx = -INFINITY;
+        // running max kept on raw scores; the softmax scale is folded into
+        // one FMA per score: p = 2^(s*scale - m*scale)
+        if (diag) {
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (T0 + 16 * tt + 4 * kg + j > lim[ct]) sacc[ct][tt][j] = -INFINITY;
+        }
+        float mx = sacc[ct][0][0];
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int e = T0 + 16 * tt + 4 * kg + j;
-            sv[tt][j] = (e <= lim[ct]) ? sacc[ct][tt][j] * scale : -INFINITY;
-            mx = fmaxf(mx, sv[tt][j]);
-          }
+          for (int j = 0; j < 4; ++j) mx = fmaxf(mx, sacc[ct][tt][j]);
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         const float mnew = fmaxf(m[ct], mx);
-        const float alpha = (m[ct] == -INFINITY) ? 0.f : exp2f(m[ct] - mnew);
-        float psum = 0.f;
+        // nothing visible yet: keep the reference finite so 2^(-inf) = 0
+        const float mref = (mnew == -INFINITY) ? 0.f : mnew * scale;
+        if (__any(mnew > m[ct])) {
+          const float alpha = (m[ct] == -INFINITY) ? 0.f : seg_exp2(m[ct] * scale - mref);
+          lsum[ct] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < NT; ++dt) acc[ct][dt] *= alpha;
+        }
+        m[ct] = mnew;
         float pj[4][4];
+        float psum = 0.f;
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            pj[tt][j] = (sv[tt][j] == -INFINITY) ? 0.f : exp2f(sv[tt][j] - mnew);
+            pj[tt][j] = seg_exp2(fmaf(sacc[ct][tt][j], scale, -mref));
             psum += pj[tt][j];
           }
-        lsum[ct] = lsum[ct] * alpha + psum;
-        m[ct] = mnew;
-#pragma unroll
-        for (int dt = 0; dt < NT; ++dt) acc[ct][dt] *= alpha;
+        lsum[ct] += psum;
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc)
           pb[ct][kc] = bf16x8s{(__bf16)pj[2 * kc][0], (__bf16)pj[2 * kc][1], (__bf16)pj[2 * kc][2],
@@ -406,7 +456,7 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void segment_fa_kernel(
             acc[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[ct][kc], acc[ct][dt], 0, 0, 0);
         }
     }
-    if (t + 1 < ntile) lstore(buf ^ 1);
+    if (t + 1 < ntile) lstore(t + 1, buf ^ 1);
     __syncthreads();
   }
 
