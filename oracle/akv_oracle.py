@@ -43,6 +43,12 @@ What is computed (every function below is the plain definition):
   queries into segments; each segment applies standard causal attention over
   its own KV list, whose last n entries are the segment's own tokens.
 
+* RoPE variants ([AKV] sec. 5.5): partial RoPE rotates only the first
+  rotary_dim dimensions (pairs (i, i + rotary_dim/2)) and copies the rest of
+  K; sliding-window layers read, per query, the entries whose position lies
+  in the window (positions, not indices, after a drop); frequencies may be
+  replaced by a caller table (Llama 3.1 / YaRN rules below, not on the pages).
+
 Readings where the pages are silent (each listed in the design doc):
   pairing/sign of RoPE (NeoX half split, +p*theta), theta_i without scaling,
   one fp64 rounding to bf16 (round half to even) per rotated element, no
@@ -65,6 +71,8 @@ __all__ = [
     "bf16_from_bits",
     "bf16_ulp_distance",
     "rope_theta",
+    "llama3_theta",
+    "yarn_theta",
     "rotate_pairs",
     "rerotate_keys",
     "attend",
@@ -132,10 +140,66 @@ def bf16_ulp_distance(a_bits, b_bits) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # RoPE re-rotation ([CE] sec. 3.3, eq. 5; [AKV] sec. 5.5)
 # ---------------------------------------------------------------------------
-def rope_theta(head_dim: int, base: float) -> np.ndarray:
-    """theta_i = base^(-2i/d) for i in [0, d/2), float64, no frequency scaling."""
-    i = np.arange(head_dim // 2, dtype=np.float64)
-    return np.power(np.float64(base), -2.0 * i / head_dim)
+def rope_theta(head_dim: int, base: float, rotary_dim: Optional[int] = None) -> np.ndarray:
+    """theta_i = base^(-2i/r) for i in [0, r/2), float64, no frequency scaling.
+
+    r = rotary_dim (default head_dim).  With partial RoPE only the first r
+    dimensions of a head are rotated ([AKV] sec. 5.5: the rest of K is copied).
+    """
+    r = head_dim if rotary_dim is None else int(rotary_dim)
+    if r % 2 or not 0 < r <= head_dim:
+        raise ValueError("rotary_dim must be even and in (0, head_dim]")
+    i = np.arange(r // 2, dtype=np.float64)
+    return np.power(np.float64(base), -2.0 * i / r)
+
+
+def llama3_theta(theta: np.ndarray, factor: float, low_freq_factor: float,
+                 high_freq_factor: float, original_max_pos: int) -> np.ndarray:
+    """Frequencies of the Llama 3.1 RoPE scaling rule applied to theta.
+
+    Not on the pages: the published rule of the Llama 3.1 release, written
+    here from its definition.  With wavelength w = 2 pi / theta and the
+    original context length C: w < C / high_freq_factor keeps theta;
+    w > C / low_freq_factor divides it by factor; in between it blends
+    linearly in C / w: s = (C / w - low) / (high - low),
+    theta' = (1 - s) theta / factor + s theta.
+    """
+    theta = np.asarray(theta, dtype=np.float64)
+    w = 2.0 * np.pi / theta
+    lo_w = original_max_pos / low_freq_factor
+    hi_w = original_max_pos / high_freq_factor
+    s = (original_max_pos / w - low_freq_factor) / (high_freq_factor - low_freq_factor)
+    mid = (1.0 - s) * theta / factor + s * theta
+    return np.where(w < hi_w, theta, np.where(w > lo_w, theta / factor, mid))
+
+
+def yarn_theta(rotary_dim: int, base: float, factor: float, original_max_pos: int,
+               beta_fast: float = 32.0, beta_slow: float = 1.0) -> np.ndarray:
+    """Frequencies of YaRN's "NTK-by-parts" interpolation.
+
+    Not on the pages: the published method (Peng et al., 2023), written here
+    from its definition.  Dimension pair i turns original_max_pos * theta_i /
+    (2 pi) times over the original context; pairs that turn more than
+    beta_fast times keep theta_i, pairs that turn fewer than beta_slow times
+    use theta_i / factor, and a linear ramp in i joins the two.  The ramp ends
+    are the (real) pair indices where the turn count equals beta_fast and
+    beta_slow, floored and ceiled, clamped to [0, r - 1].  YaRN's attention
+    temperature scales cos and sin of every position alike, so it does not
+    enter a re-rotation R(q - p).
+    """
+    r = int(rotary_dim)
+    theta = rope_theta(r, base)
+
+    def pair_at(turns):
+        return r * np.log(original_max_pos / (turns * 2.0 * np.pi)) / (2.0 * np.log(base))
+
+    lo = max(int(np.floor(pair_at(beta_fast))), 0)
+    hi = min(int(np.ceil(pair_at(beta_slow))), r - 1)
+    if lo == hi:
+        hi = lo + 1e-3
+    i = np.arange(r // 2, dtype=np.float64)
+    ramp = np.clip((i - lo) / (hi - lo), 0.0, 1.0)      # 0: keep, 1: interpolate
+    return theta * (1.0 - ramp) + (theta / factor) * ramp
 
 
 def rotate_pairs(k: np.ndarray, delta, theta: np.ndarray) -> np.ndarray:
@@ -143,17 +207,24 @@ def rotate_pairs(k: np.ndarray, delta, theta: np.ndarray) -> np.ndarray:
 
     k: [..., d].  delta: int array broadcastable to k.shape[:-1] (typically
     one value per token, shape [n, 1, 1] against k [n, L, H, d]).
-    Pair i is (k[..., i], k[..., i + d/2]); it turns by the angle
+    The rotary part is the first r = 2 * len(theta) dimensions (r = d for
+    full RoPE).  Pair i is (k[..., i], k[..., i + r/2]); it turns by the angle
     delta * theta_i (one fp64 product of the exact integer and theta_i):
         x' = x cos - y sin,   y' = y cos + x sin.
+    Dimensions [r, d) are returned unchanged ([AKV] sec. 5.5).
     """
     k = np.asarray(k, dtype=np.float64)
-    half = k.shape[-1] // 2
+    half = np.asarray(theta).shape[-1]
+    r = 2 * half
+    if r > k.shape[-1]:
+        raise ValueError("rotate_pairs: more frequencies than dimension pairs")
     d = np.asarray(delta, dtype=np.float64)[..., None]      # [..., 1]
-    ang = d * theta                                           # [..., d/2]
+    ang = d * theta                                           # [..., r/2]
     c, s = np.cos(ang), np.sin(ang)
-    x, y = k[..., :half], k[..., half:]
-    return np.concatenate([x * c - y * s, y * c + x * s], axis=-1)
+    x, y = k[..., :half], k[..., half:r]
+    xr, yr = x * c - y * s, y * c + x * s
+    tail = np.broadcast_to(k[..., r:], xr.shape[:-1] + (k.shape[-1] - r,))
+    return np.concatenate([xr, yr, tail], axis=-1)
 
 
 def rerotate_keys(k: np.ndarray, delta: np.ndarray, theta: np.ndarray) -> np.ndarray:
@@ -214,11 +285,27 @@ class OracleCache:
     """
 
     def __init__(self, n_layers: int, n_kv_heads: int, head_dim: int,
-                 rope_base: float, n_seqs: int = 1, with_kv: bool = True):
+                 rope_base: float, n_seqs: int = 1, with_kv: bool = True,
+                 rotary_dim: Optional[int] = None, theta: Optional[np.ndarray] = None,
+                 window: Optional[Sequence[int]] = None):
+        """rotary_dim: partial RoPE (first rotary_dim dims rotated, default
+        head_dim); theta: explicit frequencies (rotary_dim / 2 values, e.g.
+        from llama3_theta / yarn_theta) instead of base^(-2i/r); window: per
+        layer sliding-window length (0 or None = full attention)."""
         if head_dim % 2:
             raise ValueError("head_dim must be even for half-split RoPE")
         self.n_layers, self.n_kv_heads, self.head_dim = n_layers, n_kv_heads, head_dim
-        self.theta = rope_theta(head_dim, rope_base)
+        r = head_dim if rotary_dim is None else int(rotary_dim)
+        if theta is None:
+            self.theta = rope_theta(head_dim, rope_base, r)
+        else:
+            self.theta = np.asarray(theta, dtype=np.float64).reshape(-1)
+            if 2 * self.theta.shape[0] != r:
+                raise ValueError("theta needs rotary_dim / 2 values")
+        self.rotary_dim = r
+        self.window = [0] * n_layers if window is None else [int(w or 0) for w in window]
+        if len(self.window) != n_layers or min(self.window) < 0:
+            raise ValueError("window needs one value >= 0 per layer")
         self.with_kv = with_kv
         shape = (0, n_layers, n_kv_heads, head_dim)
         self.seqs: List[SeqState] = [
@@ -316,10 +403,26 @@ class OracleCache:
             self.reposition(dst, new_pos)
 
     # -- decode attention over the active KV ------------------------------
-    def decode_attention(self, b: int, q, active_len: Optional[int] = None) -> np.ndarray:
-        """o[l, h] = attend(q[l, h], K[:n, l, h // G], V[:n, l, h // G]).
+    def visible(self, b: int, upto: int, qpos: int, layer: int) -> np.ndarray:
+        """Indices a query at position qpos sees among the first `upto` entries.
 
-        q: [L, Hq, d] (bf16 values).  n = active_len (default: all entries).
+        Full attention: all of them.  Sliding window W ([AKV] sec. 5.5, the
+        attention plan): the entries whose *position* is at least
+        qpos - W + 1.  After a drop without reposition positions have gaps,
+        so the window is not the last W indices.
+        """
+        idx = np.arange(upto)
+        w = self.window[layer]
+        if w:
+            idx = idx[self.seqs[b].pos[:upto] >= qpos - w + 1]
+        return idx
+
+    def decode_attention(self, b: int, q, active_len: Optional[int] = None) -> np.ndarray:
+        """o[l, h] = attend(q[l, h], K[vis, l, h // G], V[vis, l, h // G]).
+
+        q: [L, Hq, d] (bf16 values).  vis = the first active_len entries
+        (default: all), cut by the layer's sliding window for a query at
+        position next_pos (the token being decoded).
         """
         s = self.seqs[b]
         q = np.asarray(q, dtype=np.float64)
@@ -330,9 +433,10 @@ class OracleCache:
         G = Hq // self.n_kv_heads
         out = np.zeros((L, Hq, d))
         for l in range(L):
+            vis = self.visible(b, n, s.next_pos, l)
             for h in range(Hq):
                 g = h // G
-                out[l, h] = attend(q[l, h], s.k[:n, l, g], s.v[:n, l, g])
+                out[l, h] = attend(q[l, h], s.k[vis, l, g], s.v[vis, l, g])
         return out
 
 
@@ -341,7 +445,8 @@ def segment_attention(cache: "OracleCache", segments) -> list:
 
     segments: list of (b, q) with q [n, L, Hq, d]: the n query rows are the
     last n entries of sequence b (the segment's own tokens); row i attends to
-    entries [0, len_b - n + i].  Returns one [n, L, Hq, d] array per segment.
+    entries [0, len_b - n + i], cut by the layer's sliding window for a query
+    at that row's own position.  Returns one [n, L, Hq, d] array per segment.
     """
     out = []
     for b, q in segments:
@@ -354,10 +459,11 @@ def segment_attention(cache: "OracleCache", segments) -> list:
         G = Hq // cache.n_kv_heads
         o = np.zeros_like(q)
         for i in range(n):
-            vis = len(s) - n + i + 1
+            me = len(s) - n + i                       # this row's own entry
             for l in range(L):
+                vis = cache.visible(b, me + 1, int(s.pos[me]), l)
                 for h in range(Hq):
-                    o[i, l, h] = attend(q[i, l, h], s.k[:vis, l, h // G], s.v[:vis, l, h // G])
+                    o[i, l, h] = attend(q[i, l, h], s.k[vis, l, h // G], s.v[vis, l, h // G])
         out.append(o)
     return out
 
