@@ -39,6 +39,7 @@ class AkvCacheDesc(C.Structure):
         ("seq_lens", C.c_void_p), ("next_pos", C.c_void_p), ("positions", C.c_void_p),
         ("token_ids", C.c_void_p), ("free_stack", C.c_void_p), ("free_count", C.c_void_p),
         ("scratch", C.c_void_p), ("scratch_bytes", C.c_size_t),
+        ("rotary_dim", C.c_int32), ("inv_freq", C.c_void_p), ("layer_window", C.c_void_p),
     ]
 
 
@@ -119,9 +120,14 @@ class AkvCache:
 
     def __init__(self, n_layers: int, n_kv_heads: int, head_dim: int, n_blocks: int,
                  n_seqs: int, max_blocks_per_seq: int, rope_base: float,
-                 device: str = "cuda", k_pool=None, v_pool=None):
+                 device: str = "cuda", k_pool=None, v_pool=None, rotary_dim: int = 0,
+                 inv_freq=None, layer_window=None):
         """k_pool / v_pool: optional caller-placed bf16 tensors of shape
-        [L][NB][Hkv][16][d] (e.g. views of one larger buffer)."""
+        [L][NB][Hkv][16][d] (e.g. views of one larger buffer).
+        rotary_dim: partial RoPE (0 = head_dim); inv_freq: host sequence of
+        rotary_dim/2 frequencies (None = rope_base^(-2i/r)); layer_window:
+        host sequence of per-layer sliding-window lengths (0 = full)."""
+        import numpy as np
         import torch
         self.L, self.H, self.D = n_layers, n_kv_heads, head_dim
         self.NB, self.B, self.maxpg = n_blocks, n_seqs, max_blocks_per_seq
@@ -152,6 +158,21 @@ class AkvCache:
         self.free_stack = self.meta[self._o_fs:]
         desc = AkvCacheDesc(n_layers, n_kv_heads, head_dim, PAGE, n_blocks, n_seqs,
                             max_blocks_per_seq, self.rope_base)
+        self.rotary_dim = int(rotary_dim) or head_dim
+        desc.rotary_dim = int(rotary_dim)
+        # host arrays are copied by akv_cache_init; keep them alive until then
+        self._inv_freq = (None if inv_freq is None
+                          else np.ascontiguousarray(inv_freq, dtype=np.float64).reshape(-1))
+        if self._inv_freq is not None:
+            if self._inv_freq.shape[0] != self.rotary_dim // 2:
+                raise ValueError("inv_freq needs rotary_dim / 2 values")
+            desc.inv_freq = self._inv_freq.ctypes.data
+        self._window = (None if layer_window is None
+                        else np.ascontiguousarray(layer_window, dtype=np.int32).reshape(-1))
+        if self._window is not None:
+            if self._window.shape[0] != n_layers:
+                raise ValueError("layer_window needs one value per layer")
+            desc.layer_window = self._window.ctypes.data
         nbytes = lib().akv_scratch_bytes(C.byref(desc))
         if nbytes == 0:
             raise AkvError(1, "akv_scratch_bytes")

@@ -39,6 +39,17 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t *p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(p));
 }
 
+#ifndef AKV_ATTN_FAST_EXP
+#define AKV_ATTN_FAST_EXP 0    // 1: softmax uses the bare v_exp_f32 (no denormal range reduction)
+#endif
+__device__ __forceinline__ float attn_exp2(float x) {
+#if AKV_ATTN_FAST_EXP
+  return __builtin_amdgcn_exp2f(x);
+#else
+  return exp2f(x);
+#endif
+}
+
 __device__ __forceinline__ short f32_to_bf16_bits(float x) {
   return __builtin_bit_cast(short, (__bf16)x);
 }
@@ -73,9 +84,21 @@ __global__ __launch_bounds__(kAttnWaves * 64, AKV_ATTN_MIN_WAVES) void attn_kern
     if (threadIdx.x == 0 && s == 0 && g == 0) atomicCAS(&d.ctl[CTL_ERR], 0, (int)AKV_ERR_ARG);
     len = len < 0 ? 0 : seqlen;
   }
+  const int32_t *trow = d.table + (size_t)b * d.maxpg;
+  // Sliding window: the query sits at next_pos and reads the entries whose
+  // position is >= next_pos - W + 1; at most W - 1 entries qualify, so the
+  // first of them is searched among the last W - 1.
+  int f = 0;
+  if (d.any_window) {
+    const int W = d.window[l];
+    if (W > 0) f = min(len, first_pos_at_least(d, trow, max(0, seqlen - W + 1), seqlen,
+                                               d.next_pos[b] - W + 1));
+  }
   const int P = (len + kPage - 1) / kPage;
-  const int chunk = (P + nsplit - 1) / nsplit;
-  const int p0 = s * chunk, p1 = min(P, p0 + chunk);
+  const int pstart = f / kPage;
+  const int npg = f < len ? P - pstart : 0;
+  const int chunk = (npg + nsplit - 1) / nsplit;
+  const int p0 = pstart + s * chunk, p1 = min(pstart + npg, p0 + chunk);
 
   // Query rows as the B operand: column hh = query head g*G + hh.
   bf16x8 qb[KC];
@@ -94,7 +117,6 @@ __global__ __launch_bounds__(kAttnWaves * 64, AKV_ATTN_MIN_WAVES) void attn_kern
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  const int32_t *trow = d.table + (size_t)b * d.maxpg;
   const PoolStrides ps = pool_strides(d.NB, d.H, D);
   const size_t head_base = (size_t)l * ps.layer + (size_t)g * ps.head;
   const size_t page_stride = ps.page;
@@ -137,16 +159,16 @@ __global__ __launch_bounds__(kAttnWaves * 64, AKV_ATTN_MIN_WAVES) void attn_kern
     const int tok0 = p * kPage + 4 * kg;
     float sv[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sv[j] = (tok0 + j < len) ? sacc[j] * scale : -INFINITY;
+    for (int j = 0; j < 4; ++j) sv[j] = (tok0 + j < len && tok0 + j >= f) ? sacc[j] * scale : -INFINITY;
     float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float mnew = fmaxf(m, mx);
-    const float alpha = exp2f(m - mnew);
+    const float alpha = attn_exp2(m - mnew);
     float pj[4], ps = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      pj[j] = exp2f(sv[j] - mnew);
+      pj[j] = attn_exp2(sv[j] - mnew);
       ps += pj[j];
     }
     lsum = lsum * alpha + ps;

@@ -434,6 +434,13 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
   const long long u1 = units * (blockIdx.x + 1) / gridDim.x;
   const int t = threadIdx.x;
   const int r = (t % TPH) / CH, pc = t % CH, slot = t / TPH;
+  // Chunk pc of a row: a rotary chunk pairs dims [8pc, 8pc+8) with the same
+  // dims + RD/2; past the rotary part ([RD, D), partial RoPE) chunks are only
+  // copied, paired the same way over the tail.
+  const int rch = d.RD / 16;
+  const bool rot_chunk = pc < rch;
+  const int xo = rot_chunk ? 8 * pc : d.RD + 8 * (pc - rch);
+  const int yoff = rot_chunk ? d.RD / 2 : (D - d.RD) / 2;
   const size_t S = (size_t)d.S;
   const PoolStrides ps = pool_strides(d.NB, d.H, D);
   const size_t hstride = ps.head, lstride = ps.layer;
@@ -500,9 +507,10 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
         s_nrep = n;
       }
       __syncthreads();
-      const int ntask = s_nrep * HALF;
+      const int RH = d.RD / 2;
+      const int ntask = s_nrep * RH;
       for (int task = t; task < ntask; task += kMoveThreads) {
-        const int ri = task / HALF, i = task - ri * HALF;
+        const int ri = task / RH, i = task - ri * RH;
         const int dl = s_repval[ri];
         double sn = 0.0, cs = 1.0;
         if (dl != 0) sincos((double)dl * d.theta[i], &sn, &cs);
@@ -513,8 +521,9 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
     const bool valid = s_valid[r] != 0;
     const int delta = s_delta[r];
     // cos/sin of this thread's 8 pairs stay in LDS and are read per use
-    const double2 *cs_row = &s_cs[(rot_any && delta != 0) ? s_rep[r] : 0][8 * pc];
-    const bool do_k = valid ? (mv || delta != 0) : mv;
+    const double2 *cs_row = &s_cs[(rot_any && delta != 0) ? s_rep[r] : 0][rot_chunk ? 8 * pc : 0];
+    const bool turn = valid && delta != 0 && rot_chunk;
+    const bool do_k = valid ? (mv || turn) : mv;
     const bool do_v = mv;
     if (!do_k) continue;
     const int nsl = (l1 - l0) * d.H;
@@ -524,14 +533,14 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
     const int rot = (int)((pgl * 7) % d.L);
 #endif
     const int sp = s_src[r];
-    const size_t src_row = (size_t)(sp >> 4) * ps.page + (size_t)(sp & 15) * D + 8 * pc;
-    const size_t dst_row = (size_t)dst * ps.page + (size_t)r * D + 8 * pc;
+    const size_t src_row = (size_t)(sp >> 4) * ps.page + (size_t)(sp & 15) * D + xo;
+    const size_t dst_row = (size_t)dst * ps.page + (size_t)r * D + xo;
 #if AKV_MOVE_SPLIT_KV
     // K slices of the unit range first, then V slices: each pass streams one
     // pool (two concurrent streams per workgroup instead of four)
     for (int plane = 0; plane < (do_v ? 2 : 1); ++plane) {
       uint16_t *pool = plane ? d.v : d.k;
-      const bool rot_plane = plane == 0 && valid && delta != 0;
+      const bool rot_plane = plane == 0 && turn;
       for (int i0 = slot; i0 < nsl; i0 += NS * U) {
         u32x4 lo[U], hi[U];
         size_t dofs[U];
@@ -546,7 +555,7 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
           lo[u] = hi[u] = u32x4{0u, 0u, 0u, 0u};
           if (on[u] && valid) {
             lo[u] = ld_stream(pool + src_row + off);
-            hi[u] = ld_stream(pool + src_row + off + HALF);
+            hi[u] = ld_stream(pool + src_row + off + yoff);
           }
         }
 #pragma unroll
@@ -554,7 +563,7 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
           if (!on[u]) continue;
           if (rot_plane) rotate8(lo[u], hi[u], cs_row);
           st_stream(pool + dofs[u], lo[u]);
-          st_stream(pool + dofs[u] + HALF, hi[u]);
+          st_stream(pool + dofs[u] + yoff, hi[u]);
         }
       }
     }
@@ -580,22 +589,22 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
         if (on[u] && valid) {
           const size_t so = src_row + off;
           klo[u] = ld_stream(d.k + so);
-          khi[u] = ld_stream(d.k + so + HALF);
+          khi[u] = ld_stream(d.k + so + yoff);
           if (do_v) {
             vlo[u] = ld_stream(d.v + so);
-            vhi[u] = ld_stream(d.v + so + HALF);
+            vhi[u] = ld_stream(d.v + so + yoff);
           }
         }
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (!on[u]) continue;
-        if (valid && delta != 0) rotate8(klo[u], khi[u], cs_row);
+        if (turn) rotate8(klo[u], khi[u], cs_row);
         st_stream(d.k + dofs[u], klo[u]);
-        st_stream(d.k + dofs[u] + HALF, khi[u]);
+        st_stream(d.k + dofs[u] + yoff, khi[u]);
         if (do_v) {
           st_stream(d.v + dofs[u], vlo[u]);
-          st_stream(d.v + dofs[u] + HALF, vhi[u]);
+          st_stream(d.v + dofs[u] + yoff, vhi[u]);
         }
       }
     }

@@ -121,7 +121,9 @@ extern "C" {
 
 size_t akv_scratch_bytes(const akv_cache_desc *d) {
   if (!d || d->n_seqs < 1 || d->max_blocks_per_seq < 1 || d->n_blocks < 1) return 0;
-  return akv::scratch_layout(d->n_seqs, d->max_blocks_per_seq * akv::kPage, d->n_blocks).total;
+  if (d->n_layers < 1) return 0;
+  return akv::scratch_layout(d->n_seqs, d->max_blocks_per_seq * akv::kPage, d->n_blocks,
+                             d->n_layers).total;
 }
 
 akv_status akv_cache_init(const akv_cache_desc *d, akv_cache **out) {
@@ -141,12 +143,23 @@ akv_status akv_cache_init(const akv_cache_desc *d, akv_cache **out) {
       !aligned(d->positions, 16) || !aligned(d->token_ids, 16))
     return AKV_ERR_ARG;
   if (d->scratch_bytes < akv_scratch_bytes(d)) return AKV_ERR_ARG;
+  const int rd = d->rotary_dim ? d->rotary_dim : d->head_dim;
+  if (rd < 16 || rd > d->head_dim || rd % 16) return AKV_ERR_ARG;
+  if (d->inv_freq)
+    for (int i = 0; i < rd / 2; ++i)
+      if (!isfinite(d->inv_freq[i]) || d->inv_freq[i] < 0.0) return AKV_ERR_ARG;
+  int any_window = 0;
+  if (d->layer_window)
+    for (int l = 0; l < d->n_layers; ++l) {
+      if (d->layer_window[l] < 0) return AKV_ERR_ARG;
+      any_window |= d->layer_window[l] > 0;
+    }
 
   akv_cache *c = new (std::nothrow) akv_cache();
   if (!c) return AKV_ERR_ARG;
   c->desc = *d;
   const int S = d->max_blocks_per_seq * akv::kPage;
-  c->layout = akv::scratch_layout(d->n_seqs, S, d->n_blocks);
+  c->layout = akv::scratch_layout(d->n_seqs, S, d->n_blocks, d->n_layers);
   char *sb = static_cast<char *>(d->scratch);
   Dev &v = c->dev;
   v.k = d->k_pool;
@@ -166,6 +179,9 @@ akv_status akv_cache_init(const akv_cache_desc *d, akv_cache **out) {
   v.stage = reinterpret_cast<int32_t *>(sb + c->layout.stage);
   v.chunk_info = reinterpret_cast<int32_t *>(sb + c->layout.chunk_info);
   v.fork_dst = reinterpret_cast<int32_t *>(sb + c->layout.fork_dst);
+  v.window = reinterpret_cast<const int32_t *>(sb + c->layout.window);
+  v.RD = rd;
+  v.any_window = any_window;
   v.L = d->n_layers;
   v.H = d->n_kv_heads;
   v.D = d->head_dim;
@@ -184,11 +200,16 @@ akv_status akv_cache_init(const akv_cache_desc *d, akv_cache **out) {
   c->move_grid = akv::move_blocks_per_cu(d->head_dim) * c->n_cu;
   c->attn_per_cu = akv::attn_blocks_per_cu(d->head_dim);
 
-  // theta_i = base^(-2i/d), double, uploaded once.
+  // theta_i over the rotary dims: the caller's table, else base^(-2i/r);
+  // double, uploaded once.  Per-layer windows likewise.
   double theta[akv::kMaxHalf] = {};
-  for (int i = 0; i < d->head_dim / 2; ++i)
-    theta[i] = pow(d->rope_base, -2.0 * (double)i / (double)d->head_dim);
-  if (hipMemcpy(sb + c->layout.theta, theta, sizeof(theta), hipMemcpyHostToDevice) != hipSuccess) {
+  for (int i = 0; i < rd / 2; ++i)
+    theta[i] = d->inv_freq ? d->inv_freq[i] : pow(d->rope_base, -2.0 * (double)i / (double)rd);
+  std::vector<int32_t> win(d->n_layers, 0);
+  if (d->layer_window) std::copy(d->layer_window, d->layer_window + d->n_layers, win.begin());
+  if (hipMemcpy(sb + c->layout.theta, theta, sizeof(theta), hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(sb + c->layout.window, win.data(), sizeof(int32_t) * win.size(),
+                hipMemcpyHostToDevice) != hipSuccess) {
     delete c;
     return AKV_ERR_HIP;
   }

@@ -61,8 +61,11 @@ struct Dev {
   uint16_t *k, *v;
   int32_t *table, *lens, *next_pos, *pos, *tok, *free_stack, *free_count;
   int32_t *ctl, *seq_info, *src_map, *delta_map, *stage, *chunk_info, *fork_dst;
-  const double *theta;        // [d/2]
+  const double *theta;        // [RD/2] rotation frequencies
+  const int32_t *window;      // [L] sliding-window length per layer, 0 = full attention
   int L, H, D, NB, B, maxpg, S, nchunk;   // nchunk: plan chunks per sequence
+  int RD;                     // rotary dims: the first RD of each head (multiple of 16)
+  int any_window;             // some layer has a sliding window
 };
 
 // Element strides of the K/V pools: page, kv head, layer.  One (layer, page,
@@ -82,9 +85,40 @@ __host__ __device__ inline PoolStrides pool_strides(int NB, int H, int D) {
 #endif
 }
 
+// Position of entry j of a sequence whose page-table row is trow.
+__device__ __forceinline__ int entry_pos(const Dev &d, const int32_t *trow, int j) {
+  return d.pos[(size_t)trow[j >> 4] * kPage + (j & 15)];
+}
+
+// First index j in [a, b) whose position is >= lo (b if none).  A sequence's
+// positions strictly increase with the index (append counts up, drop keeps
+// order, reposition requires increasing targets), so the test is monotone:
+// a 64-way search by the calling wave, two dependent loads per round.  Every
+// lane of the wave must call it; the result is the same in every lane.
+__device__ inline int first_pos_at_least(const Dev &d, const int32_t *trow, int a, int b,
+                                         int lo) {
+  const int lane = threadIdx.x & 63;
+  while (b - a > 64) {
+    const int step = (b - a + 63) / 64;            // probes a, a+step, ..., a+63*step >= b-1
+    const int j = a + lane * step;
+    const bool ge = j >= b || entry_pos(d, trow, j) >= lo;
+    const unsigned long long m = __ballot(ge);
+    if (m == 0ull) {
+      a += 63 * step + 1;                          // every probe is in range and below lo
+    } else {
+      const int t = __ffsll(m) - 1;                // first probe at or past the answer
+      b = min(b, a + t * step);
+      if (t) a += (t - 1) * step + 1;
+    }
+  }
+  const int j = a + lane;
+  const bool below = j < b && entry_pos(d, trow, j) < lo;
+  return a + __popcll(__ballot(below));
+}
+
 // Scratch layout (byte offsets from the scratch base, each 256-B aligned).
 struct ScratchLayout {
-  size_t ctl, theta, seq_info, src_map, delta_map, stage, chunk_info, fork_dst, total;
+  size_t ctl, theta, seq_info, src_map, delta_map, stage, chunk_info, fork_dst, window, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -93,7 +127,7 @@ constexpr int kPlanChunkPages = 256;   // pages per plan workgroup
 
 inline int plan_chunks(int maxpg) { return (maxpg + kPlanChunkPages - 1) / kPlanChunkPages; }
 
-inline ScratchLayout scratch_layout(int B, int S, int NB) {
+inline ScratchLayout scratch_layout(int B, int S, int NB, int L) {
   ScratchLayout s;
   size_t o = 0;
   s.ctl = o;       o = align256(o + CTL_COUNT * 4);
@@ -104,6 +138,7 @@ inline ScratchLayout scratch_layout(int B, int S, int NB) {
   s.stage = o;     o = align256(o + size_t(NB) * 4);
   s.chunk_info = o; o = align256(o + size_t(B) * plan_chunks(S / kPage) * 2 * 4);
   s.fork_dst = o;  o = align256(o + size_t(B) * 4);
+  s.window = o;    o = align256(o + size_t(L) * 4);
   s.total = o;
   return s;
 }

@@ -17,6 +17,7 @@
 // per wave in LDS and read transposed for the PV MFMA.
 #include "akv_internal.h"
 
+#include <limits.h>
 #include <math.h>
 
 namespace akv {
@@ -94,18 +95,33 @@ __global__ __launch_bounds__(kSegWaves * 64, 2) void segment_attn_kernel(
   const PoolStrides ps = pool_strides(d.NB, d.H, D);
   const size_t head_base = (size_t)l * ps.layer + (size_t)g * ps.head;
 
+  // Sliding window: a row at position p_i reads entries with position >=
+  // p_i - W + 1 (at most W entries up to itself).  Pages before the first
+  // row's first visible entry are skipped; the rest are masked by position.
+  const int W = (d.any_window && !bad) ? d.window[l] : 0;
+  int wlo = INT_MIN, pstart = 0;
+  if (W > 0) {
+    if (col_ok) wlo = entry_pos(d, trow, lim) - W + 1;
+    const int me0 = len - n + i0;
+    pstart = first_pos_at_least(d, trow, max(0, me0 - W + 1), me0 + 1,
+                                entry_pos(d, trow, me0) - W + 1) / kPage;
+  }
+
   bf16x8s ka[KC];
   uint4 vv[VC];
-  int p = wave;
+  int4 pp = make_int4(0, 0, 0, 0);                 // positions of this lane's 4 entries
+  int p = pstart + wave;
   if (p < P) {
     const size_t off = head_base + (size_t)trow[p] * ps.page;
 #pragma unroll
     for (int c = 0; c < KC; ++c) ka[c] = seg_load8(d.k + off + cl * D + 8 * kg + 32 * c);
 #pragma unroll
     for (int c = 0; c < VC; ++c) vv[c] = *reinterpret_cast<const uint4 *>(d.v + off + 8 * (lane + 64 * c));
+    if (W > 0) pp = *reinterpret_cast<const int4 *>(d.pos + (size_t)trow[p] * kPage + 4 * kg);
   }
   while (p < P) {
     const int pn = p + kSegWaves;
+    const int4 pcur = pp;
 #pragma unroll
     for (int c = 0; c < VC; ++c) {
       const int ci = lane + 64 * c, row = ci / C8, col = (ci % C8) * 8;
@@ -120,14 +136,17 @@ __global__ __launch_bounds__(kSegWaves * 64, 2) void segment_attn_kernel(
       for (int c = 0; c < KC; ++c) kan[c] = seg_load8(d.k + off + cl * D + 8 * kg + 32 * c);
 #pragma unroll
       for (int c = 0; c < VC; ++c) vv[c] = *reinterpret_cast<const uint4 *>(d.v + off + 8 * (lane + 64 * c));
+      if (W > 0) pp = *reinterpret_cast<const int4 *>(d.pos + (size_t)trow[pn] * kPage + 4 * kg);
     }
     floatx4s sacc = floatx4s{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < KC; ++c) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[c], qb[c], sacc, 0, 0, 0);
     const int tok0 = p * kPage + 4 * kg;
+    const int pj4[4] = {pcur.x, pcur.y, pcur.z, pcur.w};
     float sv[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sv[j] = (tok0 + j <= lim) ? sacc[j] * scale : -INFINITY;
+    for (int j = 0; j < 4; ++j)
+      sv[j] = (tok0 + j <= lim && (W == 0 || pj4[j] >= wlo)) ? sacc[j] * scale : -INFINITY;
     float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
@@ -226,6 +245,7 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void segment_fa_kernel(
   static_assert(KPT * NTH == kFaKT * C8, "K tile must split evenly");
   __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kFaKT][KROW];
   __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][D][VROW];
+  __shared__ __attribute__((aligned(16))) int32_t s_pos[2][kFaKT];   // sliding-window layers only
 
   const int G = Hq / d.H;
   const int TBW = kFaCols / G;                            // query tokens per workgroup
@@ -261,7 +281,6 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void segment_fa_kernel(
     lim[ct] = cok[ct] ? len - n + i : -1;
     qrow[ct] = ((size_t)(q0 + (rok[ct] ? i : 0)) * nL + li) * Hq + (size_t)g * G + hh;
   }
-  // last entry any valid column of this wave sees
   // last entry any valid column of this wave sees, and the first entry some
   // valid column cannot see (tiles wholly before it need no causal mask)
   int wave_lim = -1, wave_lo = -1;
@@ -274,6 +293,22 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void segment_fa_kernel(
   }
   const int last = bad ? -1 : len - n + min(i0 + TBW, n) - 1;
   const int ntile = (last + kFaKT) / kFaKT;
+  const int32_t *trow = d.table + (size_t)(bad ? 0 : seq) * d.maxpg;
+
+  // Sliding window: a row at position p_i reads the entries with position
+  // >= p_i - W + 1.  The sweep starts at the tile of the first row's first
+  // visible entry; entries are masked by position (kept in LDS per tile).
+  const int W = (d.any_window && !bad) ? d.window[l] : 0;
+  int wlo[2] = {INT_MIN, INT_MIN};
+  int t0 = 0;
+  if (W > 0) {
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+      if (cok[ct]) wlo[ct] = entry_pos(d, trow, lim[ct]) - W + 1;
+    const int me0 = len - n + i0;
+    t0 = first_pos_at_least(d, trow, max(0, me0 - W + 1), me0 + 1,
+                            entry_pos(d, trow, me0) - W + 1) / kFaKT;
+  }
 
   bf16x8s qf[2][KC];
 #pragma unroll
@@ -291,7 +326,6 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void segment_fa_kernel(
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[ct][t] = floatx4s{0.f, 0.f, 0.f, 0.f};
 
-  const int32_t *trow = d.table + (size_t)(bad ? 0 : seq) * d.maxpg;
   const PoolStrides ps = pool_strides(d.NB, d.H, D);
   const uint16_t *kb = d.k + (size_t)l * ps.layer + (size_t)g * ps.head;
   const uint16_t *vb = d.v + (size_t)l * ps.layer + (size_t)g * ps.head;
@@ -300,9 +334,10 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void segment_fa_kernel(
   // tile's K/V loads never wait on a table lookup.  Entries past the end of
   // the sequence read the last entry (always a valid address) and are zeroed
   // by value, so every load is unconditional.  Only called when len >= 1.
-  int pk[KPT], pv[VPT];
+  int pk[KPT], pv[VPT], pq = 0;
   auto pidx = [&](int t) {
     const int T0 = t * kFaKT;
+    if (W > 0 && tid < kFaKT) pq = trow[min(T0 + tid, len - 1) >> 4];
 #pragma unroll
     for (int r = 0; r < KPT; ++r) {
       const int tok = (tid + NTH * r) / C8;
@@ -316,8 +351,10 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void segment_fa_kernel(
     }
   };
   uint4 rk[KPT], rv[2 * VPT];
+  int rpos = 0;
   auto gload = [&](int t) {
     const int T0 = t * kFaKT;
+    if (W > 0 && tid < kFaKT) rpos = d.pos[(size_t)pq * kPage + (min(T0 + tid, len - 1) & 15)];
 #pragma unroll
     for (int r = 0; r < KPT; ++r) {
       const int idx = tid + NTH * r, tok = idx / C8, ch = idx - tok * C8, e = T0 + tok;
@@ -338,6 +375,7 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void segment_fa_kernel(
   // registers -> LDS; entries past the end of the sequence become zeros here
   auto lstore = [&](int t, int buf) {
     const int T0 = t * kFaKT;
+    if (W > 0 && tid < kFaKT) s_pos[buf][tid] = rpos;
 #pragma unroll
     for (int r = 0; r < KPT; ++r) {
       const int idx = tid + NTH * r, tok = idx / C8, ch = idx - tok * C8;
@@ -366,18 +404,18 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void segment_fa_kernel(
     }
   };
 
-  if (ntile > 0) {
-    pidx(0);
-    gload(0);
-    if (ntile > 1) pidx(1);
-    lstore(0, 0);
+  if (t0 < ntile) {
+    pidx(t0);
+    gload(t0);
+    if (t0 + 1 < ntile) pidx(t0 + 1);
+    lstore(t0, 0);
   }
   // Q and the first tile are in registers / LDS before the loop: no wait on
   // the loop's own prefetches inside it
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int t = 0; t < ntile; ++t) {
-    const int buf = t & 1;
+  for (int t = t0; t < ntile; ++t) {
+    const int buf = (t - t0) & 1;
     if (t + 1 < ntile) gload(t + 1);
     if (t + 2 < ntile) pidx(t + 2);
     const int T0 = t * kFaKT;
@@ -410,6 +448,16 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void segment_fa_kernel(
 #pragma unroll
             for (int j = 0; j < 4; ++j)
               if (T0 + 16 * tt + 4 * kg + j > lim[ct]) sacc[ct][tt][j] = -INFINITY;
+        }
+        if (W > 0) {
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) {
+            const int4 pe = *reinterpret_cast<const int4 *>(&s_pos[buf][16 * tt + 4 * kg]);
+            const int pj4[4] = {pe.x, pe.y, pe.z, pe.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (pj4[j] < wlo[ct]) sacc[ct][tt][j] = -INFINITY;
+          }
         }
         float mx = sacc[ct][0][0];
 #pragma unroll

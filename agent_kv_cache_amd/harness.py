@@ -41,11 +41,13 @@ def seq_chunk(shape: Shape, data_seed: int, b: int, c: int, n: int, which: str, 
 
 
 def make_cache(shape: Shape, seq_lens: Sequence[int], extra_pages: int,
-               max_blocks_per_seq: Optional[int] = None, device: str = "cuda") -> AkvCache:
+               max_blocks_per_seq: Optional[int] = None, device: str = "cuda",
+               **cache_kw) -> AkvCache:
+    """cache_kw: rotary_dim / inv_freq / layer_window, passed to AkvCache."""
     nb = sum(pages_for(n) for n in seq_lens) + int(extra_pages)
     maxpg = max_blocks_per_seq or max(1, max(pages_for(n) for n in seq_lens))
     return AkvCache(shape.n_layers, shape.n_kv_heads, shape.head_dim, max(nb, 1),
-                    len(seq_lens), maxpg, shape.rope_base, device=device)
+                    len(seq_lens), maxpg, shape.rope_base, device=device, **cache_kw)
 
 
 def fill(cache: AkvCache, shape: Shape, seq_lens: Sequence[int], data_seed: int,

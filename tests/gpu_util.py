@@ -28,14 +28,19 @@ def bits(t) -> np.ndarray:
 
 
 def oracle_for(shape: Shape, seq_lens: Sequence[int], data_seed: int, layers=None,
-               gen_device: str = "cpu", with_kv: bool = True, seqs=None) -> O.OracleCache:
+               gen_device: str = "cpu", with_kv: bool = True, seqs=None,
+               rotary_dim=None, theta=None, window=None) -> O.OracleCache:
     """Oracle holding the same seeded inputs as harness.fill (optionally only
     some layers: then the oracle's layer axis indexes `layers`; optionally
-    only some sequences: then oracle sequence i is sequence seqs[i])."""
+    only some sequences: then oracle sequence i is sequence seqs[i]).
+    rotary_dim / theta / window (per layer of the full cache) as in
+    OracleCache."""
     lay = list(range(shape.n_layers)) if layers is None else list(layers)
     sel = list(range(len(seq_lens))) if seqs is None else list(seqs)
+    win = None if window is None else [window[l] for l in lay]
     oc = O.OracleCache(len(lay), shape.n_kv_heads, shape.head_dim, shape.rope_base,
-                       n_seqs=len(sel), with_kv=with_kv)
+                       n_seqs=len(sel), with_kv=with_kv, rotary_dim=rotary_dim, theta=theta,
+                       window=win)
     for i, b in enumerate(sel):
         n = seq_lens[b]
         for c in range((int(n) + Hn.CHUNK - 1) // Hn.CHUNK):
@@ -92,10 +97,22 @@ def q_tensor(shape: Shape, B: int, n_layers: int, seed: int, device="cpu"):
     return randn_bf16((B, n_layers, shape.n_q_heads, shape.head_dim), seed, device=device)
 
 
+# The attention bar: 1e-2 absolute on the computation, plus the rounding of
+# the bf16 output itself (at most 2^-8 of the value).  The second term only
+# matters where few entries are visible and |o| approaches |v| (a bf16 value
+# in [2, 4) is already up to 2^-7 away from its fp64 reference).
+BF16_OUT = 2.0 ** -8
+
+
+def attn_error(got, ref) -> float:
+    """max over elements of |got - ref| - 2^-8 |ref| (compared with 1e-2)."""
+    return float((np.abs(got - ref) - BF16_OUT * np.abs(ref)).max())
+
+
 def check_attention(cache, oc: O.OracleCache, q, out, layers=None, active=None, tol=1e-2,
                     seqs=None):
-    """out [B][nL][Hq][d] vs the fp64 oracle; returns the max abs error.
-    Oracle sequence i is cache sequence seqs[i]."""
+    """out [B][nL][Hq][d] vs the fp64 oracle; returns the largest error in the
+    sense of attn_error.  Oracle sequence i is cache sequence seqs[i]."""
     qn = to_f64(q)
     on = to_f64(out)
     lay = list(range(q.shape[1])) if layers is None else list(layers)
@@ -105,7 +122,74 @@ def check_attention(cache, oc: O.OracleCache, q, out, layers=None, active=None, 
         n = None if active is None else int(active[b])
         ref = oc.decode_attention(i, qn[b][lay] if layers is not None else qn[b], n)
         got = on[b][lay] if layers is not None else on[b]
-        err = float(np.abs(got - ref).max()) if ref.size else 0.0
+        err = attn_error(got, ref) if ref.size else 0.0
         worst = max(worst, err)
+    assert worst <= tol, worst
+    return worst
+
+
+def append_seeded(cache, oc, sh, per_seq, seed, tid_base):
+    """Append per_seq[b] seeded tokens to every sequence b, on both sides."""
+    B = cache.B
+    N = int(sum(per_seq))
+    if N == 0:
+        return
+    k = randn_bf16((sh.n_layers, N, sh.n_kv_heads, sh.head_dim), seed)
+    v = randn_bf16((sh.n_layers, N, sh.n_kv_heads, sh.head_dim), seed + 1)
+    tid = np.arange(N, dtype=np.int64) + tid_base
+    import torch
+    cache.append(torch.tensor(per_seq, dtype=torch.int32, device=cache.device), N,
+                 k.to(cache.device), v.to(cache.device),
+                 torch.tensor(tid, dtype=torch.int32, device=cache.device))
+    o = 0
+    for b in range(B):
+        sl = slice(o, o + per_seq[b])
+        if per_seq[b]:
+            oc.append(b, tid[sl], to_f64(k[:, sl].permute(1, 0, 2, 3)),
+                      to_f64(v[:, sl].permute(1, 0, 2, 3)))
+        o += per_seq[b]
+
+
+def snapshot(cache, b):
+    tok, pos, _ = cache.seq_state(b)
+    ks = [bits(cache.gather_rows(b, l, "k")) for l in range(cache.L)]
+    vs = [bits(cache.gather_rows(b, l, "v")) for l in range(cache.L)]
+    return tok, pos, int(cache.next_pos[b]), ks, vs
+
+
+def same_state(a, b):
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and a[2] == b[2]
+    for x, y in zip(a[3] + a[4], b[3] + b[4]):
+        assert np.array_equal(x, y)
+
+
+def run_segments(cache, q, segs, max_q=None, layer_begin=0, n_layers=None):
+    """segs: list of (sequence, row count); q rows are laid out segment by segment."""
+    import torch
+    dev = cache.device
+    seq = torch.tensor([s for s, _ in segs], dtype=torch.int32, device=dev)
+    off = torch.tensor(np.concatenate([[0], np.cumsum([n for _, n in segs])]).astype(np.int32),
+                       device=dev)
+    out = torch.full_like(q, float("nan"))
+    mq = max([n for _, n in segs] + [1]) if max_q is None else max_q
+    cache.segment_attention(q, seq, off, mq, out, layer_begin=layer_begin, n_layers=n_layers)
+    return out
+
+
+def check_segments(oc, q, out, segs, oracle_seq=None, tol=1e-2):
+    qn, on = to_f64(q), to_f64(out)
+    o = 0
+    worst = 0.0
+    pairs = []
+    for s, n in segs:
+        pairs.append(((s if oracle_seq is None else oracle_seq[s]), qn[o:o + n]))
+        o += n
+    refs = O.segment_attention(oc, pairs)
+    o = 0
+    for (s, n), ref in zip(segs, refs):
+        got = on[o:o + n]
+        if n:
+            worst = max(worst, attn_error(got, ref))
+        o += n
     assert worst <= tol, worst
     return worst

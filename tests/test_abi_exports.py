@@ -57,6 +57,32 @@ def test_init_rejects_bad_descriptors(field, value):
     assert not h.value
 
 
+@pytest.mark.parametrize("rotary_dim,freq,window", [
+    (8, None, None),                      # not a multiple of 16
+    (24, None, None),
+    (144, None, None),                    # wider than the head
+    (-16, None, None),
+    (64, [1.0] * 31 + [float("nan")], None),
+    (64, [1.0] * 31 + [-1.0], None),
+    (0, None, [0, -1]),                   # negative window
+])
+def test_init_rejects_bad_rope_variants(rotary_dim, freq, window):
+    import numpy as np
+    d = _desc(rotary_dim=rotary_dim)
+    keep = []
+    if freq is not None:
+        a = np.asarray(freq, dtype=np.float64)
+        keep.append(a)
+        d.inv_freq = a.ctypes.data
+    if window is not None:
+        a = np.asarray(window, dtype=np.int32)
+        keep.append(a)
+        d.layer_window = a.ctypes.data
+    h = C.c_void_p()
+    assert B.lib().akv_cache_init(C.byref(d), C.byref(h)) == 1
+    assert not h.value
+
+
 def test_null_handle_calls_are_rejected():
     L = B.lib()
     assert L.akv_drop(None, None, None) == 1
@@ -64,6 +90,8 @@ def test_null_handle_calls_are_rejected():
     assert L.akv_reposition(None, None, None, None) == 1
     assert L.akv_append(None, None, 0, None, None, None, None) == 1
     assert L.akv_decode_attention(None, None, None, 0, 1, 1, None, None, 0, None) == 1
+    assert L.akv_fork(None, None, None, 0, None, None) == 1
+    assert L.akv_segment_attention(None, None, None, None, 1, 1, 0, 1, 1, None, None) == 1
     assert L.akv_sync_status(None, None) == 1
     assert L.akv_profile_enable(None, 1) == 1
     assert L.akv_decode_workspace_bytes(None, 1, 1) == 0

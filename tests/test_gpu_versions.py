@@ -18,7 +18,9 @@ from agent_kv_cache_amd import workloads as W  # noqa: E402
 from agent_kv_cache_amd.binding import AkvError  # noqa: E402
 from oracle import akv_oracle as O  # noqa: E402
 
-from gpu_util import bits, check_kv, check_meta, oracle_for, say, to_f64  # noqa: E402
+from gpu_util import (bits, check_kv, check_meta, oracle_for, say, to_f64,  # noqa: E402
+                      append_seeded as _append, check_segments as _check_segments,
+                      run_segments as _segments, snapshot as _snapshot, same_state as _same)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -27,71 +29,6 @@ def _gpu():
         pytest.skip("no GPU")
     from agent_kv_cache_amd.binding import lib
     lib()
-
-
-def _append(cache, oc, sh, per_seq, seed, tid_base):
-    """Append per_seq[b] seeded tokens to every sequence b, on both sides."""
-    B = cache.B
-    N = int(sum(per_seq))
-    if N == 0:
-        return
-    k = W.randn_bf16((sh.n_layers, N, sh.n_kv_heads, sh.head_dim), seed)
-    v = W.randn_bf16((sh.n_layers, N, sh.n_kv_heads, sh.head_dim), seed + 1)
-    tid = np.arange(N, dtype=np.int64) + tid_base
-    cache.append(torch.tensor(per_seq, dtype=torch.int32, device=cache.device), N,
-                 k.to(cache.device), v.to(cache.device),
-                 torch.tensor(tid, dtype=torch.int32, device=cache.device))
-    o = 0
-    for b in range(B):
-        sl = slice(o, o + per_seq[b])
-        if per_seq[b]:
-            oc.append(b, tid[sl], to_f64(k[:, sl].permute(1, 0, 2, 3)),
-                      to_f64(v[:, sl].permute(1, 0, 2, 3)))
-        o += per_seq[b]
-
-
-def _snapshot(cache, b):
-    tok, pos, _ = cache.seq_state(b)
-    ks = [bits(cache.gather_rows(b, l, "k")) for l in range(cache.L)]
-    vs = [bits(cache.gather_rows(b, l, "v")) for l in range(cache.L)]
-    return tok, pos, int(cache.next_pos[b]), ks, vs
-
-
-def _same(a, b):
-    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and a[2] == b[2]
-    for x, y in zip(a[3] + a[4], b[3] + b[4]):
-        assert np.array_equal(x, y)
-
-
-def _segments(cache, q, segs, max_q=None, layer_begin=0, n_layers=None):
-    """segs: list of (sequence, row count); q rows are laid out segment by segment."""
-    dev = cache.device
-    seq = torch.tensor([s for s, _ in segs], dtype=torch.int32, device=dev)
-    off = torch.tensor(np.concatenate([[0], np.cumsum([n for _, n in segs])]).astype(np.int32),
-                       device=dev)
-    out = torch.full_like(q, float("nan"))
-    mq = max([n for _, n in segs] + [1]) if max_q is None else max_q
-    cache.segment_attention(q, seq, off, mq, out, layer_begin=layer_begin, n_layers=n_layers)
-    return out
-
-
-def _check_segments(oc, q, out, segs, oracle_seq=None, tol=1e-2):
-    qn, on = to_f64(q), to_f64(out)
-    o = 0
-    worst = 0.0
-    pairs = []
-    for s, n in segs:
-        pairs.append(((s if oracle_seq is None else oracle_seq[s]), qn[o:o + n]))
-        o += n
-    refs = O.segment_attention(oc, pairs)
-    o = 0
-    for (s, n), ref in zip(segs, refs):
-        got = on[o:o + n]
-        if n:
-            worst = max(worst, float(np.abs(got - ref).max()))
-        o += n
-    assert worst <= tol, worst
-    return worst
 
 
 # ---------------------------------------------------------------------------
