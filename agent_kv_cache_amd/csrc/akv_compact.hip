@@ -49,20 +49,21 @@ constexpr int kMoveThreads = 256;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Streaming 16-B accesses: every KV byte of a move is read once and written
-// once, so they bypass cache retention (nontemporal hint).
+// once, so they bypass cache retention (nontemporal hint) -- when each load
+// instruction covers whole 128-B lines.  With partial RoPE a row's x and y
+// chunks are two 64-B pieces per instruction; the other half of each line is
+// touched by the next instruction, and with the hint it is fetched again, so
+// those moves use ordinary cached accesses (measured 1.05 -> 0.89 ms on the
+// Llama-8B-shaped drop with r = 64).
+template <bool NT>
 __device__ __forceinline__ u32x4 ld_stream(const uint16_t *p) {
-#if AKV_MOVE_NT
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-#else
-  return *reinterpret_cast<const u32x4 *>(p);
-#endif
+  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  else return *reinterpret_cast<const u32x4 *>(p);
 }
+template <bool NT>
 __device__ __forceinline__ void st_stream(uint16_t *p, u32x4 v) {
-#if AKV_MOVE_NT
-  __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
-#else
-  *reinterpret_cast<u32x4 *>(p) = v;
-#endif
+  if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
+  else *reinterpret_cast<u32x4 *>(p) = v;
 }
 
 // ---------------------------------------------------------------------------
@@ -412,7 +413,7 @@ __device__ __forceinline__ void rotate8(u32x4 &lo, u32x4 &hi, const double2 *cs)
 // the same number of (layer, page) slices whatever the page count, and the
 // per-page set-up (row sources, deltas, cos/sin) is done once per page it
 // touches.
-template <int D>
+template <int D, bool NT>
 __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(Dev d, int mode) {
   constexpr int HALF = D / 2;
   constexpr int CH = D / 16;             // 16-B chunks per half row
@@ -554,16 +555,16 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
           dofs[u] = dst_row + off;
           lo[u] = hi[u] = u32x4{0u, 0u, 0u, 0u};
           if (on[u] && valid) {
-            lo[u] = ld_stream(pool + src_row + off);
-            hi[u] = ld_stream(pool + src_row + off + yoff);
+            lo[u] = ld_stream<NT>(pool + src_row + off);
+            hi[u] = ld_stream<NT>(pool + src_row + off + yoff);
           }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           if (!on[u]) continue;
           if (rot_plane) rotate8(lo[u], hi[u], cs_row);
-          st_stream(pool + dofs[u], lo[u]);
-          st_stream(pool + dofs[u] + yoff, hi[u]);
+          st_stream<NT>(pool + dofs[u], lo[u]);
+          st_stream<NT>(pool + dofs[u] + yoff, hi[u]);
         }
       }
     }
@@ -588,11 +589,11 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
         klo[u] = khi[u] = vlo[u] = vhi[u] = u32x4{0u, 0u, 0u, 0u};
         if (on[u] && valid) {
           const size_t so = src_row + off;
-          klo[u] = ld_stream(d.k + so);
-          khi[u] = ld_stream(d.k + so + yoff);
+          klo[u] = ld_stream<NT>(d.k + so);
+          khi[u] = ld_stream<NT>(d.k + so + yoff);
           if (do_v) {
-            vlo[u] = ld_stream(d.v + so);
-            vhi[u] = ld_stream(d.v + so + yoff);
+            vlo[u] = ld_stream<NT>(d.v + so);
+            vhi[u] = ld_stream<NT>(d.v + so + yoff);
           }
         }
       }
@@ -600,11 +601,11 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
       for (int u = 0; u < U; ++u) {
         if (!on[u]) continue;
         if (turn) rotate8(klo[u], khi[u], cs_row);
-        st_stream(d.k + dofs[u], klo[u]);
-        st_stream(d.k + dofs[u] + yoff, khi[u]);
+        st_stream<NT>(d.k + dofs[u], klo[u]);
+        st_stream<NT>(d.k + dofs[u] + yoff, khi[u]);
         if (do_v) {
-          st_stream(d.v + dofs[u], vlo[u]);
-          st_stream(d.v + dofs[u] + yoff, vhi[u]);
+          st_stream<NT>(d.v + dofs[u], vlo[u]);
+          st_stream<NT>(d.v + dofs[u] + yoff, vhi[u]);
         }
       }
     }
@@ -796,18 +797,23 @@ hipError_t launch_plan(const Dev &d, const uint8_t *mask, const int32_t *new_pos
 }
 
 hipError_t launch_move(const Dev &d, int mode, int grid, hipStream_t st) {
-  if (d.D == 128)
-    hipLaunchKernelGGL(move_kernel<128>, dim3(grid), dim3(kMoveThreads), 0, st, d, mode);
-  else
-    hipLaunchKernelGGL(move_kernel<64>, dim3(grid), dim3(kMoveThreads), 0, st, d, mode);
+  const bool nt = AKV_MOVE_NT && d.RD == d.D;
+  const dim3 g(grid), b(kMoveThreads);
+  if (d.D == 128) {
+    if (nt) hipLaunchKernelGGL((move_kernel<128, true>), g, b, 0, st, d, mode);
+    else hipLaunchKernelGGL((move_kernel<128, false>), g, b, 0, st, d, mode);
+  } else {
+    if (nt) hipLaunchKernelGGL((move_kernel<64, true>), g, b, 0, st, d, mode);
+    else hipLaunchKernelGGL((move_kernel<64, false>), g, b, 0, st, d, mode);
+  }
   return hipGetLastError();
 }
 
 int move_blocks_per_cu(int D) {
   int n = 0;
   const hipError_t e = (D == 128)
-      ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, move_kernel<128>, kMoveThreads, 0)
-      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, move_kernel<64>, kMoveThreads, 0);
+      ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, move_kernel<128, true>, kMoveThreads, 0)
+      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, move_kernel<64, true>, kMoveThreads, 0);
   return (e == hipSuccess && n > 0) ? n : 2;
 }
 

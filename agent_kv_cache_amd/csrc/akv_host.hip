@@ -20,6 +20,7 @@ struct akv_cache {
   int n_cu = 256;
   int move_grid = 2048;
   int attn_per_cu = 2;
+  int n_full_layers = 0;   // layers without a sliding window
   bool profile = false;
   struct Rec {
     int kernel;
@@ -79,7 +80,14 @@ bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 // workgroups is fullest (ties: fewer splits, less combine work).  Each split's
 // page range is then cut on the device from the actual length.
 int nsplit_for(const akv_cache *c, int nL) {
-  const long long rows = (long long)c->desc.n_seqs * nL * c->desc.n_kv_heads;
+  // Rows that carry the work: with sliding-window layers the full-attention
+  // layers dominate (a window row reads at most W entries), so the split
+  // count is sized for their share of the layers.
+  long long lay = nL;
+  if (c->n_full_layers < c->desc.n_layers && c->n_full_layers > 0)
+    lay = std::max(1LL, ((long long)nL * c->n_full_layers + c->desc.n_layers - 1) /
+                            c->desc.n_layers);
+  const long long rows = (long long)c->desc.n_seqs * lay * c->desc.n_kv_heads;
   const long long cap = (long long)c->attn_per_cu * c->n_cu;
   const long long max_ns = std::max(1, c->desc.max_blocks_per_seq / 4);
   const long long ns_min = std::min(max_ns, std::max(1LL, (cap + rows - 1) / rows));
@@ -182,6 +190,9 @@ akv_status akv_cache_init(const akv_cache_desc *d, akv_cache **out) {
   v.window = reinterpret_cast<const int32_t *>(sb + c->layout.window);
   v.RD = rd;
   v.any_window = any_window;
+  c->n_full_layers = d->n_layers;
+  if (d->layer_window)
+    for (int l = 0; l < d->n_layers; ++l) c->n_full_layers -= d->layer_window[l] > 0;
   v.L = d->n_layers;
   v.H = d->n_kv_heads;
   v.D = d->head_dim;

@@ -31,33 +31,70 @@ PEAK_HBM_GBPS = 8000.0
 METRIC = "KV GB/s for drop+reposition and decode attention; % of HBM peak, 1 GPU"
 
 
-def algorithmic_bytes(shape, seq_lens, masks):
+def algorithmic_bytes(shape, seq_lens, masks, layer_window=None):
     """Bytes the method must move, for caches whose positions are 0..n-1.
 
     drop+reposition: survivors whose slot changes (at or after the first
     dropped entry) read and write K and V once; survivors whose position
     changes in place read and write K (none for canonical input positions);
     plus the mask bytes, the positions read for every survivor and the
-    positions and token ids moved with the moved rows.
-    decode: K and V of every survivor once, q in and out, the page ids.
+    positions and token ids moved with the moved rows.  Partial RoPE moves
+    the same bytes (the unrotated part of K is copied).
+    decode: K and V of every entry the query sees once, q in and out, the
+    page ids.  After the canonical reposition a sliding window of W reads
+    the last W - 1 survivors of its layer.
     """
     L, H, D = shape.n_layers, shape.n_kv_heads, shape.head_dim
-    row = L * H * D * 2                      # one token's K (or V), all layers
-    moved = surv = total = pages = 0
+    lrow = H * D * 2                         # one token's K (or V), one layer
+    row = L * lrow                           # all layers
+    win = [0] * L if layer_window is None else list(layer_window)
+    moved = surv = total = pages = seen = 0
     for n, m in zip(seq_lens, masks):
         m = np.asarray(m[:n]).astype(bool)
         r = n - int(m.sum())
         surv += r
         total += n
         pages += (r + 15) // 16
+        seen += sum(min(r, w - 1) if w else r for w in win)
         if m.any():
             f = int(np.flatnonzero(m)[0])
             moved += r - f
     b_move = moved * (2 * row) * 2 + moved * 12
     b_dr = b_move + total + 4 * surv
-    b_att = surv * 2 * row + 2 * (len(seq_lens) * L * shape.n_q_heads * D * 2) + 4 * pages
+    b_att = seen * 2 * lrow + 2 * (len(seq_lens) * L * shape.n_q_heads * D * 2) + 4 * pages
     return dict(moved=moved, survivors=surv, tokens=total, b_move=b_move, b_dr=b_dr,
-                b_att=b_att, b_att_kv=surv * 2 * row)
+                b_att=b_att, b_att_kv=seen * 2 * lrow)
+
+
+def rope_options(args, shape):
+    """Cache options for the RoPE-variant runs (partial RoPE, a frequency
+    table, alternating sliding-window layers), as AkvCache keywords."""
+    kw = {}
+    r = args.rotary_dim or shape.head_dim
+    if args.rotary_dim:
+        kw["rotary_dim"] = args.rotary_dim
+    if args.freq != "base":
+        # the published schedules, written out here for the benchmark only
+        # (same definitions as the test oracle's llama3_theta / yarn_theta)
+        i = np.arange(r // 2, dtype=np.float64)
+        th = np.power(shape.rope_base, -2.0 * i / r)
+        if args.freq == "llama3":
+            C, f, lo, hi = 8192.0, 8.0, 1.0, 4.0
+            w = 2 * np.pi / th
+            sm = (C / w - lo) / (hi - lo)
+            th = np.where(w < C / hi, th, np.where(w > C / lo, th / f,
+                                                  (1 - sm) * th / f + sm * th))
+        else:
+            C, f = 4096.0, 32.0
+            at = lambda t: r * np.log(C / (t * 2 * np.pi)) / (2 * np.log(shape.rope_base))
+            a, b = max(int(np.floor(at(32.0))), 0), min(int(np.ceil(at(1.0))), r - 1)
+            ramp = np.clip((i - a) / max(b - a, 1e-3), 0.0, 1.0)
+            th = th * (1 - ramp) + th / f * ramp
+        kw["inv_freq"] = th
+    if args.window:
+        kw["layer_window"] = [args.window if l % args.window_every != args.window_every - 1
+                              else 0 for l in range(shape.n_layers)]
+    return kw
 
 
 def cpu_baseline(wl, layer_stride: int, time_budget_s: float = 25.0):
@@ -407,6 +444,14 @@ def main():
                     choices=["c1", "c2", "c3", "c4", "c5", "restore"])
     ap.add_argument("--cpu-rows", type=int, default=256,
                     help="restore: rows per segment in the oracle sample")
+    ap.add_argument("--rotary-dim", type=int, default=0,
+                    help="partial RoPE: rotate only the first R dims of each head")
+    ap.add_argument("--freq", default="base", choices=["base", "llama3", "yarn"],
+                    help="RoPE frequency schedule (Llama 3.1 or YaRN tables)")
+    ap.add_argument("--window", type=int, default=0,
+                    help="sliding-window length for decode in all but every "
+                         "--window-every-th layer")
+    ap.add_argument("--window-every", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured once in a HIP graph and replayed "
@@ -443,7 +488,8 @@ def main():
     wl = W.WORKLOADS[args.workload]()
     sh = wl.shape
     extra = sum(Hn.moved_pages(n, m) for n, m in zip(wl.seq_lens, wl.masks)) + 8
-    cache = Hn.make_cache(sh, wl.seq_lens, extra)
+    ropt = rope_options(args, sh)
+    cache = Hn.make_cache(sh, wl.seq_lens, extra, **ropt)
     cache.reset(None if wl.block_order is None else
                 np.concatenate([wl.block_order, np.arange(len(wl.block_order), cache.NB,
                                                           dtype=np.int32)]))
@@ -483,7 +529,7 @@ def main():
         raise RuntimeError(f"device status {st}")
     kt = {k: cache.profile_read(k) for k in ("plan", "move", "commit", "attn", "combine")}
 
-    ab = algorithmic_bytes(sh, wl.seq_lens, wl.masks)
+    ab = algorithmic_bytes(sh, wl.seq_lens, wl.masks, ropt.get("layer_window"))
     ms_step = (t1 - t0) * 1e3 / args.steps
     value = (ab["b_dr"] + ab["b_att"]) / (ms_step * 1e-3) / 1e9
 
@@ -530,6 +576,9 @@ def main():
             "q_heads": sh.n_q_heads, "rope_base": sh.rope_base, "page_tokens": 16,
             "sequences": wl.n_seqs, "tokens": ab["tokens"], "survivors": ab["survivors"],
             "moved_tokens": ab["moved"], "parallelism": "single GPU",
+            **({"rotary_dim": args.rotary_dim} if args.rotary_dim else {}),
+            **({"rope_freq": args.freq} if args.freq != "base" else {}),
+            **({"layer_window": ropt["layer_window"]} if args.window else {}),
         },
         "roofline": {
             "bound": "hbm",
@@ -579,7 +628,7 @@ def main():
         gms = (tg1 - tg0) * 1e3 / args.steps
         res["graph_ms_per_step"] = round(gms, 4)
         res["graph_value"] = round((ab["b_dr"] + ab["b_att"]) / (gms * 1e-3) / 1e9, 2)
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not ropt:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_layer_stride)
     print(json.dumps(res), flush=True)
 
