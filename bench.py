@@ -231,6 +231,23 @@ def run_history(args):
     }
 
 
+def counted_traffic(name):
+    """HBM bytes per launch from a committed rocprofv3 counter record under
+    profiles/ (FETCH_SIZE and WRITE_SIZE scaled by what they read for a
+    plain copy of known size), used only while the kernel source is
+    unchanged since the counters were taken; else None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    pj = json.load(open(path))
+    src = os.path.join(ROOT, pj.get("source_file", ""))
+    if os.path.exists(src) and hashlib.sha256(open(src, "rb").read()).hexdigest() == \
+            pj.get("source_sha256"):
+        return pj.get("hbm_bytes_per_launch")
+    return None
+
+
 def restore_counts(rs):
     """Per-version survivors, rows, attention flops and fork bytes."""
     sh = rs.shape
@@ -371,6 +388,7 @@ def run_restore(args):
     move_b = sum(c["len"] * 2 * (sh.n_layers * sh.n_kv_heads * sh.head_dim * 2) * 2 for c in cnt)
     seg_tf = flops / (seg_ms * 1e-3) / 1e12
     peak_tf = 2500.0
+    traffic = counted_traffic("segment_fa_kernel_restore_c2_counters.json")
     res = {
         "metric": "restore: segment-batch attention TFLOP/s (bf16 MFMA) and fork GB/s, 1 GPU",
         "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
@@ -389,7 +407,7 @@ def run_restore(args):
         "roofline": {
             "bound": "mfma", "kernel": "segment_fa_kernel",
             "achieved": round(seg_tf, 1), "peak": peak_tf, "unit": "TFLOP/s",
-            "frac": round(seg_tf / peak_tf, 4), "traffic": None,
+            "frac": round(seg_tf / peak_tf, 4), "traffic": traffic,
         },
         "parts": {
             "segment_attention": {"flops": flops, "ms": round(seg_ms, 4),
@@ -547,15 +565,7 @@ def main():
     # kernel and workload (FETCH_SIZE and WRITE_SIZE scaled by what they read
     # for a plain copy of known size), used only while the kernel source is
     # unchanged since the counters were taken.
-    traffic = None
-    prof_json = os.path.join(ROOT, "profiles", f"{dom}_kernel_{wl.name}_counters.json")
-    if os.path.exists(prof_json):
-        import hashlib
-        pj = json.load(open(prof_json))
-        src = os.path.join(ROOT, pj.get("source_file", ""))
-        if os.path.exists(src) and hashlib.sha256(open(src, "rb").read()).hexdigest() == \
-                pj.get("source_sha256"):
-            traffic = pj.get("hbm_bytes_per_launch")
+    traffic = counted_traffic(f"{dom}_kernel_{wl.name}_counters.json") if not ropt else None
 
     res = {
         "metric": METRIC,
