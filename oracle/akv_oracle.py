@@ -22,7 +22,10 @@ Sources (cited by page title and section, never by line):
 What is computed (every function below is the plain definition):
 
 * append (eq. 3):  new entries are concatenated after the active ones and
-  take positions next_pos, next_pos+1, ...; next_pos advances.
+  take positions next_pos, next_pos+1, ...; next_pos advances.  The model
+  rotates the new keys at those positions; append_rotated does that step
+  here (one fp64 rotation, one rounding).  release empties a sequence and
+  resets its next position (a request ends; its pages return to the pool).
 * drop (eq. 4):    an order-preserving removal of the active entries named by
   an index set.  Survivors keep their order, K, V, positions and token id;
   next_pos is NOT lowered.
@@ -335,6 +338,25 @@ class OracleCache:
                 raise ValueError(f"append: K/V shape must be {want}")
             s.k = np.concatenate([s.k, k])
             s.v = np.concatenate([s.v, v])
+
+    def append_rotated(self, b: int, token_ids, k_raw, v) -> None:
+        """Append with the model's RoPE applied here (the rotation step of
+        eq. 3 fused into the append): entry j takes position p_j = next_pos + j
+        and key bf16(R(p_j) k_raw_j) -- one fp64 rotation by p_j * theta_i,
+        rounded once; V is stored as given.  k_raw: [n, L, H, d] bf16 values.
+        """
+        s = self.seqs[b]
+        k_raw = np.asarray(k_raw, dtype=np.float64)
+        n = k_raw.shape[0]
+        pos = (s.next_pos + np.arange(n, dtype=np.int64)).reshape((n,) + (1,) * (k_raw.ndim - 2))
+        self.append(b, token_ids, bf16_round(rotate_pairs(k_raw, pos, self.theta)), v)
+
+    def release(self, b: int) -> None:
+        """End of a request: the sequence becomes empty and its next position
+        returns to 0 (its pages go back to the free pool)."""
+        shape = (0, self.n_layers, self.n_kv_heads, self.head_dim)
+        self.seqs[b] = SeqState(k=np.zeros(shape) if self.with_kv else None,
+                                v=np.zeros(shape) if self.with_kv else None)
 
     # -- eq. (4): drop ----------------------------------------------------
     def drop(self, b: int, mask) -> np.ndarray:

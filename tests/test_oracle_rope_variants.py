@@ -275,3 +275,74 @@ def test_planted_mistakes_in_variants_are_caught(monkeypatch):
     monkeypatch.setattr(O, "llama3_theta", lambda th, f, lo, hi, C: orig3(th, f, hi, lo, C))
     with pytest.raises(AssertionError):
         test_llama3_rule_bands_closed_form()
+
+
+# ---------------------------------------------------------------------------
+# append with the RoPE rotation fused in, release
+# ---------------------------------------------------------------------------
+def test_append_rotated_unit_vectors_and_position_zero():
+    d, r = 16, 8
+    c = O.OracleCache(1, 1, d, 1e4, rotary_dim=r)
+    e = np.eye(d)
+    k_raw = np.stack([e[0], e[4], e[1], e[12]])[:, None, None, :]      # 4 tokens at 0..3
+    c.append_rotated(0, np.arange(4), k_raw, k_raw)
+    k = c.seqs[0].k[:, 0, 0]
+    assert _bits_equal(k[0], e[0])                          # position 0: unchanged
+    # e_4 at position 1: pair 0 turns by 1 rad -> (-sin 1, cos 1) at dims 0, 4
+    assert k[1, 0] == O.bf16_round(np.array(-math.sin(1.0)))[()]
+    assert k[1, 4] == O.bf16_round(np.array(math.cos(1.0)))[()]
+    # e_1 at position 2: pair 1 (theta = 0.1) turns by 0.2
+    assert k[2, 1] == O.bf16_round(np.array(math.cos(0.2)))[()]
+    assert k[2, 5] == O.bf16_round(np.array(math.sin(0.2)))[()]
+    assert _bits_equal(k[3, r:], e[12, r:])                  # tail copied at position 3
+    assert c.seqs[0].next_pos == 4 and list(c.seqs[0].pos) == [0, 1, 2, 3]
+
+
+def test_append_rotated_commutes_with_reposition():
+    """Keys appended at positions s.. equal keys appended at 0.. and then
+    moved by s (two roundings against one: within 2^-7 of the pair norm)."""
+    rng = np.random.default_rng(8)
+    d, s_shift = 64, 777
+    k_raw = O.bf16_round(rng.standard_normal((20, 2, 2, d)))
+    v = O.bf16_round(rng.standard_normal((20, 2, 2, d)))
+    a = O.OracleCache(2, 2, d, 1.5e5)
+    a.append_rotated(0, np.arange(20), k_raw, v)
+    a.reposition(0, np.arange(20) + s_shift)
+    b = O.OracleCache(2, 2, d, 1.5e5)
+    b.append(0, [10 ** 6], np.zeros((1, 2, 2, d)), np.zeros((1, 2, 2, d)))
+    b.seqs[0].next_pos = s_shift                            # as after dropping earlier tokens
+    b.drop(0, [1])
+    b.append_rotated(0, np.arange(20), k_raw, v)
+    assert list(b.seqs[0].pos) == list(a.seqs[0].pos)
+    half = d // 2
+    norm = np.sqrt(k_raw[..., :half] ** 2 + k_raw[..., half:] ** 2)
+    bound = 2.0 ** -7 * np.concatenate([norm, norm], axis=-1) + 1e-30
+    assert np.all(np.abs(a.seqs[0].k - b.seqs[0].k) <= bound)
+    assert _bits_equal(a.seqs[0].v, b.seqs[0].v)
+
+
+def test_release_empties_and_resets_positions():
+    rng = np.random.default_rng(9)
+    c = O.OracleCache(1, 1, 16, 1e4, n_seqs=2)
+    for b in range(2):
+        k = O.bf16_round(rng.standard_normal((5, 1, 1, 16)))
+        c.append_rotated(b, np.arange(5), k, k)
+    c.release(0)
+    assert len(c.seqs[0]) == 0 and c.seqs[0].next_pos == 0
+    assert len(c.seqs[1]) == 5 and c.seqs[1].next_pos == 5
+    k = O.bf16_round(rng.standard_normal((2, 1, 1, 16)))
+    c.append_rotated(0, [7, 8], k, k)
+    assert list(c.seqs[0].pos) == [0, 1] and _bits_equal(c.seqs[0].k[0], k[0])
+
+
+def test_planted_mistakes_in_append_rotated_are_caught(monkeypatch):
+    orig = O.OracleCache.append_rotated
+
+    def off_by_one(self, b, token_ids, k_raw, v):
+        self.seqs[b].next_pos += 1
+        orig(self, b, token_ids, k_raw, v)
+        self.seqs[b].next_pos -= 1
+        self.seqs[b].pos = self.seqs[b].pos - 1
+    monkeypatch.setattr(O.OracleCache, "append_rotated", off_by_one)
+    with pytest.raises(AssertionError):
+        test_append_rotated_unit_vectors_and_position_zero()
