@@ -20,7 +20,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 STATUS = {0: "AKV_OK", 1: "AKV_ERR_ARG", 2: "AKV_ERR_ORDER", 3: "AKV_ERR_POS_MISMATCH",
           4: "AKV_ERR_NO_BLOCKS", 5: "AKV_ERR_CAPACITY", 6: "AKV_ERR_HIP"}
 KERNELS = {"plan": 0, "move": 1, "commit": 2, "attn": 3, "combine": 4, "append": 5,
-           "segment": 6}
+           "segment": 6, "release": 7}
 PAGE = 16
 
 
@@ -62,6 +62,8 @@ def lib() -> C.CDLL:
         "akv_cache_free": (None, [_P]),
         "akv_cache_reset": (C.c_int, [_P, _P, _P]),
         "akv_append": (C.c_int, [_P, _P, C.c_int64, _P, _P, _P, _P]),
+        "akv_append_rope": (C.c_int, [_P, _P, C.c_int64, _P, _P, _P, _P]),
+        "akv_release": (C.c_int, [_P, _P, _P]),
         "akv_drop": (C.c_int, [_P, _P, _P]),
         "akv_reposition": (C.c_int, [_P, _P, _P, _P]),
         "akv_drop_reposition": (C.c_int, [_P, _P, _P, _P]),
@@ -207,6 +209,19 @@ class AkvCache:
     def append(self, counts, n_new: int, k_new=None, v_new=None, token_ids=None, stream=None):
         _check(lib().akv_append(self.handle, _ptr(counts), int(n_new), _ptr(k_new), _ptr(v_new),
                                 _ptr(token_ids), _stream(stream)), "akv_append")
+
+    def append_rope(self, counts, n_new: int, k_raw=None, v_new=None, token_ids=None,
+                    stream=None):
+        """akv_append with the keys given before RoPE (rotated at their new
+        positions inside the append)."""
+        _check(lib().akv_append_rope(self.handle, _ptr(counts), int(n_new), _ptr(k_raw),
+                                     _ptr(v_new), _ptr(token_ids), _stream(stream)),
+               "akv_append_rope")
+
+    def release(self, release_mask, stream=None):
+        """Free the flagged sequences (uint8 device [B]): pages back to the
+        free stack, length and next position 0."""
+        _check(lib().akv_release(self.handle, _ptr(release_mask), _stream(stream)), "akv_release")
 
     def drop(self, drop_mask, stream=None):
         _check(lib().akv_drop(self.handle, _ptr(drop_mask), _stream(stream)), "akv_drop")

@@ -724,14 +724,19 @@ __global__ __launch_bounds__(kPlanThreads) void append_plan_kernel(Dev d, const 
 }
 
 // One workgroup per new token: copies its K/V rows of every (layer, head)
-// with 16-B accesses and writes its position and token id.
-template <int D>
+// with 16-B accesses and writes its position and token id.  With ROPE the
+// keys arrive unrotated and are turned to the token's position p on the way
+// (the model's RoPE step fused into the append): cos/sin of p * theta_i in
+// fp64 once per token in LDS, each rotary chunk pair rotated in fp64 and
+// rounded once, the non-rotary tail copied.
+template <int D, bool ROPE>
 __global__ __launch_bounds__(256) void append_copy_kernel(Dev d, int64_t n_new,
                                                           const uint16_t *__restrict__ k_new,
                                                           const uint16_t *__restrict__ v_new,
                                                           const int32_t *__restrict__ tok_new) {
   if (d.ctl[CTL_OP_OK] == 0) return;
-  __shared__ int s_page, s_row;
+  __shared__ int s_page, s_row, s_pos;
+  __shared__ double2 s_cs[ROPE ? kMaxHalf : 1];
   const int64_t tk = blockIdx.x;
   if (threadIdx.x == 0) {
     int lo = 0, hi = d.B - 1;
@@ -746,22 +751,83 @@ __global__ __launch_bounds__(256) void append_copy_kernel(Dev d, int64_t n_new,
     const int page = d.table[(size_t)lo * d.maxpg + slot / kPage];
     s_page = page;
     s_row = slot % kPage;
+    s_pos = si[SI_OLD_NEXT] + j;
     d.pos[(size_t)page * kPage + slot % kPage] = si[SI_OLD_NEXT] + j;
     d.tok[(size_t)page * kPage + slot % kPage] = tok_new[tk];
   }
   __syncthreads();
   const int page = s_page, row = s_row;
+  const PoolStrides ps = pool_strides(d.NB, d.H, D);
   constexpr int C8 = D / 8;
+  if constexpr (ROPE) {
+    const int pos = s_pos;
+    for (int i = threadIdx.x; i < d.RD / 2; i += blockDim.x) {
+      double sn = 0.0, cs = 1.0;
+      if (pos != 0) sincos((double)pos * d.theta[i], &sn, &cs);
+      s_cs[i] = make_double2(cs, sn);
+    }
+    __syncthreads();
+    constexpr int CH = D / 16;                 // chunk pairs per row
+    const int rch = d.RD / 16;
+    const int npair = d.L * d.H * CH;
+    for (int c = threadIdx.x; c < npair; c += blockDim.x) {
+      const int pc = c % CH, lh = c / CH, h = lh % d.H, l = lh / d.H;
+      const bool rot = pc < rch;
+      const int xo = rot ? 8 * pc : d.RD + 8 * (pc - rch);
+      const int yoff = rot ? d.RD / 2 : (D - d.RD) / 2;
+      const size_t src = (((size_t)l * n_new + tk) * d.H + h) * D + xo;
+      const size_t dst = (size_t)l * ps.layer + (size_t)page * ps.page + (size_t)h * ps.head +
+                         (size_t)row * D + xo;
+      u32x4 x = *reinterpret_cast<const u32x4 *>(k_new + src);
+      u32x4 y = *reinterpret_cast<const u32x4 *>(k_new + src + yoff);
+      if (rot && pos != 0) rotate8(x, y, &s_cs[8 * pc]);
+      *reinterpret_cast<u32x4 *>(d.k + dst) = x;
+      *reinterpret_cast<u32x4 *>(d.k + dst + yoff) = y;
+    }
+  }
   const int nchunk = d.L * d.H * C8;
   for (int c = threadIdx.x; c < nchunk; c += blockDim.x) {
     const int e8 = c % C8, lh = c / C8, h = lh % d.H, l = lh / d.H;
     const size_t src = (((size_t)l * n_new + tk) * d.H + h) * D + 8 * e8;
-    const PoolStrides ps = pool_strides(d.NB, d.H, D);
     const size_t dst = (size_t)l * ps.layer + (size_t)page * ps.page + (size_t)h * ps.head +
                        (size_t)row * D + 8 * e8;
-    *reinterpret_cast<uint4 *>(d.k + dst) = *reinterpret_cast<const uint4 *>(k_new + src);
+    if constexpr (!ROPE)
+      *reinterpret_cast<uint4 *>(d.k + dst) = *reinterpret_cast<const uint4 *>(k_new + src);
     *reinterpret_cast<uint4 *>(d.v + dst) = *reinterpret_cast<const uint4 *>(v_new + src);
   }
+}
+
+// ---------------------------------------------------------------------------
+// release: the flagged sequences' pages go back on the free stack
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kPlanThreads) void release_kernel(Dev d, const uint8_t *sel) {
+  __shared__ int s_wave[kPlanThreads / 64 + 1];
+  __shared__ int s_ok;
+  const int t = threadIdx.x;
+  if (t == 0) s_ok = d.ctl[CTL_ERR] == 0;    // a latched error makes mutating calls no-ops
+  __syncthreads();
+  if (!s_ok) return;
+  const int fc = *d.free_count;
+  int run = 0;
+  for (int base = 0; base < d.B; base += kPlanThreads) {
+    const int b = base + t;
+    int np = 0;
+    if (b < d.B && sel[b]) np = (d.lens[b] + kPage - 1) / kPage;
+    int tot;
+    const int ex = block_exclusive_scan<kPlanThreads>(np, s_wave, &tot);
+    if (b < d.B && sel[b]) {
+      int32_t *row = d.table + (size_t)b * d.maxpg;
+      for (int k = 0; k < np; ++k) {
+        d.free_stack[fc + run + ex + k] = row[k];
+        row[k] = -1;
+      }
+      d.lens[b] = 0;
+      d.next_pos[b] = 0;
+    }
+    run += tot;
+  }
+  __syncthreads();
+  if (t == 0) *d.free_count = fc + run;
 }
 
 // ---------------------------------------------------------------------------
@@ -824,17 +890,23 @@ hipError_t launch_commit(const Dev &d, hipStream_t st) {
 
 hipError_t launch_append(const Dev &d, const int32_t *counts, int64_t n_new,
                          const uint16_t *k_new, const uint16_t *v_new, const int32_t *tok_new,
-                         hipStream_t st, hipEvent_t ev_mid) {
+                         bool rope, hipStream_t st) {
   hipLaunchKernelGGL(append_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, d, counts);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_new == 0) return e;
-  (void)ev_mid;
-  if (d.D == 128)
-    hipLaunchKernelGGL(append_copy_kernel<128>, dim3((unsigned)n_new), dim3(256), 0, st, d,
-                       n_new, k_new, v_new, tok_new);
-  else
-    hipLaunchKernelGGL(append_copy_kernel<64>, dim3((unsigned)n_new), dim3(256), 0, st, d,
-                       n_new, k_new, v_new, tok_new);
+  const dim3 g((unsigned)n_new), b(256);
+  if (d.D == 128) {
+    if (rope) hipLaunchKernelGGL((append_copy_kernel<128, true>), g, b, 0, st, d, n_new, k_new, v_new, tok_new);
+    else hipLaunchKernelGGL((append_copy_kernel<128, false>), g, b, 0, st, d, n_new, k_new, v_new, tok_new);
+  } else {
+    if (rope) hipLaunchKernelGGL((append_copy_kernel<64, true>), g, b, 0, st, d, n_new, k_new, v_new, tok_new);
+    else hipLaunchKernelGGL((append_copy_kernel<64, false>), g, b, 0, st, d, n_new, k_new, v_new, tok_new);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_release(const Dev &d, const uint8_t *sel, hipStream_t st) {
+  hipLaunchKernelGGL(release_kernel, dim3(1), dim3(kPlanThreads), 0, st, d, sel);
   return hipGetLastError();
 }
 

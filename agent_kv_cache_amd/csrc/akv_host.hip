@@ -258,14 +258,34 @@ akv_status akv_cache_reset(akv_cache *c, const int32_t *page_order, void *stream
   return AKV_OK;
 }
 
-akv_status akv_append(akv_cache *c, const int32_t *counts, int64_t n_new, const uint16_t *k_new,
-                      const uint16_t *v_new, const int32_t *token_ids, void *stream) {
+static akv_status append_impl(akv_cache *c, const int32_t *counts, int64_t n_new,
+                              const uint16_t *k_new, const uint16_t *v_new,
+                              const int32_t *token_ids, bool rope, void *stream) {
   if (!c || !counts || n_new < 0 || n_new > INT32_MAX) return AKV_ERR_ARG;
   if (n_new > 0 && (!k_new || !v_new || !token_ids)) return AKV_ERR_ARG;
   if (n_new > 0 && (!aligned(k_new, 16) || !aligned(v_new, 16))) return AKV_ERR_ARG;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   Timed tm(c, AKV_KERNEL_APPEND, st);
-  AKV_HIP(akv::launch_append(c->dev, counts, n_new, k_new, v_new, token_ids, st, nullptr));
+  AKV_HIP(akv::launch_append(c->dev, counts, n_new, k_new, v_new, token_ids, rope, st));
+  return AKV_OK;
+}
+
+akv_status akv_append(akv_cache *c, const int32_t *counts, int64_t n_new, const uint16_t *k_new,
+                      const uint16_t *v_new, const int32_t *token_ids, void *stream) {
+  return append_impl(c, counts, n_new, k_new, v_new, token_ids, false, stream);
+}
+
+akv_status akv_append_rope(akv_cache *c, const int32_t *counts, int64_t n_new,
+                           const uint16_t *k_raw, const uint16_t *v_new, const int32_t *token_ids,
+                           void *stream) {
+  return append_impl(c, counts, n_new, k_raw, v_new, token_ids, true, stream);
+}
+
+akv_status akv_release(akv_cache *c, const uint8_t *release, void *stream) {
+  if (!c || !release) return AKV_ERR_ARG;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  Timed tm(c, AKV_KERNEL_RELEASE, st);
+  AKV_HIP(akv::launch_release(c->dev, release, st));
   return AKV_OK;
 }
 

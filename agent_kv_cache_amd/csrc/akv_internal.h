@@ -151,8 +151,8 @@ hipError_t launch_commit(const Dev &d, hipStream_t st);
 int move_blocks_per_cu(int D);
 hipError_t launch_append(const Dev &d, const int32_t *counts, int64_t n_new,
                          const uint16_t *k_new, const uint16_t *v_new,
-                         const int32_t *tok_new, hipStream_t st,
-                         hipEvent_t ev_mid);
+                         const int32_t *tok_new, bool rope, hipStream_t st);
+hipError_t launch_release(const Dev &d, const uint8_t *sel, hipStream_t st);
 hipError_t launch_reset(const Dev &d, const int32_t *order_dev, hipStream_t st);
 hipError_t launch_attention(const Dev &d, const uint16_t *q, const int32_t *active_len,
                             int l0, int nL, int Hq, uint16_t *out, float *part,

@@ -426,6 +426,73 @@ def run_restore(args):
     return res
 
 
+def run_append(args):
+    """Append of the c2 request's 32768 tokens in one call (a prefill's KV
+    write), plain (keys already rotated) and with the RoPE step fused in
+    (akv_append_rope).  One step = reset the cache metadata + one append.
+    Algorithmic bytes: K and V of every new token read once and written once,
+    plus its position and token id."""
+    import torch
+
+    from agent_kv_cache_amd import harness as Hn
+    from agent_kv_cache_amd import workloads as W
+
+    wl = W.c2()
+    sh = wl.shape
+    n = wl.seq_lens[0]
+    ropt = rope_options(args, sh)
+    cache = Hn.make_cache(sh, [n], 8, **ropt)
+    cache.reset()
+    dev = cache.device
+    k = W.randn_bf16((sh.n_layers, n, sh.n_kv_heads, sh.head_dim), 205, device="cuda")
+    v = W.randn_bf16((sh.n_layers, n, sh.n_kv_heads, sh.head_dim), 206, device="cuda")
+    tid = torch.arange(n, dtype=torch.int32, device=dev)
+    counts = torch.tensor([n], dtype=torch.int32, device=dev)
+    snap = cache.meta.clone()
+    row = sh.n_layers * sh.n_kv_heads * sh.head_dim * 2
+    alg = n * 2 * row * 2 + n * 12
+    res = {}
+    for name, fn in (("append", cache.append), ("append_rope", cache.append_rope)):
+        def step():
+            cache.meta.copy_(snap)
+            fn(counts, n, k, v, tid)
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        if cache.sync_status() != 0:
+            raise RuntimeError("device status during warm-up")
+        cache.profile_read("append", reset=True)
+        cache.profile_enable(True)
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        cache.profile_enable(False)
+        if cache.sync_status() != 0:
+            raise RuntimeError("device status after the timed steps")
+        ms, cnt = cache.profile_read("append")
+        kms = ms / max(cnt, 1)
+        res[name] = {"ms": round(kms, 4), "gbps": round(alg / (kms * 1e-3) / 1e9, 1),
+                     "frac_of_peak": round(alg / (kms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                     "ms_per_step_wall": round((t1 - t0) * 1e3 / args.steps, 4)}
+    fr = res["append_rope"]
+    return {
+        "metric": "append GB/s (K/V write of new tokens, plain and RoPE-fused), 1 GPU",
+        "value": fr["gbps"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": fr["ms_per_step_wall"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "append of 32768 tokens to one sequence, Llama-8B shape "
+                               "(32 layers, 8 kv heads, d 128)",
+                   "tokens": n, "algorithmic_bytes": alg,
+                   **({"rotary_dim": args.rotary_dim} if args.rotary_dim else {})},
+        "roofline": {"bound": "hbm", "kernel": "append_copy_kernel (RoPE fused)",
+                     "achieved": fr["gbps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": fr["frac_of_peak"], "traffic": None},
+        "parts": res,
+    }
+
+
 def calibrate(nbytes: int, reps: int):
     """Achieved GB/s of torch's device copy (read+write), fill (write) and a
     max-reduction (read) over `nbytes`: the plain streaming kernels that bound
@@ -459,7 +526,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c2",
-                    choices=["c1", "c2", "c3", "c4", "c5", "restore"])
+                    choices=["c1", "c2", "c3", "c4", "c5", "restore", "append"])
     ap.add_argument("--cpu-rows", type=int, default=256,
                     help="restore: rows per segment in the oracle sample")
     ap.add_argument("--rotary-dim", type=int, default=0,
@@ -502,6 +569,9 @@ def main():
         return
     if args.workload == "restore":
         print(json.dumps(run_restore(args)), flush=True)
+        return
+    if args.workload == "append":
+        print(json.dumps(run_append(args)), flush=True)
         return
     wl = W.WORKLOADS[args.workload]()
     sh = wl.shape

@@ -134,6 +134,22 @@ akv_status akv_append(akv_cache *c, const int32_t *counts, int64_t n_new,
                       const uint16_t *k_new, const uint16_t *v_new,
                       const int32_t *token_ids, void *stream);
 
+/* akv_append with the model's RoPE step fused in ([CE] eq. 3: the new keys
+ * are rotated at the positions they take): k_raw holds the keys before RoPE,
+ * same layout as k_new; entry j of sequence b is stored as
+ * bf16(R(next_pos_b + j) k_raw) -- fp64 angle (next_pos_b + j) * theta_i and
+ * fp64 rotation of each pair (i, i + r/2), rounded once to nearest even; the
+ * non-rotary tail (partial RoPE) and V are copied.  Errors as akv_append. */
+akv_status akv_append_rope(akv_cache *c, const int32_t *counts, int64_t n_new,
+                           const uint16_t *k_raw, const uint16_t *v_new,
+                           const int32_t *token_ids, void *stream);
+
+/* End of a request: every sequence b with release[b] != 0 returns all its
+ * pages to the device free stack and becomes empty with next_pos = 0, ready
+ * for a new request (or as the destination of akv_fork).  release: DEVICE
+ * uint8 [B].  A no-op while a device error is latched. */
+akv_status akv_release(akv_cache *c, const uint8_t *release, void *stream);
+
 /* [CE] eq. (4): drop the active entries whose mask byte is non-zero.
  *   drop_mask : DEVICE uint8 [B][S]
  * Survivors keep their order, K, V, position and token id; seq_lens shrink;
@@ -243,7 +259,8 @@ enum {
   AKV_KERNEL_COMBINE = 4,  /* split-K merge */
   AKV_KERNEL_APPEND = 5,   /* append plan + copy */
   AKV_KERNEL_SEGMENT = 6,  /* segment-batch attention */
-  AKV_KERNEL_COUNT = 7
+  AKV_KERNEL_RELEASE = 7,  /* page release */
+  AKV_KERNEL_COUNT = 8
 };
 akv_status akv_profile_enable(akv_cache *c, int on);
 /* Synchronises the recorded events; *total_ms and *launches accumulate

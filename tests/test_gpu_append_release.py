@@ -1,0 +1,161 @@
+"""GPU parity of the append with the RoPE step fused in (akv_append_rope) and
+of the page release (akv_release), through the C ABI, against the fp64
+oracle's append_rotated / release.
+
+Bars: positions / token ids / lengths / next_pos bit-exact; K within one bf16
+step of the oracle's single rounding; V bit-exact; free-stack accounting
+exact.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+from agent_kv_cache_amd import harness as Hn  # noqa: E402
+from agent_kv_cache_amd import workloads as W  # noqa: E402
+from oracle import akv_oracle as O  # noqa: E402
+
+from gpu_util import (check_attention, check_kv, check_meta, oracle_for, say,  # noqa: E402
+                      snapshot, same_state, to_f64)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from agent_kv_cache_amd.binding import lib
+    lib()
+
+
+def _append_rope(cache, oc, sh, per_seq, seed, tid_base):
+    N = int(sum(per_seq))
+    k = W.randn_bf16((sh.n_layers, N, sh.n_kv_heads, sh.head_dim), seed)
+    v = W.randn_bf16((sh.n_layers, N, sh.n_kv_heads, sh.head_dim), seed + 1)
+    tid = np.arange(N, dtype=np.int64) + tid_base
+    cache.append_rope(torch.tensor(per_seq, dtype=torch.int32, device=cache.device), N,
+                      k.to(cache.device), v.to(cache.device),
+                      torch.tensor(tid, dtype=torch.int32, device=cache.device))
+    o = 0
+    for b, n in enumerate(per_seq):
+        if n:
+            sl = slice(o, o + n)
+            oc.append_rotated(b, tid[sl], to_f64(k[:, sl].permute(1, 0, 2, 3)),
+                              to_f64(v[:, sl].permute(1, 0, 2, 3)))
+        o += n
+
+
+@pytest.mark.parametrize("d,r,freq", [(128, 0, None), (128, 64, None), (64, 0, "yarn"),
+                                      (128, 0, "llama3"), (64, 32, None)])
+def test_append_rope_matches_oracle(d, r, freq):
+    sh = W.Shape(3, 2, d, 8, 1.5e5 if d == 64 else 5.0e5)
+    rr = r or d
+    th = None
+    if freq == "yarn":
+        th = O.yarn_theta(rr, sh.rope_base, 32.0, 4096)
+    elif freq == "llama3":
+        th = O.llama3_theta(O.rope_theta(d, sh.rope_base), 8.0, 1.0, 4.0, 8192)
+    lens = [0, 7, 100, 300]
+    B = len(lens)
+    say(f"case append_rope d={d} r={r} freq={freq}")
+    cache = Hn.make_cache(sh, lens, 120, max_blocks_per_seq=48, rotary_dim=r,
+                          inv_freq=th)
+    cache.reset(np.random.default_rng(d + r).permutation(cache.NB).astype(np.int32))
+    Hn.fill(cache, sh, lens, 31, gen_device="cpu")
+    oc = oracle_for(sh, lens, 31, rotary_dim=r or None, theta=th)
+    # move sequences to large, gapped positions first: next_pos far from len
+    rng = np.random.default_rng(5)
+    masks = [(rng.uniform(size=n) < 0.3).astype(np.uint8) for n in lens]
+    cache.drop(Hn.mask_tensor(cache, masks))
+    for b in range(B):
+        oc.drop(b, masks[b])
+    old = [oc.seqs[b].pos.copy() for b in range(B)]
+    newp = [np.arange(len(p)) * 3 + 100000 for p in old]
+    cache.reposition(Hn.pos_tensor(cache, old), Hn.pos_tensor(cache, newp))
+    for b in range(B):
+        oc.reposition(b, newp[b])
+    assert cache.sync_status() == 0
+    _append_rope(cache, oc, sh, [5, 0, 33, 17], 40, 1 << 26)
+    _append_rope(cache, oc, sh, [1, 16, 0, 2], 42, 1 << 27)
+    assert cache.sync_status() == 0
+    check_meta(cache, oc)
+    worst = check_kv(cache, oc, k_ulp=1)        # one rounding per key on both sides
+    say(" worst K ulp", worst)
+    q = W.randn_bf16((B, sh.n_layers, sh.n_q_heads, d), 43).to(cache.device)
+    out = torch.empty_like(q)
+    ws = torch.empty(max(256, cache.decode_workspace_bytes(sh.n_layers, sh.n_q_heads)),
+                     dtype=torch.uint8, device=cache.device)
+    cache.decode_attention(q, out, ws)
+    check_attention(cache, oc, q, out)
+
+
+def test_append_rope_first_tokens_are_copied():
+    """Position 0 is the identity: a fresh sequence's first key is stored as given."""
+    sh = W.Shape(2, 2, 128, 8, 1e4)
+    cache = Hn.make_cache(sh, [0, 0], 8)
+    cache.reset()
+    k = W.randn_bf16((2, 2, 2, 128), 50).to(cache.device)
+    v = W.randn_bf16((2, 2, 2, 128), 51).to(cache.device)
+    cache.append_rope(torch.tensor([1, 1], dtype=torch.int32, device=cache.device), 2, k, v,
+                      torch.tensor([0, 1], dtype=torch.int32, device=cache.device))
+    assert cache.sync_status() == 0
+    for b in range(2):
+        for l in range(2):
+            got = cache.gather_rows(b, l, "k")[0]
+            assert torch.equal(got.view(torch.int16), k[l, b].view(torch.int16))
+
+
+def test_release_returns_pages_and_slots_are_reused():
+    sh = W.Shape(2, 2, 64, 4, 1e4)
+    lens = [33, 100, 0, 257]
+    cache = Hn.make_cache(sh, lens, 20)
+    cache.reset(np.random.default_rng(3).permutation(cache.NB).astype(np.int32))
+    Hn.fill(cache, sh, lens, 60, gen_device="cpu")
+    oc = oracle_for(sh, lens, 60)
+    say("case release")
+    fc0 = int(cache.free_count)
+    keep = {b: snapshot(cache, b) for b in (0, 2)}
+    pages1, pages3 = (set(cache.block_table[b, :Hn.pages_for(lens[b])].tolist()) for b in (1, 3))
+    sel = torch.tensor([0, 1, 0, 1], dtype=torch.uint8, device=cache.device)
+    cache.release(sel)
+    assert cache.sync_status() == 0
+    oc.release(1)
+    oc.release(3)
+    assert int(cache.free_count) == fc0 + len(pages1) + len(pages3)
+    top = cache.free_stack[fc0:int(cache.free_count)].tolist()
+    assert set(top) == pages1 | pages3
+    assert (cache.block_table[1] == -1).all() and (cache.block_table[3] == -1).all()
+    check_meta(cache, oc)
+    for b in (0, 2):
+        same_state(keep[b], snapshot(cache, b))
+    # every page is owned exactly once: free stack + tables
+    owned = cache.free_stack[:int(cache.free_count)].tolist()
+    for b in range(4):
+        owned += cache.block_table[b, :Hn.pages_for(int(cache.seq_lens[b]))].tolist()
+    assert sorted(owned) == list(range(cache.NB))
+    # reuse: appends start at position 0; a fork may target a released slot
+    _append_rope(cache, oc, sh, [0, 20, 0, 0], 61, 1 << 26)
+    cache.fork([3, -1, -1, -1])
+    oc.fork(0, 3)
+    assert cache.sync_status() == 0
+    check_meta(cache, oc)
+    check_kv(cache, oc, k_ulp=1)
+
+
+def test_release_is_a_no_op_while_an_error_is_latched():
+    sh = W.Shape(1, 1, 64, 4, 1e4)
+    lens = [40, 40]
+    cache = Hn.make_cache(sh, lens, 4)
+    cache.reset()
+    Hn.fill(cache, sh, lens, 70, gen_device="cpu")
+    say("case release with a latched error")
+    before = [snapshot(cache, b) for b in range(2)]
+    fc = int(cache.free_count)
+    bad = [np.arange(40)[::-1].copy(), None]               # decreasing targets: ORDER latched
+    cache.reposition(None, Hn.pos_tensor(cache, bad))
+    cache.release(torch.tensor([1, 1], dtype=torch.uint8, device=cache.device))
+    assert cache.sync_status() == 2
+    assert int(cache.free_count) == fc
+    for b in range(2):
+        same_state(before[b], snapshot(cache, b))
