@@ -105,7 +105,10 @@ BF16_OUT = 2.0 ** -8
 
 
 def attn_error(got, ref) -> float:
-    """max over elements of |got - ref| - 2^-8 |ref| (compared with 1e-2)."""
+    """max over elements of |got - ref| - 2^-8 |ref| (compared with 1e-2);
+    a non-finite output counts as an infinite error."""
+    if not np.isfinite(got).all():
+        return float("inf")
     return float((np.abs(got - ref) - BF16_OUT * np.abs(ref)).max())
 
 
