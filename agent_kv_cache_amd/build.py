@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libakv.so")
-SOURCES = ["akv_host.hip", "akv_compact.hip", "akv_attn.hip", "akv_segment.hip"]
+SOURCES = ["akv_host.hip", "akv_compact.hip", "akv_move.hip", "akv_attn.hip", "akv_segment.hip"]
 ARCH = os.environ.get("AKV_OFFLOAD_ARCH", "gfx950")
 
 

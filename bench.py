@@ -234,18 +234,20 @@ def run_history(args):
 def counted_traffic(name):
     """HBM bytes per launch from a committed rocprofv3 counter record under
     profiles/ (FETCH_SIZE and WRITE_SIZE scaled by what they read for a
-    plain copy of known size), used only while the kernel source is
-    unchanged since the counters were taken; else None."""
+    plain copy of known size), used only while every kernel source file the
+    record names is unchanged since the counters were taken; else None."""
     import hashlib
     path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     pj = json.load(open(path))
-    src = os.path.join(ROOT, pj.get("source_file", ""))
-    if os.path.exists(src) and hashlib.sha256(open(src, "rb").read()).hexdigest() == \
-            pj.get("source_sha256"):
-        return pj.get("hbm_bytes_per_launch")
-    return None
+    files = pj.get("source_files") or {pj.get("source_file", ""): pj.get("source_sha256")}
+    for rel, digest in files.items():
+        src = os.path.join(ROOT, rel)
+        if not (rel and os.path.exists(src)
+                and hashlib.sha256(open(src, "rb").read()).hexdigest() == digest):
+            return None
+    return pj.get("hbm_bytes_per_launch")
 
 
 def restore_counts(rs):
