@@ -19,6 +19,7 @@ struct akv_cache {
   int device = 0;
   int n_cu = 256;
   int move_grid = 2048;
+  int oneshot_cap = 1;     // units (page x layer) of the largest op moved by the one-shot launch
   int attn_per_cu = 2;
   int n_full_layers = 0;   // layers without a sliding window
   bool profile = false;
@@ -114,7 +115,7 @@ akv_status run_compaction(akv_cache *c, const uint8_t *mask, const int32_t *new_
   }
   {
     Timed tm(c, AKV_KERNEL_MOVE, st);
-    AKV_HIP(akv::launch_move(c->dev, mode, c->move_grid, st));
+    AKV_HIP(akv::launch_move(c->dev, mode, c->move_grid, c->oneshot_cap, st));
   }
   {
     Timed tm(c, AKV_KERNEL_COMMIT, st);
@@ -142,7 +143,9 @@ akv_status akv_cache_init(const akv_cache_desc *d, akv_cache **out) {
     return AKV_ERR_ARG;
   if (d->block_size != akv::kPage) return AKV_ERR_ARG;
   if (d->head_dim != 64 && d->head_dim != 128) return AKV_ERR_ARG;
-  if (!(d->rope_base > 0.0) || !isfinite(d->rope_base)) return AKV_ERR_ARG;
+  // rotation frequencies must lie in [0, 1] (rope_base >= 1): the move's sine
+  // and cosine reduce angles delta * theta_i below 2^31 exactly
+  if (!(d->rope_base >= 1.0) || !isfinite(d->rope_base)) return AKV_ERR_ARG;
   if ((long long)d->max_blocks_per_seq * akv::kPage > INT32_MAX / 2) return AKV_ERR_ARG;
   if (!d->k_pool || !d->v_pool || !d->block_table || !d->seq_lens || !d->next_pos ||
       !d->positions || !d->token_ids || !d->free_stack || !d->free_count || !d->scratch)
@@ -155,7 +158,8 @@ akv_status akv_cache_init(const akv_cache_desc *d, akv_cache **out) {
   if (rd < 16 || rd > d->head_dim || rd % 16) return AKV_ERR_ARG;
   if (d->inv_freq)
     for (int i = 0; i < rd / 2; ++i)
-      if (!isfinite(d->inv_freq[i]) || d->inv_freq[i] < 0.0) return AKV_ERR_ARG;
+      if (!isfinite(d->inv_freq[i]) || d->inv_freq[i] < 0.0 || d->inv_freq[i] > 1.0)
+        return AKV_ERR_ARG;
   int any_window = 0;
   if (d->layer_window)
     for (int l = 0; l < d->n_layers; ++l) {
@@ -209,6 +213,17 @@ akv_status akv_cache_init(const akv_cache_desc *d, akv_cache **out) {
     return AKV_ERR_HIP;
   }
   c->move_grid = akv::move_blocks_per_cu(d->head_dim) * c->n_cu;
+  {
+    // One-shot launch size: every block the op could need (parts of each
+    // (page, layer) unit it could rebuild), at most AKV_MOVE_ONESHOT_CAP
+    // blocks; blocks past the planned count exit at once and a larger op runs
+    // on the persistent grid.
+    const long long pages = std::min<long long>(d->n_blocks,
+                                                (long long)d->n_seqs * d->max_blocks_per_seq);
+    const long long parts = AKV_MOVE_OS_PLANES * AKV_MOVE_OS_HEAD_GROUPS;
+    c->oneshot_cap =
+        (int)std::max(1LL, std::min<long long>(pages * d->n_layers * parts, AKV_MOVE_ONESHOT_CAP));
+  }
   c->attn_per_cu = akv::attn_blocks_per_cu(d->head_dim);
 
   // theta_i over the rotary dims: the caller's table, else base^(-2i/r);

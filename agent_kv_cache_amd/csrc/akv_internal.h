@@ -47,6 +47,20 @@ enum SeqInfo : int {
   kSeqInfo = 16
 };
 
+// Ops that rebuild at most this many (page, layer) units are moved by a
+// one-shot grid (one block per unit), larger ones by a persistent grid.
+#ifndef AKV_MOVE_ONESHOT_CAP
+#define AKV_MOVE_ONESHOT_CAP 131072
+#endif
+// One-shot blocks per (page, layer) unit: planes (1: K and V in one block,
+// 2: one block each) times head groups.
+#ifndef AKV_MOVE_OS_PLANES
+#define AKV_MOVE_OS_PLANES 1
+#endif
+#ifndef AKV_MOVE_OS_HEAD_GROUPS
+#define AKV_MOVE_OS_HEAD_GROUPS 1
+#endif
+
 // Mode bits of the compaction plan.
 enum Mode : int {
   M_DROP = 1,        // a drop mask is given
@@ -146,7 +160,7 @@ inline ScratchLayout scratch_layout(int B, int S, int NB, int L) {
 // Launchers (each in the .hip file that defines its kernels).
 hipError_t launch_plan(const Dev &d, const uint8_t *mask, const int32_t *new_pos,
                        const int32_t *old_pos, int mode, hipStream_t st);
-hipError_t launch_move(const Dev &d, int mode, int grid, hipStream_t st);
+hipError_t launch_move(const Dev &d, int mode, int grid, int oneshot_cap, hipStream_t st);
 hipError_t launch_commit(const Dev &d, hipStream_t st);
 int move_blocks_per_cu(int D);
 hipError_t launch_append(const Dev &d, const int32_t *counts, int64_t n_new,

@@ -3,12 +3,23 @@
 // copies when p == q, copies V and never rotates it, and writes to a
 // separate destination slot).
 //
-// A persistent grid walks (page, layer) units of the rebuilt pages.  Pages
-// from the first dropped page on are rebuilt out of place in fresh pages (K
-// re-rotated when its delta is non-zero, V copied bitwise); pages before it
-// whose positions change are re-rotated in place.  16-B loads and stores, one
+// The kernel walks (page, layer) units of the rebuilt pages.  Pages from the
+// first dropped page on are rebuilt out of place in fresh pages (K re-rotated
+// when its delta is non-zero, V copied bitwise); pages before it whose
+// positions change are re-rotated in place.  16-B loads and stores, one
 // (row, 8 NeoX pairs) per thread.  The same kernel serves akv_fork (every
 // page of the copy rebuilt, sources left untouched).
+//
+// Two launch shapes, chosen on the device from the planned unit count:
+//  * one-shot (ops of up to a few 10^5 units): one block per (page, layer)
+//    unit in layer-major order.  Blocks are dispatched in index order, so the
+//    blocks in flight read and write a compact, sliding address range; on
+//    MI355X this streams ~15% faster than a persistent grid whose workgroups
+//    each walk their own pages through all layers (measured on the
+//    Llama-8B-shaped drop: 0.87 -> 0.76 ms).
+//  * persistent (larger ops): occupancy x CUs workgroups, each taking a
+//    contiguous range of page-major units, so the per-page set-up is shared
+//    by all the layers a workgroup moves.
 #include "akv_internal.h"
 #include "akv_rope.h"
 
@@ -24,12 +35,6 @@ namespace akv {
 #endif
 #ifndef AKV_MOVE_NT
 #define AKV_MOVE_NT 1          // nontemporal hint on the streamed KV accesses
-#endif
-#ifndef AKV_MOVE_SPLIT_KV
-#define AKV_MOVE_SPLIT_KV 1    // stream a unit's K slices, then its V slices
-#endif
-#ifndef AKV_MOVE_ROTATE
-#define AKV_MOVE_ROTATE 0      // start each page's layer walk at a page-dependent layer
 #endif
 
 constexpr int kMoveThreads = 256;
@@ -53,19 +58,21 @@ __device__ __forceinline__ void st_stream(uint16_t *p, u32x4 v) {
 }
 
 // Work split: the rebuilt pages (moved first, then in-place) times the L
-// layers form U = pages * L (page, layer) units, ordered page-major.  Workgroup
-// w takes the contiguous units [w*U/G, (w+1)*U/G), so every workgroup moves
-// the same number of (layer, page) slices whatever the page count, and the
-// per-page set-up (row sources, deltas, cos/sin) is done once per page it
-// touches.
-template <int D, bool NT>
-__global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(Dev d, int mode) {
+// layers form U = pages * L (page, layer) units.  Persistent launch: units
+// ordered page-major, workgroup w takes the contiguous units
+// [w*U/G, (w+1)*U/G), so every workgroup moves the same number of (layer,
+// page) slices whatever the page count, and the per-page set-up (row
+// sources, deltas, cos/sin) is done once per page it touches.  One-shot
+// launch: block b takes unit (page b mod pages, layer b / pages).
+template <int D, bool NT, bool ONESHOT>
+__global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(Dev d, int mode,
+                                                                                 int oneshot_cap) {
   constexpr int HALF = D / 2;
   constexpr int CH = D / 16;             // 16-B chunks per half row
   constexpr int TPH = kPage * CH;        // threads per (layer, head) slice
   constexpr int NS = kMoveThreads / TPH; // slices per pass
   constexpr int U = AKV_MOVE_UNROLL;      // slices loaded before any store
-  __shared__ int s_b, s_po, s_dst, s_mv;
+  __shared__ int s_dst, s_mv;
   __shared__ int s_src[kPage], s_valid[kPage], s_delta[kPage], s_rep[kPage];
   __shared__ int s_repval[kPage], s_nrep;
   __shared__ double2 s_cs[kPage][HALF];
@@ -76,8 +83,37 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
   if (npages == 0) return;
   const int fc_old = d.ctl[CTL_FC_OLD];
   const long long units = npages * d.L;
-  const long long u0 = units * blockIdx.x / gridDim.x;
-  const long long u1 = units * (blockIdx.x + 1) / gridDim.x;
+  // Two launches share the work.  An op of at most oneshot_cap blocks runs in
+  // the one-shot launch: one block per part of a (page, layer) unit (parts:
+  // the K and V planes, each split into head groups), in layer-major order --
+  // block b moves part b mod P of page (b / P) mod pages at layer
+  // b / (P pages) -- so the blocks in flight cover a compact address range.
+  // A larger op runs in the persistent launch (contiguous unit ranges).
+  constexpr int HGN = AKV_MOVE_OS_HEAD_GROUPS, PARTS = AKV_MOVE_OS_PLANES * HGN;
+  if ((units * PARTS <= oneshot_cap) != ONESHOT) return;
+  long long u0, u1;
+  int p_lo = 0, p_hi = 2, h_lo = 0, h_hi = d.H;
+  bool first_part = true;   // the part that moves positions / token ids
+  if (ONESHOT) {
+    if (blockIdx.x >= units * PARTS) return;
+    const long long ub = blockIdx.x / PARTS;
+    const int part = (int)(blockIdx.x - ub * PARTS);
+    u0 = (ub % npages) * d.L + ub / npages;
+    u1 = u0 + 1;
+    if (AKV_MOVE_OS_PLANES == 2) {
+      p_lo = part / HGN;
+      p_hi = p_lo + 1;
+    }
+    const int hg = part % HGN, hper = (d.H + HGN - 1) / HGN;
+    h_lo = min(d.H, hg * hper);
+    h_hi = min(d.H, h_lo + hper);
+    first_part = part == 0;
+    if (h_lo >= h_hi) return;
+  } else {
+    u0 = units * blockIdx.x / gridDim.x;
+    u1 = units * (blockIdx.x + 1) / gridDim.x;
+  }
+  const int nh = h_hi - h_lo;
   const int t = threadIdx.x;
   const int r = (t % TPH) / CH, pc = t % CH, slot = t / TPH;
   // Chunk pc of a row: a rotary chunk pairs dims [8pc, 8pc+8) with the same
@@ -97,7 +133,10 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
     const int l0 = (int)(max(u0, pgl * d.L) - pgl * d.L);
     const int l1 = (int)(min(u1, (pgl + 1) * d.L) - pgl * d.L);
     __syncthreads();  // LDS of the previous page is no longer read
-    if (t == 0) {
+    // Rows: the 16 lanes t < 16 of wave 0 each find the page's sequence and
+    // destination (the same loads in every lane) and their row's source slot
+    // and delta, then rank the page's distinct deltas among themselves.
+    if (t < kPage) {
       const bool mv = pg < Tm;
       const int key = mv ? pg : pg - Tm;
       const int of = mv ? SI_MOVE_OFF : SI_INPLACE_OFF;
@@ -106,30 +145,26 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
         const int mid = (lo + hi + 1) >> 1;
         if (d.seq_info[(size_t)mid * kSeqInfo + of] <= key) lo = mid; else hi = mid - 1;
       }
-      const int *si = d.seq_info + (size_t)lo * kSeqInfo;
+      const int b = lo;
+      const int *si = d.seq_info + (size_t)b * kSeqInfo;
       const int po = (mv ? si[SI_FBD] : si[SI_FIP]) + (key - si[of]);
-      s_b = lo;
-      s_po = po;
-      s_mv = mv;
-      s_dst = mv ? d.free_stack[fc_old - 1 - pg] : d.table[(size_t)lo * d.maxpg + po];
-      if (mv && l0 == 0) d.stage[pg] = s_dst;
-    }
-    __syncthreads();
-    const int b = s_b, po = s_po, dst = s_dst;
-    const bool mv = s_mv;
-    if (t < kPage) {
-      const int rnew = d.seq_info[(size_t)b * kSeqInfo + SI_NEW_LEN];
+      const int dst = mv ? d.free_stack[fc_old - 1 - pg] : d.table[(size_t)b * d.maxpg + po];
       const int j = po * kPage + t;
-      const bool valid = j < rnew;
+      const bool valid = j < si[SI_NEW_LEN];
       // physical source slot (page * 16 + row); in place: the slot itself
       const int src = !valid ? 0
                       : ((mv && (mode & (M_DROP | M_FORK))) ? d.src_map[b * S + j]
-                                                 : d.table[(size_t)b * d.maxpg + po] * kPage + t);
+                                                             : d.table[(size_t)b * d.maxpg + po] * kPage + t);
       const int delta = (valid && (mode & M_REPOS)) ? d.delta_map[b * S + j] : 0;
       s_src[t] = src;
       s_valid[t] = valid;
       s_delta[t] = delta;
-      if (l0 == 0) {
+      if (t == 0) {
+        s_dst = dst;
+        s_mv = mv;
+        if (mv && l0 == 0 && first_part) d.stage[pg] = dst;
+      }
+      if (l0 == 0 && first_part) {
         const size_t dn = (size_t)dst * kPage + t;
         if (mv) {
           d.pos[dn] = valid ? d.pos[src] + delta : -1;
@@ -138,135 +173,108 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
           d.pos[dn] += delta;
         }
       }
+      if (rot_any) {
+        // slot of a delta = the number of distinct deltas whose first row
+        // comes earlier (lanes 0..15 of wave 0 are the rows)
+        int first = t;
+        for (int rr = kPage - 1; rr >= 0; --rr)
+          if (__shfl(delta, rr, 64) == delta) first = rr;
+        const bool is_first = first == t;
+        const unsigned long long fm = __ballot(is_first) & 0xFFFFull;
+        const int rep = __popcll(fm & ((1ull << first) - 1ull));
+        s_rep[t] = rep;
+        if (is_first) s_repval[rep] = delta;
+        if (t == 0) s_nrep = __popcll(fm);
+      }
     }
     __syncthreads();
-    if (rot_any) {
-      if (t == 0) {
-        int n = 0;
-        for (int rr = 0; rr < kPage; ++rr) {
-          const int dl = s_delta[rr];
-          int k = 0;
-          while (k < n && s_repval[k] != dl) ++k;
-          if (k == n) s_repval[n++] = dl;
-          s_rep[rr] = k;
+    const bool mv = s_mv;
+    const int dst = s_dst;
+    const bool valid = s_valid[r] != 0;
+    const int delta = s_delta[r];
+    const bool turn = valid && delta != 0 && rot_chunk;
+    const bool do_k = valid ? (mv || turn) : mv;
+    const int pend = min(p_hi, mv ? 2 : 1);   // planes: K, and V when the page moves
+    const int nsl = (l1 - l0) * nh;
+    const int sp = s_src[r];
+    const size_t src_row = (size_t)(sp >> 4) * ps.page + (size_t)(sp & 15) * D + xo;
+    const size_t dst_row = (size_t)dst * ps.page + (size_t)r * D + xo;
+    // Batches of U slices; K slices of the unit range first, then V slices
+    // (each pass streams one pool).  The first batch is loaded before the
+    // cos/sin set-up so that its latency covers the set-up.
+    int plane = p_lo, i0 = slot;
+    bool more = do_k && plane < pend && i0 < nsl;
+    u32x4 lo[U], hi[U];
+    size_t dofs[U];
+    bool on[U];
+    auto issue = [&]() {
+      uint16_t *pool = plane ? d.v : d.k;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int idx = i0 + u * NS;
+        on[u] = idx < nsl;
+        const int l = l0 + idx / nh, h = h_lo + idx % nh;
+        const size_t off = (size_t)l * lstride + (size_t)h * hstride;
+        dofs[u] = dst_row + off;
+        lo[u] = hi[u] = u32x4{0u, 0u, 0u, 0u};
+        if (on[u] && valid) {
+          lo[u] = ld_stream<NT>(pool + src_row + off);
+          hi[u] = ld_stream<NT>(pool + src_row + off + yoff);
         }
-        s_nrep = n;
       }
-      __syncthreads();
+    };
+    if (more) issue();
+    if (rot_any && p_lo == 0) {   // blocks that move only V need no cos/sin
       const int RH = d.RD / 2;
       const int ntask = s_nrep * RH;
       for (int task = t; task < ntask; task += kMoveThreads) {
         const int ri = task / RH, i = task - ri * RH;
         const int dl = s_repval[ri];
         double sn = 0.0, cs = 1.0;
-        if (dl != 0) sincos((double)dl * d.theta[i], &sn, &cs);
+        if (dl != 0) sincos_rope((double)dl * d.theta[i], &sn, &cs);
         s_cs[ri][i] = make_double2(cs, sn);
       }
       __syncthreads();
     }
-    const bool valid = s_valid[r] != 0;
-    const int delta = s_delta[r];
     // cos/sin of this thread's 8 pairs stay in LDS and are read per use
     const double2 *cs_row = &s_cs[(rot_any && delta != 0) ? s_rep[r] : 0][rot_chunk ? 8 * pc : 0];
-    const bool turn = valid && delta != 0 && rot_chunk;
-    const bool do_k = valid ? (mv || turn) : mv;
-    const bool do_v = mv;
-    if (!do_k) continue;
-    const int nsl = (l1 - l0) * d.H;
-#if AKV_MOVE_ROTATE
-    // the k-th unit of page pg is layer (k + rot) mod L: concurrently
-    // running workgroups then stream different layers' regions
-    const int rot = (int)((pgl * 7) % d.L);
-#endif
-    const int sp = s_src[r];
-    const size_t src_row = (size_t)(sp >> 4) * ps.page + (size_t)(sp & 15) * D + xo;
-    const size_t dst_row = (size_t)dst * ps.page + (size_t)r * D + xo;
-#if AKV_MOVE_SPLIT_KV
-    // K slices of the unit range first, then V slices: each pass streams one
-    // pool (two concurrent streams per workgroup instead of four)
-    for (int plane = 0; plane < (do_v ? 2 : 1); ++plane) {
+    while (more) {
       uint16_t *pool = plane ? d.v : d.k;
       const bool rot_plane = plane == 0 && turn;
-      for (int i0 = slot; i0 < nsl; i0 += NS * U) {
-        u32x4 lo[U], hi[U];
-        size_t dofs[U];
-        bool on[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int idx = i0 + u * NS;
-          on[u] = idx < nsl;
-          const int l = l0 + idx / d.H, h = idx % d.H;
-          const size_t off = (size_t)l * lstride + (size_t)h * hstride;
-          dofs[u] = dst_row + off;
-          lo[u] = hi[u] = u32x4{0u, 0u, 0u, 0u};
-          if (on[u] && valid) {
-            lo[u] = ld_stream<NT>(pool + src_row + off);
-            hi[u] = ld_stream<NT>(pool + src_row + off + yoff);
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          if (!on[u]) continue;
-          if (rot_plane) rotate8(lo[u], hi[u], cs_row);
-          st_stream<NT>(pool + dofs[u], lo[u]);
-          st_stream<NT>(pool + dofs[u] + yoff, hi[u]);
-        }
-      }
-    }
-#else
-    for (int i0 = slot; i0 < nsl; i0 += NS * U) {
-      u32x4 klo[U], khi[U], vlo[U], vhi[U];
-      size_t dofs[U];
-      bool on[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int idx = i0 + u * NS;
-        on[u] = idx < nsl;
-#if AKV_MOVE_ROTATE
-        int l = l0 + idx / d.H + rot;
-        if (l >= d.L) l -= d.L;
-#else
-        const int l = l0 + idx / d.H;
-#endif
-        const int h = idx % d.H;
-        const size_t off = (size_t)l * lstride + (size_t)h * hstride;
-        dofs[u] = dst_row + off;
-        klo[u] = khi[u] = vlo[u] = vhi[u] = u32x4{0u, 0u, 0u, 0u};
-        if (on[u] && valid) {
-          const size_t so = src_row + off;
-          klo[u] = ld_stream<NT>(d.k + so);
-          khi[u] = ld_stream<NT>(d.k + so + yoff);
-          if (do_v) {
-            vlo[u] = ld_stream<NT>(d.v + so);
-            vhi[u] = ld_stream<NT>(d.v + so + yoff);
-          }
-        }
-      }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (!on[u]) continue;
-        if (turn) rotate8(klo[u], khi[u], cs_row);
-        st_stream<NT>(d.k + dofs[u], klo[u]);
-        st_stream<NT>(d.k + dofs[u] + yoff, khi[u]);
-        if (do_v) {
-          st_stream<NT>(d.v + dofs[u], vlo[u]);
-          st_stream<NT>(d.v + dofs[u] + yoff, vhi[u]);
-        }
+        if (rot_plane) rotate8(lo[u], hi[u], cs_row);
+        st_stream<NT>(pool + dofs[u], lo[u]);
+        st_stream<NT>(pool + dofs[u] + yoff, hi[u]);
       }
+      i0 += NS * U;
+      if (i0 >= nsl) {
+        ++plane;
+        i0 = slot;
+      }
+      more = plane < pend && i0 < nsl;
+      if (more) issue();
     }
-#endif
   }
 }
 
-hipError_t launch_move(const Dev &d, int mode, int grid, hipStream_t st) {
-  const bool nt = AKV_MOVE_NT && d.RD == d.D;
-  const dim3 g(grid), b(kMoveThreads);
-  if (d.D == 128) {
-    if (nt) hipLaunchKernelGGL((move_kernel<128, true>), g, b, 0, st, d, mode);
-    else hipLaunchKernelGGL((move_kernel<128, false>), g, b, 0, st, d, mode);
+template <bool NT, bool OS>
+static void launch_move_shape(const Dev &d, int mode, dim3 g, int oneshot_cap, hipStream_t st) {
+  const dim3 b(kMoveThreads);
+  if (d.D == 128) hipLaunchKernelGGL((move_kernel<128, NT, OS>), g, b, 0, st, d, mode, oneshot_cap);
+  else hipLaunchKernelGGL((move_kernel<64, NT, OS>), g, b, 0, st, d, mode, oneshot_cap);
+}
+
+hipError_t launch_move(const Dev &d, int mode, int grid, int oneshot_cap, hipStream_t st) {
+  // one-shot launch first (oneshot_cap blocks), then the persistent grid;
+  // each checks the planned unit count and only one of them moves
+  if (AKV_MOVE_NT && d.RD == d.D) {
+    launch_move_shape<true, true>(d, mode, dim3(oneshot_cap), oneshot_cap, st);
+    launch_move_shape<true, false>(d, mode, dim3(grid), oneshot_cap, st);
   } else {
-    if (nt) hipLaunchKernelGGL((move_kernel<64, true>), g, b, 0, st, d, mode);
-    else hipLaunchKernelGGL((move_kernel<64, false>), g, b, 0, st, d, mode);
+    launch_move_shape<false, true>(d, mode, dim3(oneshot_cap), oneshot_cap, st);
+    launch_move_shape<false, false>(d, mode, dim3(grid), oneshot_cap, st);
   }
   return hipGetLastError();
 }
@@ -274,8 +282,8 @@ hipError_t launch_move(const Dev &d, int mode, int grid, hipStream_t st) {
 int move_blocks_per_cu(int D) {
   int n = 0;
   const hipError_t e = (D == 128)
-      ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, move_kernel<128, true>, kMoveThreads, 0)
-      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, move_kernel<64, true>, kMoveThreads, 0);
+      ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, move_kernel<128, true, false>, kMoveThreads, 0)
+      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, move_kernel<64, true, false>, kMoveThreads, 0);
   return (e == hipSuccess && n > 0) ? n : 2;
 }
 

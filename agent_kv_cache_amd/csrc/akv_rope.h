@@ -59,4 +59,48 @@ __device__ __forceinline__ void rotate8(u32x4 &lo, u32x4 &hi, const double2 *cs)
   hi = u32x4{bb[0], bb[1], bb[2], bb[3]};
 }
 
+
+// sin and cos of x = delta * theta_i in fp64, for |x| < 2^31 (|delta| < 2^31,
+// 0 <= theta_i <= 1).  Cody-Waite reduction by pi/2, with pi/2 split into
+// three 22-bit parts and a double tail so that k * part is exact for
+// |k| < 2^31, then the Taylor series of sin and cos on [-pi/4, pi/4] (terms
+// through r^19 and r^20; the first omitted term is below 1e-21) in Horner
+// form.  Short and free of table loads: the move computes it per page.
+__host__ __device__ inline void sincos_rope(double x, double *sn, double *cs) {
+  const double kTwoOverPi = 0x1.45f306dc9c883p-1;
+  const double kP1 = 0x1.921fb8p+0, kP2 = -0x1.5dde98p-23, kP3 = 0x1.846988p-48,
+               kP4 = 0x1.8cc51701b839ap-72;
+  const double k = rint(x * kTwoOverPi);
+  double r = fma(-k, kP1, x);
+  r = fma(-k, kP2, r);
+  r = fma(-k, kP3, r);
+  r = fma(-k, kP4, r);
+  const double z = r * r;
+  // 1/n! for odd n = 3..19 (sin) and even n = 2..20 (cos)
+  double ps = -0x1.2f49b46814157p-57;              // -1/19!
+  ps = fma(ps, z, 0x1.952c77030ad4ap-49);          //  1/17!
+  ps = fma(ps, z, -0x1.ae7f3e733b81fp-41);         // -1/15!
+  ps = fma(ps, z, 0x1.6124613a86d09p-33);          //  1/13!
+  ps = fma(ps, z, -0x1.ae64567f544e4p-26);         // -1/11!
+  ps = fma(ps, z, 0x1.71de3a556c734p-19);          //  1/9!
+  ps = fma(ps, z, -0x1.a01a01a01a01ap-13);         // -1/7!
+  ps = fma(ps, z, 0x1.1111111111111p-7);           //  1/5!
+  ps = fma(ps, z, -0x1.5555555555555p-3);          // -1/3!
+  const double s = fma(ps * z, r, r);
+  double pc = 0x1.e542ba4020225p-62;               //  1/20!
+  pc = fma(pc, z, -0x1.6827863b97d97p-53);         // -1/18!
+  pc = fma(pc, z, 0x1.ae7f3e733b81fp-45);          //  1/16!
+  pc = fma(pc, z, -0x1.93974a8c07c9dp-37);         // -1/14!
+  pc = fma(pc, z, 0x1.1eed8eff8d898p-29);          //  1/12!
+  pc = fma(pc, z, -0x1.27e4fb7789f5cp-22);         // -1/10!
+  pc = fma(pc, z, 0x1.a01a01a01a01ap-16);          //  1/8!
+  pc = fma(pc, z, -0x1.6c16c16c16c17p-10);         // -1/6!
+  pc = fma(pc, z, 0x1.5555555555555p-5);           //  1/4!
+  pc = fma(pc, z, -0x1.0p-1);                      // -1/2!
+  const double c = fma(pc, z, 1.0);
+  const int q = (int)((long long)k & 3);
+  *sn = (q == 0) ? s : (q == 1) ? c : (q == 2) ? -s : -c;
+  *cs = (q == 0) ? c : (q == 1) ? -s : (q == 2) ? -c : s;
+}
+
 }  // namespace akv

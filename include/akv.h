@@ -76,7 +76,7 @@ typedef struct {
   int32_t n_blocks;           /* NB pages in the pool, >= 1 */
   int32_t n_seqs;             /* B sequences, >= 1 */
   int32_t max_blocks_per_seq; /* page-table row length, >= 1 */
-  double rope_base;           /* theta_i = rope_base^(-2i/r), NeoX half split over the r rotary dims */
+  double rope_base;           /* >= 1; theta_i = rope_base^(-2i/r), NeoX half split over the r rotary dims */
   uint16_t *k_pool;           /* bf16 [L][NB][Hkv][16][d] */
   uint16_t *v_pool;           /* bf16 [L][NB][Hkv][16][d] */
   int32_t *block_table;       /* [B][max_blocks_per_seq] */
@@ -95,7 +95,7 @@ typedef struct {
   int32_t rotary_dim;         /* r: 0 = head_dim, else a multiple of 16 in [16, d]; pairs
                                  (i, i + r/2) are rotated, dims [r, d) are copied */
   const double *inv_freq;     /* HOST [r/2] frequencies theta_i (e.g. a Llama 3.1 or YaRN
-                                 table), finite and >= 0; NULL = rope_base^(-2i/r); copied */
+                                 table), in [0, 1]; NULL = rope_base^(-2i/r); copied */
   const int32_t *layer_window;/* HOST [L] sliding-window length per layer, >= 0, 0 = full
                                  attention; NULL = all full; copied.  A query at position P
                                  reads the entries whose position is >= P - W + 1 */

@@ -47,7 +47,8 @@ def test_scratch_size_formula():
 @pytest.mark.parametrize("field,value", [
     ("head_dim", 96), ("head_dim", 256), ("block_size", 32), ("n_layers", 0),
     ("n_kv_heads", 0), ("n_blocks", 0), ("n_seqs", 0), ("max_blocks_per_seq", 0),
-    ("rope_base", 0.0), ("rope_base", float("inf")), ("k_pool", None), ("scratch", None),
+    ("rope_base", 0.0), ("rope_base", 0.5), ("rope_base", float("inf")), ("k_pool", None),
+    ("scratch", None),
     ("scratch", 4096 + 8), ("scratch_bytes", 16), ("k_pool", 4096 + 2),
 ])
 def test_init_rejects_bad_descriptors(field, value):
@@ -64,6 +65,7 @@ def test_init_rejects_bad_descriptors(field, value):
     (-16, None, None),
     (64, [1.0] * 31 + [float("nan")], None),
     (64, [1.0] * 31 + [-1.0], None),
+    (64, [1.0] * 31 + [1.5], None),       # frequencies above 1
     (0, None, [0, -1]),                   # negative window
 ])
 def test_init_rejects_bad_rope_variants(rotary_dim, freq, window):
