@@ -2,6 +2,7 @@
 // include/akv.h and optional per-kernel event timing.
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -221,8 +222,9 @@ akv_status akv_cache_init(const akv_cache_desc *d, akv_cache **out) {
     const long long pages = std::min<long long>(d->n_blocks,
                                                 (long long)d->n_seqs * d->max_blocks_per_seq);
     const long long parts = AKV_MOVE_OS_PLANES * AKV_MOVE_OS_HEAD_GROUPS;
-    c->oneshot_cap =
-        (int)std::max(1LL, std::min<long long>(pages * d->n_layers * parts, AKV_MOVE_ONESHOT_CAP));
+    long long cap = AKV_MOVE_ONESHOT_CAP;
+    if (const char *e = getenv("AKV_MOVE_ONESHOT_CAP")) cap = std::max(0LL, atoll(e));
+    c->oneshot_cap = (int)std::max(1LL, std::min<long long>(pages * d->n_layers * parts, cap));
   }
   c->attn_per_cu = akv::attn_blocks_per_cu(d->head_dim);
 

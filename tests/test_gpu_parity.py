@@ -198,6 +198,40 @@ def test_fused_equals_sequential_bitwise():
     assert np.array_equal(a.next_pos.cpu().numpy(), b.next_pos.cpu().numpy())
 
 
+def test_move_launch_shapes_agree_bitwise(monkeypatch):
+    """The one-shot and the persistent move grid give identical bytes: the
+    same ops on two identically filled caches, the second with the one-shot
+    grid switched off (AKV_MOVE_ONESHOT_CAP=0, read at cache creation)."""
+    sh = W.Shape(3, 2, 128, 8, 5.0e5)
+    lens = [700, 45, 1000, 0]
+    rng = np.random.default_rng(17)
+    masks = [(rng.uniform(size=n) < 0.35).astype(np.uint8) for n in lens]
+    say("case one-shot vs persistent move grid")
+    a = _setup(sh, lens, seed=5, extra=2 * sum(Hn.pages_for(n) for n in lens) + 8, order_seed=6)
+    monkeypatch.setenv("AKV_MOVE_ONESHOT_CAP", "0")
+    b = _setup(sh, lens, seed=5, extra=2 * sum(Hn.pages_for(n) for n in lens) + 8, order_seed=6)
+    monkeypatch.delenv("AKV_MOVE_ONESHOT_CAP")
+    for c in (a, b):
+        c.drop_reposition(Hn.mask_tensor(c, masks))
+        # every entry to its own gapped position: every row a different delta
+        newp = [np.arange(int(n)) * 7 + 3 + 11 * s for s, n in enumerate(c.seq_lens.cpu().numpy())]
+        c.reposition(None, Hn.pos_tensor(c, newp))
+        c.drop(Hn.mask_tensor(c, [np.zeros(int(n), np.uint8) if s != 2 else
+                                  (np.arange(int(n)) % 5 == 1).astype(np.uint8)
+                                  for s, n in enumerate(c.seq_lens.cpu().numpy())]))
+        c.fork([3, -1, -1, -1], None, reposition=True)
+        assert c.sync_status() == 0
+    for s in range(len(lens)):
+        ta, pa, _ = a.seq_state(s)
+        tb, pb, _ = b.seq_state(s)
+        assert np.array_equal(ta, tb) and np.array_equal(pa, pb), s
+        for l in range(sh.n_layers):
+            assert np.array_equal(bits(a.gather_rows(s, l, "k")), bits(b.gather_rows(s, l, "k"))), (s, l)
+            assert np.array_equal(bits(a.gather_rows(s, l, "v")), bits(b.gather_rows(s, l, "v"))), (s, l)
+    assert np.array_equal(a.next_pos.cpu().numpy(), b.next_pos.cpu().numpy())
+    assert np.array_equal(a.seq_lens.cpu().numpy(), b.seq_lens.cpu().numpy())
+
+
 def test_identity_reposition_is_bitwise_copy():
     sh = W.Shape(2, 2, 128, 4, 5.0e5)
     lens = [100, 33]
