@@ -20,7 +20,7 @@ struct akv_cache {
   int device = 0;
   int n_cu = 256;
   int move_grid = 2048;
-  int oneshot_cap = 1;     // units (page x layer) of the largest op moved by the one-shot launch
+  int oneshot_cap = 1;     // blocks of the one-shot move launch (the largest op it moves)
   int attn_per_cu = 2;
   int n_full_layers = 0;   // layers without a sliding window
   bool profile = false;
@@ -222,9 +222,11 @@ akv_status akv_cache_init(const akv_cache_desc *d, akv_cache **out) {
     const long long pages = std::min<long long>(d->n_blocks,
                                                 (long long)d->n_seqs * d->max_blocks_per_seq);
     const long long parts = AKV_MOVE_OS_PLANES * AKV_MOVE_OS_HEAD_GROUPS;
+    const int lpb = AKV_MOVE_OS_LAYERS > 0 ? AKV_MOVE_OS_LAYERS : (d->head_dim == 128 ? 1 : 2);
+    const long long groups = (d->n_layers + lpb - 1) / lpb;
     long long cap = AKV_MOVE_ONESHOT_CAP;
     if (const char *e = getenv("AKV_MOVE_ONESHOT_CAP")) cap = std::max(0LL, atoll(e));
-    c->oneshot_cap = (int)std::max(1LL, std::min<long long>(pages * d->n_layers * parts, cap));
+    c->oneshot_cap = (int)std::max(1LL, std::min<long long>(pages * groups * parts, cap));
   }
   c->attn_per_cu = akv::attn_blocks_per_cu(d->head_dim);
 

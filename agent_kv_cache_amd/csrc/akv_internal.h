@@ -60,6 +60,10 @@ enum SeqInfo : int {
 #ifndef AKV_MOVE_OS_HEAD_GROUPS
 #define AKV_MOVE_OS_HEAD_GROUPS 1
 #endif
+// Layers per one-shot block (0: 1 at head_dim 128, 2 at 64).
+#ifndef AKV_MOVE_OS_LAYERS
+#define AKV_MOVE_OS_LAYERS 0
+#endif
 
 // Mode bits of the compaction plan.
 enum Mode : int {

@@ -41,11 +41,12 @@ constexpr int kMoveThreads = 256;
 
 // Streaming 16-B accesses: every KV byte of a move is read once and written
 // once, so they bypass cache retention (nontemporal hint) -- when each load
-// instruction covers whole 128-B lines.  With partial RoPE a row's x and y
-// chunks are two 64-B pieces per instruction; the other half of each line is
-// touched by the next instruction, and with the hint it is fetched again, so
-// those moves use ordinary cached accesses (measured 1.05 -> 0.89 ms on the
-// Llama-8B-shaped drop with r = 64).
+// instruction covers whole 128-B lines, i.e. full RoPE at d = 128.  Otherwise
+// (partial RoPE, or d = 64 where a half row is 64 B) a row's x and y chunks
+// are two 64-B pieces per instruction; the other half of each line is touched
+// by the next instruction, and with the hint it is fetched again, so those
+// moves use ordinary cached accesses (measured: Llama-8B-shaped drop with
+// r = 64 1.05 -> 0.89 ms; the d = 64 history ops 4.0 -> 4.17 TB/s).
 template <bool NT>
 __device__ __forceinline__ u32x4 ld_stream(const uint16_t *p) {
   if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
@@ -90,16 +91,22 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
   // b / (P pages) -- so the blocks in flight cover a compact address range.
   // A larger op runs in the persistent launch (contiguous unit ranges).
   constexpr int HGN = AKV_MOVE_OS_HEAD_GROUPS, PARTS = AKV_MOVE_OS_PLANES * HGN;
-  if ((units * PARTS <= oneshot_cap) != ONESHOT) return;
+  // one-shot blocks move LPB consecutive layers of a page (64 KiB of K+V
+  // read per block at the Llama-8B shape, whatever the head size)
+  constexpr int LPB = AKV_MOVE_OS_LAYERS > 0 ? AKV_MOVE_OS_LAYERS : (D == 128 ? 1 : 2);
+  const long long ngroups = (d.L + LPB - 1) / LPB;
+  const long long os_blocks = npages * ngroups * PARTS;
+  if ((os_blocks <= oneshot_cap) != ONESHOT) return;
   long long u0, u1;
   int p_lo = 0, p_hi = 2, h_lo = 0, h_hi = d.H;
   bool first_part = true;   // the part that moves positions / token ids
   if (ONESHOT) {
-    if (blockIdx.x >= units * PARTS) return;
+    if (blockIdx.x >= os_blocks) return;
     const long long ub = blockIdx.x / PARTS;
     const int part = (int)(blockIdx.x - ub * PARTS);
-    u0 = (ub % npages) * d.L + ub / npages;
-    u1 = u0 + 1;
+    const long long pg = ub % npages, lg = ub / npages;
+    u0 = pg * d.L + lg * LPB;
+    u1 = min(u0 + LPB, (pg + 1) * d.L);
     if (AKV_MOVE_OS_PLANES == 2) {
       p_lo = part / HGN;
       p_hi = p_lo + 1;
@@ -269,7 +276,7 @@ static void launch_move_shape(const Dev &d, int mode, dim3 g, int oneshot_cap, h
 hipError_t launch_move(const Dev &d, int mode, int grid, int oneshot_cap, hipStream_t st) {
   // one-shot launch first (oneshot_cap blocks), then the persistent grid;
   // each checks the planned unit count and only one of them moves
-  if (AKV_MOVE_NT && d.RD == d.D) {
+  if (AKV_MOVE_NT && d.RD == d.D && d.D == 128) {
     launch_move_shape<true, true>(d, mode, dim3(oneshot_cap), oneshot_cap, st);
     launch_move_shape<true, false>(d, mode, dim3(grid), oneshot_cap, st);
   } else {
