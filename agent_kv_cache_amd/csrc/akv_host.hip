@@ -215,18 +215,17 @@ akv_status akv_cache_init(const akv_cache_desc *d, akv_cache **out) {
   }
   c->move_grid = akv::move_blocks_per_cu(d->head_dim) * c->n_cu;
   {
-    // One-shot launch size: every block the op could need (parts of each
-    // (page, layer) unit it could rebuild), at most AKV_MOVE_ONESHOT_CAP
+    // One-shot launch size: every block the op could need (one per layer
+    // group of each page it could rebuild), at most AKV_MOVE_ONESHOT_CAP
     // blocks; blocks past the planned count exit at once and a larger op runs
     // on the persistent grid.
     const long long pages = std::min<long long>(d->n_blocks,
                                                 (long long)d->n_seqs * d->max_blocks_per_seq);
-    const long long parts = AKV_MOVE_OS_PLANES * AKV_MOVE_OS_HEAD_GROUPS;
     const int lpb = AKV_MOVE_OS_LAYERS > 0 ? AKV_MOVE_OS_LAYERS : (d->head_dim == 128 ? 1 : 2);
     const long long groups = (d->n_layers + lpb - 1) / lpb;
     long long cap = AKV_MOVE_ONESHOT_CAP;
     if (const char *e = getenv("AKV_MOVE_ONESHOT_CAP")) cap = std::max(0LL, atoll(e));
-    c->oneshot_cap = (int)std::max(1LL, std::min<long long>(pages * groups * parts, cap));
+    c->oneshot_cap = (int)std::max(1LL, std::min<long long>(pages * groups, cap));
   }
   c->attn_per_cu = akv::attn_blocks_per_cu(d->head_dim);
 

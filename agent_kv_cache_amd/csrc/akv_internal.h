@@ -47,18 +47,11 @@ enum SeqInfo : int {
   kSeqInfo = 16
 };
 
-// Ops that rebuild at most this many (page, layer) units are moved by a
-// one-shot grid (one block per unit), larger ones by a persistent grid.
+// Ops that need at most this many one-shot blocks (one per layer group of
+// each rebuilt page) are moved by a one-shot grid, larger ones by a
+// persistent grid.
 #ifndef AKV_MOVE_ONESHOT_CAP
 #define AKV_MOVE_ONESHOT_CAP 131072
-#endif
-// One-shot blocks per (page, layer) unit: planes (1: K and V in one block,
-// 2: one block each) times head groups.
-#ifndef AKV_MOVE_OS_PLANES
-#define AKV_MOVE_OS_PLANES 1
-#endif
-#ifndef AKV_MOVE_OS_HEAD_GROUPS
-#define AKV_MOVE_OS_HEAD_GROUPS 1
 #endif
 // Layers per one-shot block (0: 1 at head_dim 128, 2 at 64).
 #ifndef AKV_MOVE_OS_LAYERS

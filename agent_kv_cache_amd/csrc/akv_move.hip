@@ -85,42 +85,27 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
   const int fc_old = d.ctl[CTL_FC_OLD];
   const long long units = npages * d.L;
   // Two launches share the work.  An op of at most oneshot_cap blocks runs in
-  // the one-shot launch: one block per part of a (page, layer) unit (parts:
-  // the K and V planes, each split into head groups), in layer-major order --
-  // block b moves part b mod P of page (b / P) mod pages at layer
-  // b / (P pages) -- so the blocks in flight cover a compact address range.
-  // A larger op runs in the persistent launch (contiguous unit ranges).
-  constexpr int HGN = AKV_MOVE_OS_HEAD_GROUPS, PARTS = AKV_MOVE_OS_PLANES * HGN;
-  // one-shot blocks move LPB consecutive layers of a page (64 KiB of K+V
-  // read per block at the Llama-8B shape, whatever the head size)
+  // the one-shot launch: one block per LPB layers of a page, in layer-major
+  // order -- block b moves page b mod pages at layer group b / pages -- so
+  // the blocks in flight cover a compact address range.  A larger op runs in
+  // the persistent launch (contiguous unit ranges).  One-shot blocks move
+  // LPB consecutive layers (64 KiB of K+V read per block at the Llama-8B
+  // shape, whatever the head size; blocks per (page, layer, plane) or per
+  // head group were measured slower: each repeats the per-page set-up).
   constexpr int LPB = AKV_MOVE_OS_LAYERS > 0 ? AKV_MOVE_OS_LAYERS : (D == 128 ? 1 : 2);
   const long long ngroups = (d.L + LPB - 1) / LPB;
-  const long long os_blocks = npages * ngroups * PARTS;
+  const long long os_blocks = npages * ngroups;
   if ((os_blocks <= oneshot_cap) != ONESHOT) return;
   long long u0, u1;
-  int p_lo = 0, p_hi = 2, h_lo = 0, h_hi = d.H;
-  bool first_part = true;   // the part that moves positions / token ids
   if (ONESHOT) {
     if (blockIdx.x >= os_blocks) return;
-    const long long ub = blockIdx.x / PARTS;
-    const int part = (int)(blockIdx.x - ub * PARTS);
-    const long long pg = ub % npages, lg = ub / npages;
+    const long long pg = blockIdx.x % npages, lg = blockIdx.x / npages;
     u0 = pg * d.L + lg * LPB;
     u1 = min(u0 + LPB, (pg + 1) * d.L);
-    if (AKV_MOVE_OS_PLANES == 2) {
-      p_lo = part / HGN;
-      p_hi = p_lo + 1;
-    }
-    const int hg = part % HGN, hper = (d.H + HGN - 1) / HGN;
-    h_lo = min(d.H, hg * hper);
-    h_hi = min(d.H, h_lo + hper);
-    first_part = part == 0;
-    if (h_lo >= h_hi) return;
   } else {
     u0 = units * blockIdx.x / gridDim.x;
     u1 = units * (blockIdx.x + 1) / gridDim.x;
   }
-  const int nh = h_hi - h_lo;
   const int t = threadIdx.x;
   const int r = (t % TPH) / CH, pc = t % CH, slot = t / TPH;
   // Chunk pc of a row: a rotary chunk pairs dims [8pc, 8pc+8) with the same
@@ -169,9 +154,9 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
       if (t == 0) {
         s_dst = dst;
         s_mv = mv;
-        if (mv && l0 == 0 && first_part) d.stage[pg] = dst;
+        if (mv && l0 == 0) d.stage[pg] = dst;
       }
-      if (l0 == 0 && first_part) {
+      if (l0 == 0) {
         const size_t dn = (size_t)dst * kPage + t;
         if (mv) {
           d.pos[dn] = valid ? d.pos[src] + delta : -1;
@@ -201,15 +186,15 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
     const int delta = s_delta[r];
     const bool turn = valid && delta != 0 && rot_chunk;
     const bool do_k = valid ? (mv || turn) : mv;
-    const int pend = min(p_hi, mv ? 2 : 1);   // planes: K, and V when the page moves
-    const int nsl = (l1 - l0) * nh;
+    const int pend = mv ? 2 : 1;   // planes: K, and V when the page moves
+    const int nsl = (l1 - l0) * d.H;
     const int sp = s_src[r];
     const size_t src_row = (size_t)(sp >> 4) * ps.page + (size_t)(sp & 15) * D + xo;
     const size_t dst_row = (size_t)dst * ps.page + (size_t)r * D + xo;
     // Batches of U slices; K slices of the unit range first, then V slices
     // (each pass streams one pool).  The first batch is loaded before the
     // cos/sin set-up so that its latency covers the set-up.
-    int plane = p_lo, i0 = slot;
+    int plane = 0, i0 = slot;
     bool more = do_k && plane < pend && i0 < nsl;
     u32x4 lo[U], hi[U];
     size_t dofs[U];
@@ -220,7 +205,7 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
       for (int u = 0; u < U; ++u) {
         const int idx = i0 + u * NS;
         on[u] = idx < nsl;
-        const int l = l0 + idx / nh, h = h_lo + idx % nh;
+        const int l = l0 + idx / d.H, h = idx % d.H;
         const size_t off = (size_t)l * lstride + (size_t)h * hstride;
         dofs[u] = dst_row + off;
         lo[u] = hi[u] = u32x4{0u, 0u, 0u, 0u};
@@ -231,7 +216,7 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
       }
     };
     if (more) issue();
-    if (rot_any && p_lo == 0) {   // blocks that move only V need no cos/sin
+    if (rot_any) {
       const int RH = d.RD / 2;
       const int ntask = s_nrep * RH;
       for (int task = t; task < ntask; task += kMoveThreads) {
