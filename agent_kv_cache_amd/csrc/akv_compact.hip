@@ -422,11 +422,30 @@ __global__ __launch_bounds__(kPlanThreads) void append_plan_kernel(Dev d, const 
 }
 
 // One workgroup per new token: copies its K/V rows of every (layer, head)
-// with 16-B accesses and writes its position and token id.  With ROPE the
+// with 16-B accesses (a batch of loads issued before their stores) and
+// writes its position and token id.  With ROPE the
 // keys arrive unrotated and are turned to the token's position p on the way
 // (the model's RoPE step fused into the append): cos/sin of p * theta_i in
 // fp64 once per token in LDS, each rotary chunk pair rotated in fp64 and
 // rounded once, the non-rotary tail copied.
+#ifndef AKV_APPEND_BATCH
+#define AKV_APPEND_BATCH 4
+#endif
+constexpr int kAppendBatch = AKV_APPEND_BATCH;   // 16-B chunks loaded before they are stored
+
+// Inputs are read once and the pages written once: streamed with the
+// nontemporal hint where every access instruction covers whole 128-B lines.
+template <bool NT>
+__device__ __forceinline__ u32x4 ld_once(const uint16_t *p) {
+  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  else return *reinterpret_cast<const u32x4 *>(p);
+}
+template <bool NT>
+__device__ __forceinline__ void st_once(uint16_t *p, u32x4 v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
+  else *reinterpret_cast<u32x4 *>(p) = v;
+}
+
 template <int D, bool ROPE>
 __global__ __launch_bounds__(256) void append_copy_kernel(Dev d, int64_t n_new,
                                                           const uint16_t *__restrict__ k_new,
@@ -466,32 +485,61 @@ __global__ __launch_bounds__(256) void append_copy_kernel(Dev d, int64_t n_new,
     }
     __syncthreads();
     constexpr int CH = D / 16;                 // chunk pairs per row
+    // a chunk pair's x and y halves are whole 128-B lines only at d = 128
+    constexpr bool NTP = D == 128;
     const int rch = d.RD / 16;
     const int npair = d.L * d.H * CH;
-    for (int c = threadIdx.x; c < npair; c += blockDim.x) {
-      const int pc = c % CH, lh = c / CH, h = lh % d.H, l = lh / d.H;
-      const bool rot = pc < rch;
-      const int xo = rot ? 8 * pc : d.RD + 8 * (pc - rch);
-      const int yoff = rot ? d.RD / 2 : (D - d.RD) / 2;
-      const size_t src = (((size_t)l * n_new + tk) * d.H + h) * D + xo;
-      const size_t dst = (size_t)l * ps.layer + (size_t)page * ps.page + (size_t)h * ps.head +
-                         (size_t)row * D + xo;
-      u32x4 x = *reinterpret_cast<const u32x4 *>(k_new + src);
-      u32x4 y = *reinterpret_cast<const u32x4 *>(k_new + src + yoff);
-      if (rot && pos != 0) rotate8(x, y, &s_cs[8 * pc]);
-      *reinterpret_cast<u32x4 *>(d.k + dst) = x;
-      *reinterpret_cast<u32x4 *>(d.k + dst + yoff) = y;
+    // batches of kAppendBatch chunk pairs: every load of a batch is issued
+    // before its stores
+    for (int c0 = threadIdx.x; c0 < npair; c0 += blockDim.x * kAppendBatch) {
+      u32x4 x[kAppendBatch], y[kAppendBatch];
+      size_t dst[kAppendBatch];
+      int yo[kAppendBatch], pcs[kAppendBatch];
+#pragma unroll
+      for (int u = 0; u < kAppendBatch; ++u) {
+        const int c = c0 + u * blockDim.x;
+        if (c >= npair) continue;
+        const int pc = c % CH, lh = c / CH, h = lh % d.H, l = lh / d.H;
+        const bool rot = pc < rch;
+        const int xo = rot ? 8 * pc : d.RD + 8 * (pc - rch);
+        yo[u] = rot ? d.RD / 2 : (D - d.RD) / 2;
+        pcs[u] = pc;
+        const size_t src = (((size_t)l * n_new + tk) * d.H + h) * D + xo;
+        dst[u] = (size_t)l * ps.layer + (size_t)page * ps.page + (size_t)h * ps.head +
+                 (size_t)row * D + xo;
+        x[u] = ld_once<NTP>(k_new + src);
+        y[u] = ld_once<NTP>(k_new + src + yo[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < kAppendBatch; ++u) {
+        if (c0 + u * (int)blockDim.x >= npair) continue;
+        if (pcs[u] < rch && pos != 0) rotate8(x[u], y[u], &s_cs[8 * pcs[u]]);
+        st_once<NTP>(d.k + dst[u], x[u]);
+        st_once<NTP>(d.k + dst[u] + yo[u], y[u]);
+      }
     }
   }
   const int nchunk = d.L * d.H * C8;
-  for (int c = threadIdx.x; c < nchunk; c += blockDim.x) {
-    const int e8 = c % C8, lh = c / C8, h = lh % d.H, l = lh / d.H;
-    const size_t src = (((size_t)l * n_new + tk) * d.H + h) * D + 8 * e8;
-    const size_t dst = (size_t)l * ps.layer + (size_t)page * ps.page + (size_t)h * ps.head +
-                       (size_t)row * D + 8 * e8;
-    if constexpr (!ROPE)
-      *reinterpret_cast<uint4 *>(d.k + dst) = *reinterpret_cast<const uint4 *>(k_new + src);
-    *reinterpret_cast<uint4 *>(d.v + dst) = *reinterpret_cast<const uint4 *>(v_new + src);
+  for (int c0 = threadIdx.x; c0 < nchunk; c0 += blockDim.x * kAppendBatch) {
+    u32x4 kk[kAppendBatch], vv[kAppendBatch];
+    size_t dst[kAppendBatch];
+#pragma unroll
+    for (int u = 0; u < kAppendBatch; ++u) {
+      const int c = c0 + u * blockDim.x;
+      if (c >= nchunk) continue;
+      const int e8 = c % C8, lh = c / C8, h = lh % d.H, l = lh / d.H;
+      const size_t src = (((size_t)l * n_new + tk) * d.H + h) * D + 8 * e8;
+      dst[u] = (size_t)l * ps.layer + (size_t)page * ps.page + (size_t)h * ps.head +
+               (size_t)row * D + 8 * e8;
+      if constexpr (!ROPE) kk[u] = ld_once<true>(k_new + src);
+      vv[u] = ld_once<true>(v_new + src);
+    }
+#pragma unroll
+    for (int u = 0; u < kAppendBatch; ++u) {
+      if (c0 + u * (int)blockDim.x >= nchunk) continue;
+      if constexpr (!ROPE) st_once<true>(d.k + dst[u], kk[u]);
+      st_once<true>(d.v + dst[u], vv[u]);
+    }
   }
 }
 
