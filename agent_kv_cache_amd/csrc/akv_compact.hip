@@ -62,11 +62,12 @@ __device__ __forceinline__ int block_exclusive_scan(int x, int *wave_tmp, int *t
 // ---------------------------------------------------------------------------
 // A sequence's pages are cut into chunks of kChunkPages pages, one 256-thread
 // workgroup per (chunk, sequence) and one page per thread, so a long sequence
-// is planned by many CUs.  plan_count: keep counts and the first dropped slot
-// of every chunk.  plan_write: the chunk's first survivor rank (sum of the
-// earlier chunks' counts), an in-chunk prefix sum, the gather map src[j]
-// (physical slot) and the rotation delta q_j - p, staged in LDS and written
-// coalesced; the last workgroup finalizes every sequence and the op.
+// is planned by many CUs, in one launch.  Each workgroup recounts the keep
+// bits of its sequence's earlier chunks (the survivor rank of its first page),
+// takes an in-chunk prefix sum, and writes the gather map src[j] (physical
+// slot) and the rotation delta q_j - p, staged in LDS and written coalesced,
+// plus its chunk's keep count and first dropped slot; the last workgroup
+// finalizes every sequence and the op.
 constexpr int kChunkPages = kPlanChunkPages;
 
 __device__ __forceinline__ unsigned page_drop_bits(const uint4 m) {
@@ -84,42 +85,11 @@ __device__ __forceinline__ unsigned page_valid_bits(int len, int pg) {
   return nvalid >= kPage ? 0xFFFFu : (nvalid <= 0 ? 0u : ((1u << nvalid) - 1u));
 }
 
-__global__ __launch_bounds__(kChunkPages) void plan_count_kernel(Dev d, const uint8_t *__restrict__ mask,
-                                                                 int mode) {
-  __shared__ int s_wave[kChunkPages / 64 + 1];
-  __shared__ int s_fdrop;
-  const int c = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
-  // in fork mode only sources with a destination take part
-  const int len = ((mode & M_FORK) && d.fork_dst[b] < 0) ? 0 : d.lens[b];
-  const int pg = c * kChunkPages + t;
-  if (t == 0) s_fdrop = INT_MAX;
-  __syncthreads();
-  unsigned keep = page_valid_bits(len, pg);
-  if (keep && (mode & M_DROP)) {
-    const unsigned dropbits =
-        page_drop_bits(*reinterpret_cast<const uint4 *>(mask + (size_t)b * d.S + (size_t)pg * kPage)) & keep;
-    keep &= ~dropbits;
-    if (dropbits) atomicMin(&s_fdrop, pg * kPage + __ffs(dropbits) - 1);
-  }
-  int total;
-  block_exclusive_scan<kChunkPages>(__popc(keep), s_wave, &total);
-  if (t == 0) {
-    int *ci = d.chunk_info + ((size_t)b * d.nchunk + c) * 2;
-    ci[0] = total;
-    ci[1] = s_fdrop;
-    if (c == 0) {
-      int *si = d.seq_info + (size_t)b * kSeqInfo;
-      si[SI_FPOS] = INT_MAX;
-      si[SI_ERR] = 0;
-    }
-  }
-}
-
-__global__ __launch_bounds__(kChunkPages) void plan_write_kernel(
+__global__ __launch_bounds__(kChunkPages) void plan_kernel(
     Dev d, const uint8_t *__restrict__ mask, const int32_t *__restrict__ new_pos,
     const int32_t *__restrict__ old_pos, int mode) {
   __shared__ int s_wave[kChunkPages / 64 + 1];
-  __shared__ int s_base, s_last, s_gerr;
+  __shared__ int s_last, s_gerr, s_fdrop;
   __shared__ int s_src[kChunkPages * kPage], s_dlt[kChunkPages * kPage];
   const int c = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
   const size_t S = (size_t)d.S;
@@ -147,18 +117,31 @@ __global__ __launch_bounds__(kChunkPages) void plan_write_kernel(
         }
       }
     }
-    // survivor rank of the chunk's first page: earlier chunks' counts
-    if (t < 64) {
-      int acc = 0;
-      for (int cc = t; cc < c; cc += 64) acc += d.chunk_info[((size_t)b * d.nchunk + cc) * 2];
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
-      if (t == 0) s_base = acc;
+    // survivor rank of the chunk's first page: the keep bits of the
+    // sequence's earlier chunks, recounted (one page per thread per chunk)
+    int acc = 0;
+    for (int cc = 0; cc < c; ++cc) {
+      const int pq = cc * kChunkPages + t;
+      unsigned kq = page_valid_bits(len, pq);
+      if (kq && (mode & M_DROP))
+        kq &= ~page_drop_bits(*reinterpret_cast<const uint4 *>(mask + b * S + (size_t)pq * kPage));
+      acc += __popc(kq);
     }
-    if (keep && (mode & M_DROP)) keep &= ~page_drop_bits(m);
+    if (t == 0) s_fdrop = INT_MAX;
+    int base;
+    block_exclusive_scan<kChunkPages>(acc, s_wave, &base);
+    if (keep && (mode & M_DROP)) {
+      const unsigned dropbits = page_drop_bits(m) & keep;
+      keep &= ~dropbits;
+      if (dropbits) atomicMin(&s_fdrop, pg * kPage + __ffs(dropbits) - 1);
+    }
     int total;
     const int excl = block_exclusive_scan<kChunkPages>(__popc(keep), s_wave, &total);
-    const int base = s_base;
+    if (t == 0) {
+      int *ci = d.chunk_info + ((size_t)b * d.nchunk + c) * 2;
+      ci[0] = total;
+      ci[1] = s_fdrop;
+    }
     int err = 0, fpos = INT_MAX;
     if (keep) {
       const int j0 = base + excl;
@@ -241,6 +224,9 @@ __global__ __launch_bounds__(kChunkPages) void plan_write_kernel(
       }
       const int fpos = nch ? __atomic_load_n(&si[SI_FPOS], __ATOMIC_RELAXED) : INT_MAX;
       const int e = nch ? __atomic_load_n(&si[SI_ERR], __ATOMIC_RELAXED) : 0;
+      // re-armed for the next op (the workgroups of a plan only lower / raise them)
+      si[SI_FPOS] = INT_MAX;
+      si[SI_ERR] = 0;
       const int Pn = (rnew + kPage - 1) / kPage;
       int fbd = P0;
       int ee = e;
@@ -586,6 +572,8 @@ __global__ void reset_kernel(Dev d, const int32_t *order) {
   if (i < d.B) {
     d.lens[i] = 0;
     d.next_pos[i] = 0;
+    d.seq_info[i * kSeqInfo + SI_FPOS] = INT_MAX;   // plan accumulators, re-armed by every plan
+    d.seq_info[i * kSeqInfo + SI_ERR] = 0;
   }
   if (i < d.NB) d.free_stack[d.NB - 1 - i] = order ? order[i] : (int)i;
   if (i == 0) {
@@ -600,11 +588,7 @@ __global__ void reset_kernel(Dev d, const int32_t *order) {
 hipError_t launch_plan(const Dev &d, const uint8_t *mask, const int32_t *new_pos,
                        const int32_t *old_pos, int mode, hipStream_t st) {
   const dim3 grid(d.nchunk, d.B);
-  hipLaunchKernelGGL(plan_count_kernel, grid, dim3(kChunkPages), 0, st, d, mask, mode);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(plan_write_kernel, grid, dim3(kChunkPages), 0, st, d, mask, new_pos, old_pos,
-                     mode);
+  hipLaunchKernelGGL(plan_kernel, grid, dim3(kChunkPages), 0, st, d, mask, new_pos, old_pos, mode);
   return hipGetLastError();
 }
 

@@ -21,6 +21,7 @@ struct akv_cache {
   int n_cu = 256;
   int move_grid = 2048;
   int oneshot_cap = 1;     // blocks of the one-shot move launch (the largest op it moves)
+  bool move_persistent = true;   // some op could be too large for the one-shot launch
   int attn_per_cu = 2;
   int n_full_layers = 0;   // layers without a sliding window
   bool profile = false;
@@ -116,7 +117,8 @@ akv_status run_compaction(akv_cache *c, const uint8_t *mask, const int32_t *new_
   }
   {
     Timed tm(c, AKV_KERNEL_MOVE, st);
-    AKV_HIP(akv::launch_move(c->dev, mode, c->move_grid, c->oneshot_cap, st));
+    AKV_HIP(akv::launch_move(c->dev, mode, c->move_persistent ? c->move_grid : 0,
+                             c->oneshot_cap, st));
   }
   {
     Timed tm(c, AKV_KERNEL_COMMIT, st);
@@ -226,6 +228,7 @@ akv_status akv_cache_init(const akv_cache_desc *d, akv_cache **out) {
     long long cap = AKV_MOVE_ONESHOT_CAP;
     if (const char *e = getenv("AKV_MOVE_ONESHOT_CAP")) cap = std::max(0LL, atoll(e));
     c->oneshot_cap = (int)std::max(1LL, std::min<long long>(pages * groups, cap));
+    c->move_persistent = pages * groups > c->oneshot_cap;
   }
   c->attn_per_cu = akv::attn_blocks_per_cu(d->head_dim);
 

@@ -258,15 +258,16 @@ static void launch_move_shape(const Dev &d, int mode, dim3 g, int oneshot_cap, h
   else hipLaunchKernelGGL((move_kernel<64, NT, OS>), g, b, 0, st, d, mode, oneshot_cap);
 }
 
+// The one-shot launch (oneshot_cap blocks), then the persistent grid (grid
+// workgroups; 0 when no op of this cache can exceed the one-shot launch);
+// each checks the planned unit count and only one of them moves.
 hipError_t launch_move(const Dev &d, int mode, int grid, int oneshot_cap, hipStream_t st) {
-  // one-shot launch first (oneshot_cap blocks), then the persistent grid;
-  // each checks the planned unit count and only one of them moves
   if (AKV_MOVE_NT && d.RD == d.D && d.D == 128) {
     launch_move_shape<true, true>(d, mode, dim3(oneshot_cap), oneshot_cap, st);
-    launch_move_shape<true, false>(d, mode, dim3(grid), oneshot_cap, st);
+    if (grid > 0) launch_move_shape<true, false>(d, mode, dim3(grid), oneshot_cap, st);
   } else {
     launch_move_shape<false, true>(d, mode, dim3(oneshot_cap), oneshot_cap, st);
-    launch_move_shape<false, false>(d, mode, dim3(grid), oneshot_cap, st);
+    if (grid > 0) launch_move_shape<false, false>(d, mode, dim3(grid), oneshot_cap, st);
   }
   return hipGetLastError();
 }
