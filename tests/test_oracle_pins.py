@@ -200,8 +200,8 @@ def _filled_cache(n, L=1, H=2, d=8, base=1e4, seed=0):
 
 
 def test_drop_brute_force_every_small_mask():
-    """Every mask of length <= 10 against a literal list filter."""
-    for n in range(0, 11):
+    """Every mask of length <= 12 against a literal list filter."""
+    for n in range(0, 13):
         for bits in itertools.product((0, 1), repeat=n):
             c, k, v = _filled_cache(n)
             before = [(int(t), int(p)) for t, p in zip(c.seqs[0].token_ids, c.seqs[0].pos)]
