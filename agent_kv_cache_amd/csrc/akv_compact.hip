@@ -407,17 +407,32 @@ __global__ __launch_bounds__(kPlanThreads) void append_plan_kernel(Dev d, const 
   if (t == 0) *d.free_count = fc - run_p;
 }
 
-// One workgroup per new token: copies its K/V rows of every (layer, head)
-// with 16-B accesses (a batch of loads issued before their stores) and
-// writes its position and token id.  With ROPE the
-// keys arrive unrotated and are turned to the token's position p on the way
-// (the model's RoPE step fused into the append): cos/sin of p * theta_i in
-// fp64 once per token in LDS, each rotary chunk pair rotated in fp64 and
-// rounded once, the non-rotary tail copied.
+// Append copy.  One workgroup per (layer group, 16 new tokens), in
+// layer-major order (the token group varies fastest), so the workgroups in
+// flight read a compact range of the input and write a compact range of the
+// pages.  16 lanes find their token's page, row and position (positions and
+// token ids are written by the first layer group); the workgroup then copies
+// its tokens' K/V rows of every kv head with 16-B accesses, a batch of loads
+// issued before their stores.  With ROPE the keys arrive unrotated and are
+// turned to each token's position p on the way (the model's RoPE step fused
+// into the append): cos/sin of p * theta_i in fp64 per token in LDS, each
+// rotary chunk pair rotated in fp64 and rounded once, the non-rotary tail
+// copied.
 #ifndef AKV_APPEND_BATCH
 #define AKV_APPEND_BATCH 4
 #endif
 constexpr int kAppendBatch = AKV_APPEND_BATCH;   // 16-B chunks loaded before they are stored
+constexpr int kAppTok = 16;                      // new tokens per workgroup
+#ifndef AKV_APPEND_LAYERS
+#define AKV_APPEND_LAYERS 2
+#endif
+#ifndef AKV_APPEND_ROPE_LAYERS
+#define AKV_APPEND_ROPE_LAYERS 1
+#endif
+// layers per workgroup (measured on 32768 tokens at the Llama-8B shape:
+// plain 2 layers 5.47 TB/s vs 1 layer 5.42; RoPE-fused 1 layer 5.68 vs 2
+// layers 5.51 and 4 layers 5.36 -- the per-token cos/sin are cheap to redo)
+constexpr int append_layers(bool rope) { return rope ? AKV_APPEND_ROPE_LAYERS : AKV_APPEND_LAYERS; }
 
 // Inputs are read once and the pages written once: streamed with the
 // nontemporal hint where every access instruction covers whole 128-B lines.
@@ -433,98 +448,111 @@ __device__ __forceinline__ void st_once(uint16_t *p, u32x4 v) {
 }
 
 template <int D, bool ROPE>
-__global__ __launch_bounds__(256) void append_copy_kernel(Dev d, int64_t n_new,
+__global__ __launch_bounds__(256) void append_copy_kernel(Dev d, int64_t n_new, int ntg,
                                                           const uint16_t *__restrict__ k_new,
                                                           const uint16_t *__restrict__ v_new,
                                                           const int32_t *__restrict__ tok_new) {
   if (d.ctl[CTL_OP_OK] == 0) return;
-  __shared__ int s_page, s_row, s_pos;
-  __shared__ double2 s_cs[ROPE ? kMaxHalf : 1];
-  const int64_t tk = blockIdx.x;
-  if (threadIdx.x == 0) {
+  constexpr int LPB = append_layers(ROPE);
+  constexpr int C8 = D / 8;                    // 16-B chunks per row
+  __shared__ int s_page[kAppTok], s_row[kAppTok], s_pos[kAppTok];
+  __shared__ double2 s_cs[ROPE ? kAppTok : 1][ROPE ? kMaxHalf : 1];
+  const int tg = blockIdx.x % ntg, lg = blockIdx.x / ntg;
+  const int64_t tk0 = (int64_t)tg * kAppTok;
+  const int ntok = (int)min<int64_t>(kAppTok, n_new - tk0);
+  const int t = threadIdx.x;
+  if (t < ntok) {
+    const int64_t tk = tk0 + t;
     int lo = 0, hi = d.B - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (d.seq_info[(size_t)mid * kSeqInfo + SI_APP_OFF] <= tk) lo = mid; else hi = mid - 1;
     }
-    // skip sequences that append nothing but share the offset
+    // sequences that append nothing share the offset of the next one: the
+    // search lands on the last sequence whose offset is <= tk
     const int *si = d.seq_info + (size_t)lo * kSeqInfo;
     const int j = (int)(tk - si[SI_APP_OFF]);
     const int slot = si[SI_OLD_LEN] + j;
     const int page = d.table[(size_t)lo * d.maxpg + slot / kPage];
-    s_page = page;
-    s_row = slot % kPage;
-    s_pos = si[SI_OLD_NEXT] + j;
-    d.pos[(size_t)page * kPage + slot % kPage] = si[SI_OLD_NEXT] + j;
-    d.tok[(size_t)page * kPage + slot % kPage] = tok_new[tk];
+    s_page[t] = page;
+    s_row[t] = slot % kPage;
+    s_pos[t] = si[SI_OLD_NEXT] + j;
+    if (lg == 0) {
+      d.pos[(size_t)page * kPage + slot % kPage] = si[SI_OLD_NEXT] + j;
+      d.tok[(size_t)page * kPage + slot % kPage] = tok_new[tk];
+    }
+  }
+  if constexpr (ROPE) {
+    __syncthreads();
+    const int RH = d.RD / 2;
+    for (int task = t; task < ntok * RH; task += blockDim.x) {
+      const int i = task / RH, pr = task - i * RH;
+      const int pos = s_pos[i];
+      double sn = 0.0, cs = 1.0;
+      if (pos != 0) sincos_rope((double)pos * d.theta[pr], &sn, &cs);
+      s_cs[i][pr] = make_double2(cs, sn);
+    }
   }
   __syncthreads();
-  const int page = s_page, row = s_row;
   const PoolStrides ps = pool_strides(d.NB, d.H, D);
-  constexpr int C8 = D / 8;
-  if constexpr (ROPE) {
-    const int pos = s_pos;
-    for (int i = threadIdx.x; i < d.RD / 2; i += blockDim.x) {
-      double sn = 0.0, cs = 1.0;
-      if (pos != 0) sincos((double)pos * d.theta[i], &sn, &cs);
-      s_cs[i] = make_double2(cs, sn);
+  const int l_lo = lg * LPB, l_hi = min(d.L, l_lo + LPB);
+  for (int l = l_lo; l < l_hi; ++l) {
+    if constexpr (ROPE) {
+      constexpr int CH = D / 16;               // chunk pairs per row
+      // a chunk pair's x and y halves are whole 128-B lines only at d = 128
+      constexpr bool NTP = D == 128;
+      const int rch = d.RD / 16;
+      const int npair = ntok * d.H * CH;
+      for (int c0 = t; c0 < npair; c0 += blockDim.x * kAppendBatch) {
+        u32x4 x[kAppendBatch], y[kAppendBatch];
+        size_t dst[kAppendBatch];
+        int yo[kAppendBatch], pcs[kAppendBatch], tix[kAppendBatch];
+#pragma unroll
+        for (int u = 0; u < kAppendBatch; ++u) {
+          const int c = c0 + u * blockDim.x;
+          if (c >= npair) continue;
+          const int pc = c % CH, ih = c / CH, h = ih % d.H, i = ih / d.H;
+          const bool rot = pc < rch;
+          const int xo = rot ? 8 * pc : d.RD + 8 * (pc - rch);
+          yo[u] = rot ? d.RD / 2 : (D - d.RD) / 2;
+          pcs[u] = pc;
+          tix[u] = i;
+          const size_t src = (((size_t)l * n_new + tk0 + i) * d.H + h) * D + xo;
+          dst[u] = (size_t)l * ps.layer + (size_t)s_page[i] * ps.page + (size_t)h * ps.head +
+                   (size_t)s_row[i] * D + xo;
+          x[u] = ld_once<NTP>(k_new + src);
+          y[u] = ld_once<NTP>(k_new + src + yo[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < kAppendBatch; ++u) {
+          if (c0 + u * (int)blockDim.x >= npair) continue;
+          if (pcs[u] < rch && s_pos[tix[u]] != 0) rotate8(x[u], y[u], &s_cs[tix[u]][8 * pcs[u]]);
+          st_once<NTP>(d.k + dst[u], x[u]);
+          st_once<NTP>(d.k + dst[u] + yo[u], y[u]);
+        }
+      }
     }
-    __syncthreads();
-    constexpr int CH = D / 16;                 // chunk pairs per row
-    // a chunk pair's x and y halves are whole 128-B lines only at d = 128
-    constexpr bool NTP = D == 128;
-    const int rch = d.RD / 16;
-    const int npair = d.L * d.H * CH;
-    // batches of kAppendBatch chunk pairs: every load of a batch is issued
-    // before its stores
-    for (int c0 = threadIdx.x; c0 < npair; c0 += blockDim.x * kAppendBatch) {
-      u32x4 x[kAppendBatch], y[kAppendBatch];
+    const int nchunk = ntok * d.H * C8;
+    for (int c0 = t; c0 < nchunk; c0 += blockDim.x * kAppendBatch) {
+      u32x4 kk[kAppendBatch], vv[kAppendBatch];
       size_t dst[kAppendBatch];
-      int yo[kAppendBatch], pcs[kAppendBatch];
 #pragma unroll
       for (int u = 0; u < kAppendBatch; ++u) {
         const int c = c0 + u * blockDim.x;
-        if (c >= npair) continue;
-        const int pc = c % CH, lh = c / CH, h = lh % d.H, l = lh / d.H;
-        const bool rot = pc < rch;
-        const int xo = rot ? 8 * pc : d.RD + 8 * (pc - rch);
-        yo[u] = rot ? d.RD / 2 : (D - d.RD) / 2;
-        pcs[u] = pc;
-        const size_t src = (((size_t)l * n_new + tk) * d.H + h) * D + xo;
-        dst[u] = (size_t)l * ps.layer + (size_t)page * ps.page + (size_t)h * ps.head +
-                 (size_t)row * D + xo;
-        x[u] = ld_once<NTP>(k_new + src);
-        y[u] = ld_once<NTP>(k_new + src + yo[u]);
+        if (c >= nchunk) continue;
+        const int e8 = c % C8, ih = c / C8, h = ih % d.H, i = ih / d.H;
+        const size_t src = (((size_t)l * n_new + tk0 + i) * d.H + h) * D + 8 * e8;
+        dst[u] = (size_t)l * ps.layer + (size_t)s_page[i] * ps.page + (size_t)h * ps.head +
+                 (size_t)s_row[i] * D + 8 * e8;
+        if constexpr (!ROPE) kk[u] = ld_once<true>(k_new + src);
+        vv[u] = ld_once<true>(v_new + src);
       }
 #pragma unroll
       for (int u = 0; u < kAppendBatch; ++u) {
-        if (c0 + u * (int)blockDim.x >= npair) continue;
-        if (pcs[u] < rch && pos != 0) rotate8(x[u], y[u], &s_cs[8 * pcs[u]]);
-        st_once<NTP>(d.k + dst[u], x[u]);
-        st_once<NTP>(d.k + dst[u] + yo[u], y[u]);
+        if (c0 + u * (int)blockDim.x >= nchunk) continue;
+        if constexpr (!ROPE) st_once<true>(d.k + dst[u], kk[u]);
+        st_once<true>(d.v + dst[u], vv[u]);
       }
-    }
-  }
-  const int nchunk = d.L * d.H * C8;
-  for (int c0 = threadIdx.x; c0 < nchunk; c0 += blockDim.x * kAppendBatch) {
-    u32x4 kk[kAppendBatch], vv[kAppendBatch];
-    size_t dst[kAppendBatch];
-#pragma unroll
-    for (int u = 0; u < kAppendBatch; ++u) {
-      const int c = c0 + u * blockDim.x;
-      if (c >= nchunk) continue;
-      const int e8 = c % C8, lh = c / C8, h = lh % d.H, l = lh / d.H;
-      const size_t src = (((size_t)l * n_new + tk) * d.H + h) * D + 8 * e8;
-      dst[u] = (size_t)l * ps.layer + (size_t)page * ps.page + (size_t)h * ps.head +
-               (size_t)row * D + 8 * e8;
-      if constexpr (!ROPE) kk[u] = ld_once<true>(k_new + src);
-      vv[u] = ld_once<true>(v_new + src);
-    }
-#pragma unroll
-    for (int u = 0; u < kAppendBatch; ++u) {
-      if (c0 + u * (int)blockDim.x >= nchunk) continue;
-      if constexpr (!ROPE) st_once<true>(d.k + dst[u], kk[u]);
-      st_once<true>(d.v + dst[u], vv[u]);
     }
   }
 }
@@ -603,13 +631,15 @@ hipError_t launch_append(const Dev &d, const int32_t *counts, int64_t n_new,
   hipLaunchKernelGGL(append_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, d, counts);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_new == 0) return e;
-  const dim3 g((unsigned)n_new), b(256);
+  const int ntg = (int)((n_new + kAppTok - 1) / kAppTok);
+  const int lpb = append_layers(rope);
+  const dim3 g((unsigned)((long long)ntg * ((d.L + lpb - 1) / lpb))), b(256);
   if (d.D == 128) {
-    if (rope) hipLaunchKernelGGL((append_copy_kernel<128, true>), g, b, 0, st, d, n_new, k_new, v_new, tok_new);
-    else hipLaunchKernelGGL((append_copy_kernel<128, false>), g, b, 0, st, d, n_new, k_new, v_new, tok_new);
+    if (rope) hipLaunchKernelGGL((append_copy_kernel<128, true>), g, b, 0, st, d, n_new, ntg, k_new, v_new, tok_new);
+    else hipLaunchKernelGGL((append_copy_kernel<128, false>), g, b, 0, st, d, n_new, ntg, k_new, v_new, tok_new);
   } else {
-    if (rope) hipLaunchKernelGGL((append_copy_kernel<64, true>), g, b, 0, st, d, n_new, k_new, v_new, tok_new);
-    else hipLaunchKernelGGL((append_copy_kernel<64, false>), g, b, 0, st, d, n_new, k_new, v_new, tok_new);
+    if (rope) hipLaunchKernelGGL((append_copy_kernel<64, true>), g, b, 0, st, d, n_new, ntg, k_new, v_new, tok_new);
+    else hipLaunchKernelGGL((append_copy_kernel<64, false>), g, b, 0, st, d, n_new, ntg, k_new, v_new, tok_new);
   }
   return hipGetLastError();
 }
