@@ -11,12 +11,13 @@
 // page of the copy rebuilt, sources left untouched).
 //
 // Two launch shapes, chosen on the device from the planned unit count:
-//  * one-shot (ops of up to a few 10^5 units): one block per (page, layer)
-//    unit in layer-major order.  Blocks are dispatched in index order, so the
-//    blocks in flight read and write a compact, sliding address range; on
-//    MI355X this streams ~15% faster than a persistent grid whose workgroups
-//    each walk their own pages through all layers (measured on the
-//    Llama-8B-shaped drop: 0.87 -> 0.76 ms).
+//  * one-shot (ops of up to 131072 blocks): one block per page and layer
+//    group (one layer at d = 128, two at d = 64) in layer-major order.
+//    Blocks are dispatched in index order, so the blocks in flight read and
+//    write a compact, sliding address range; on MI355X this streams ~15%
+//    faster than a persistent grid whose workgroups each walk their own
+//    pages through all layers (measured on the Llama-8B-shaped drop: 0.87 ->
+//    0.74 ms).
 //  * persistent (larger ops): occupancy x CUs workgroups, each taking a
 //    contiguous range of page-major units, so the per-page set-up is shared
 //    by all the layers a workgroup moves.
@@ -64,7 +65,7 @@ __device__ __forceinline__ void st_stream(uint16_t *p, u32x4 v) {
 // [w*U/G, (w+1)*U/G), so every workgroup moves the same number of (layer,
 // page) slices whatever the page count, and the per-page set-up (row
 // sources, deltas, cos/sin) is done once per page it touches.  One-shot
-// launch: block b takes unit (page b mod pages, layer b / pages).
+// launch: block b takes page b mod pages at layer group b / pages.
 template <int D, bool NT, bool ONESHOT>
 __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(Dev d, int mode,
                                                                                  int oneshot_cap) {

@@ -47,8 +47,8 @@
  *     serialise them on one stream.
  *   - Environment (read by akv_cache_init): AKV_MOVE_ONESHOT_CAP=<n> caps
  *     the one-shot grid of the drop / reposition / fork move at n blocks,
- *     one per (page, layer) unit; ops needing more use the persistent grid
- *     (0 = always persistent).  Both grids give bit-identical results.
+ *     one per page and layer group; ops needing more use the persistent
+ *     grid (0 = always persistent).  Both grids give bit-identical results.
  */
 #ifndef AKV_H
 #define AKV_H
