@@ -212,8 +212,8 @@ __global__ __launch_bounds__(kSegWaves * 64, 2) void segment_attn_kernel(
 // ---------------------------------------------------------------------------
 // Long segments: a prefill-shaped kernel.  A workgroup owns 256 columns
 // (256/G query tokens x G heads of one kv head); each of its 8 waves owns 32
-// of them (two MFMA column tiles) and keeps their Q fragments, running max,
-// running sum and O^T accumulators in registers.  The workgroup sweeps the
+// of them (two MFMA column tiles) and keeps their Q fragments, exponent
+// references, weight sums and O^T accumulators in registers.  The workgroup sweeps the
 // causal KV range in 64-token tiles staged in LDS (K as rows, V transposed)
 // and double-buffered: the next tile's global loads are in flight while the
 // current one is multiplied, so every KV byte is fetched once per workgroup
@@ -222,6 +222,12 @@ __global__ __launch_bounds__(kSegWaves * 64, 2) void segment_attn_kernel(
 //   O^T (16 dims x 16 columns) += V^T (16 dims x 32 tokens) * P^T: the 32
 //   tokens of one MFMA step are ordered so that a lane's 8 k-values are the
 //   4 + 4 probabilities it already holds from two S^T tiles.
+//   Each column's weight sum is one more MFMA (a ones operand times P^T).
+// On this GPU the matrix core and the vector ALU of a SIMD hardly overlap,
+// so the tile time is the MFMA time plus the VALU time: the loop keeps VALU
+// work to the softmax itself (per-thread load offsets fixed before the
+// sweep, zeroing only on the tile where the sequence ends, a reference that
+// moves lazily, cross-row maxima with the row-swap instructions).
 // ---------------------------------------------------------------------------
 #ifndef AKV_FA_VPAD
 #define AKV_FA_VPAD 4      // halfwords of padding per transposed-V row in LDS
@@ -230,6 +236,19 @@ __global__ __launch_bounds__(kSegWaves * 64, 2) void segment_attn_kernel(
 #define AKV_FA_KPAD 8      // halfwords of padding per K row in LDS (keeps 16-B alignment)
 #endif
 constexpr int kFaWaves = 8, kFaKT = 64, kFaCols = 256;
+#ifndef AKV_FA_TAU
+#define AKV_FA_TAU 8.0f    // log2 of the largest weight allowed before a column's reference moves
+#endif
+
+// Maximum over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four 16-lane rows of a
+// wave, which hold the same MFMA column), with the gfx950 row-swap
+// instructions; every lane gets the same value.
+__device__ __forceinline__ float fa_rows_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 
 template <int D>
 __global__ __launch_bounds__(kFaWaves * 64, 1) void segment_fa_kernel(
@@ -319,86 +338,115 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void segment_fa_kernel(
                           : __builtin_bit_cast(bf16x8s, make_uint4(0, 0, 0, 0));
 
   const float scale = 1.4426950408889634f / sqrtf((float)D);
-  float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
-  floatx4s acc[2][NT];
+  // Per column: the exponent reference in log2 units, -inf until a score is
+  // visible.  Weights are p = 2^(s*scale - ref).  The reference moves to the
+  // running maximum only when a score exceeds it by more than 2^AKV_FA_TAU,
+  // so weights lie in [0, 2^AKV_FA_TAU] and the accumulators are rescaled on
+  // few tiles; the final division by the sum of the same bf16 weights
+  // cancels the reference.
+  // nref = -ref (0 while ref = -inf); thr = the exponent above which the
+  // reference moves (-inf while nothing is visible, then AKV_FA_TAU)
+  float nref[2] = {0.f, 0.f}, thr[2] = {-INFINITY, -INFINITY};
+  floatx4s acc[2][NT], lacc[2];
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct)
+  for (int ct = 0; ct < 2; ++ct) {
+    lacc[ct] = floatx4s{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[ct][t] = floatx4s{0.f, 0.f, 0.f, 0.f};
+  }
+  // 1.0 in every k-slot: ones x P^T gives each column's weight sum on the
+  // matrix core (every row of lacc holds it)
+  const bf16x8s ones = __builtin_bit_cast(bf16x8s, make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
 
   const PoolStrides ps = pool_strides(d.NB, d.H, D);
   const uint16_t *kb = d.k + (size_t)l * ps.layer + (size_t)g * ps.head;
   const uint16_t *vb = d.v + (size_t)l * ps.layer + (size_t)g * ps.head;
+  const uint32_t pstride = (uint32_t)ps.page;           // elements per page
+
+  // What each thread loads is fixed: K chunk r is 16-B chunk ck of tile row
+  // tk[r]; V pair r is chunk vc[r] of rows 2 va[r] and 2 va[r] + 1.  Tiles
+  // start on page boundaries, so tile row x lies in the tile's page x / 16,
+  // at row x % 16 of that page: the in-page offsets are set once here and
+  // each load adds one page base (a 32 x 32 -> 64-bit multiply-add).
+  int tk[KPT], va[VPT], vc[VPT];
+  bool von[VPT];
+  const int ck = tid % C8;
+  const uint16_t *kbt[KPT], *vbt[VPT];
+#pragma unroll
+  for (int r = 0; r < KPT; ++r) {
+    tk[r] = (tid + NTH * r) / C8;
+    kbt[r] = kb + (tk[r] & 15) * D + 8 * ck;
+  }
+#pragma unroll
+  for (int r = 0; r < VPT; ++r) {
+    const int idx = tid + NTH * r;
+    von[r] = idx < VPAIRS;
+    va[r] = von[r] ? (idx & 31) : 0;
+    vc[r] = von[r] ? (idx >> 5) : 0;
+    vbt[r] = vb + ((2 * va[r]) & 15) * D + 8 * vc[r];
+  }
+  const int lastp = (max(len, 1) - 1) >> 4;            // last page of the sequence
 
   // Page ids of the tile fetched next are loaded one tile ahead, so a
-  // tile's K/V loads never wait on a table lookup.  Entries past the end of
-  // the sequence read the last entry (always a valid address) and are zeroed
-  // by value, so every load is unconditional.  Only called when len >= 1.
+  // tile's K/V loads never wait on a table lookup.  Rows past the end of the
+  // sequence read a row of its last page (always a valid address) and are
+  // zeroed by value, so every load is unconditional.  Only called when
+  // len >= 1.
   int pk[KPT], pv[VPT], pq = 0;
   auto pidx = [&](int t) {
-    const int T0 = t * kFaKT;
-    if (W > 0 && tid < kFaKT) pq = trow[min(T0 + tid, len - 1) >> 4];
+    const int p0 = t * (kFaKT / kPage);
+    if (W > 0 && tid < kFaKT) pq = trow[min(t * kFaKT + tid, len - 1) >> 4];
 #pragma unroll
-    for (int r = 0; r < KPT; ++r) {
-      const int tok = (tid + NTH * r) / C8;
-      pk[r] = trow[min(T0 + tok, len - 1) >> 4];
-    }
+    for (int r = 0; r < KPT; ++r) pk[r] = trow[min(p0 + (tk[r] >> 4), lastp)];
 #pragma unroll
-    for (int r = 0; r < VPT; ++r) {
-      const int idx = tid + NTH * r;
-      const int a = idx < VPAIRS ? (idx & 31) : 0;
-      pv[r] = trow[min(T0 + 2 * a, len - 1) >> 4];
-    }
+    for (int r = 0; r < VPT; ++r) pv[r] = trow[min(p0 + ((2 * va[r]) >> 4), lastp)];
   };
   uint4 rk[KPT], rv[2 * VPT];
   int rpos = 0;
   auto gload = [&](int t) {
-    const int T0 = t * kFaKT;
-    if (W > 0 && tid < kFaKT) rpos = d.pos[(size_t)pq * kPage + (min(T0 + tid, len - 1) & 15)];
+    if (W > 0 && tid < kFaKT) rpos = d.pos[(size_t)pq * kPage + (min(t * kFaKT + tid, len - 1) & 15)];
 #pragma unroll
-    for (int r = 0; r < KPT; ++r) {
-      const int idx = tid + NTH * r, tok = idx / C8, ch = idx - tok * C8, e = T0 + tok;
-      const int ec = min(e, len - 1);
-      rk[r] = *reinterpret_cast<const uint4 *>(kb + (size_t)pk[r] * ps.page + (ec & 15) * D + 8 * ch);
-    }
+    for (int r = 0; r < KPT; ++r)
+      rk[r] = *reinterpret_cast<const uint4 *>(kbt[r] + (uint64_t)(uint32_t)pk[r] * pstride);
 #pragma unroll
     for (int r = 0; r < VPT; ++r) {
-      const int idx = tid + NTH * r;
-      const bool on = idx < VPAIRS;
-      const int a = on ? (idx & 31) : 0, ch = on ? (idx >> 5) : 0, e = T0 + 2 * a;
-      // e is even, so e and e + 1 (each clamped to len - 1) share a page
-      const uint16_t *pg = vb + (size_t)pv[r] * ps.page;
-      rv[2 * r] = *reinterpret_cast<const uint4 *>(pg + (min(e, len - 1) & 15) * D + 8 * ch);
-      rv[2 * r + 1] = *reinterpret_cast<const uint4 *>(pg + (min(e + 1, len - 1) & 15) * D + 8 * ch);
+      // rows 2a and 2a + 1 share a page
+      const uint16_t *pg = vbt[r] + (uint64_t)(uint32_t)pv[r] * pstride;
+      rv[2 * r] = *reinterpret_cast<const uint4 *>(pg);
+      rv[2 * r + 1] = *reinterpret_cast<const uint4 *>(pg + D);
     }
   };
-  // registers -> LDS; entries past the end of the sequence become zeros here
+  // registers -> LDS (V transposed); rows past the end of the sequence
+  // become zeros here, which only the tile holding its end needs
   auto lstore = [&](int t, int buf) {
     const int T0 = t * kFaKT;
     if (W > 0 && tid < kFaKT) s_pos[buf][tid] = rpos;
+    if (T0 + kFaKT > len) {
 #pragma unroll
-    for (int r = 0; r < KPT; ++r) {
-      const int idx = tid + NTH * r, tok = idx / C8, ch = idx - tok * C8;
-      uint4 x = rk[r];
-      if (T0 + tok >= len) x = make_uint4(0u, 0u, 0u, 0u);
-      *reinterpret_cast<uint4 *>(&s_k[buf][tok][8 * ch]) = x;
+      for (int r = 0; r < KPT; ++r)
+        if (T0 + tk[r] >= len) rk[r] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+      for (int r = 0; r < VPT; ++r) {
+        const int e = T0 + 2 * va[r];
+        if (e >= len) rv[2 * r] = make_uint4(0u, 0u, 0u, 0u);
+        if (e + 1 >= len) rv[2 * r + 1] = make_uint4(0u, 0u, 0u, 0u);
+      }
     }
 #pragma unroll
+    for (int r = 0; r < KPT; ++r) *reinterpret_cast<uint4 *>(&s_k[buf][tk[r]][8 * ck]) = rk[r];
+#pragma unroll
     for (int r = 0; r < VPT; ++r) {
-      const int idx = tid + NTH * r;
-      if (idx < VPAIRS) {
-        const int a = idx & 31, ch = idx >> 5, e = T0 + 2 * a;
-        uint4 v0 = rv[2 * r], v1 = rv[2 * r + 1];
-        if (e >= len) v0 = make_uint4(0u, 0u, 0u, 0u);
-        if (e + 1 >= len) v1 = make_uint4(0u, 0u, 0u, 0u);
+      if (von[r]) {
+        const int a = va[r], ch = vc[r];
+        const uint4 v0 = rv[2 * r], v1 = rv[2 * r + 1];
         const uint32_t x0[4] = {v0.x, v0.y, v0.z, v0.w}, x1[4] = {v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          // dims 8ch+2w (low halves) and 8ch+2w+1 (high halves) of tokens 2a, 2a+1
+          // dims 8ch+2w (low halves) and 8ch+2w+1 (high halves) of rows 2a, 2a+1
           *reinterpret_cast<uint32_t *>(&s_vt[buf][8 * ch + 2 * w][2 * a]) =
-              (x0[w] & 0xffffu) | (x1[w] << 16);
+              __builtin_amdgcn_perm(x1[w], x0[w], 0x05040100u);
           *reinterpret_cast<uint32_t *>(&s_vt[buf][8 * ch + 2 * w + 1][2 * a]) =
-              (x0[w] >> 16) | (x1[w] & 0xffff0000u);
+              __builtin_amdgcn_perm(x1[w], x0[w], 0x07060302u);
         }
       }
     }
@@ -436,18 +484,19 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void segment_fa_kernel(
           sacc[ct][tt] = sa;
         }
       }
-      bf16x8s pb[2][2];
       const bool diag = T0 + kFaKT - 1 > wave_lo;            // wave-uniform
+      float mx[2];
+      bool up[2];
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
-        // running max kept on raw scores; the softmax scale is folded into
-        // one FMA per score: p = 2^(s*scale - m*scale)
         if (diag) {
+          // entry T0 + 16 tt + 4 kg + j is visible while <= lim
+          const int rel = lim[ct] - T0 - 4 * kg;
 #pragma unroll
           for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-              if (T0 + 16 * tt + 4 * kg + j > lim[ct]) sacc[ct][tt][j] = -INFINITY;
+              if (16 * tt + j > rel) sacc[ct][tt][j] = -INFINITY;
         }
         if (W > 0) {
 #pragma unroll
@@ -459,39 +508,47 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void segment_fa_kernel(
               if (pj4[j] < wlo[ct]) sacc[ct][tt][j] = -INFINITY;
           }
         }
-        float mx = sacc[ct][0][0];
+        // exponents against the current reference, and their column maximum
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) mx = fmaxf(mx, sacc[ct][tt][j]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float mnew = fmaxf(m[ct], mx);
-        // nothing visible yet: keep the reference finite so 2^(-inf) = 0
-        const float mref = (mnew == -INFINITY) ? 0.f : mnew * scale;
-        if (__any(mnew > m[ct])) {
-          const float alpha = (m[ct] == -INFINITY) ? 0.f : seg_exp2(m[ct] * scale - mref);
-          lsum[ct] *= alpha;
+          for (int j = 0; j < 4; ++j) sacc[ct][tt][j] = fmaf(sacc[ct][tt][j], scale, nref[ct]);
+        float m0 = fmaxf(fmaxf(sacc[ct][0][0], sacc[ct][0][1]), fmaxf(sacc[ct][0][2], sacc[ct][0][3]));
+        float m1 = fmaxf(fmaxf(sacc[ct][1][0], sacc[ct][1][1]), fmaxf(sacc[ct][1][2], sacc[ct][1][3]));
+        float m2 = fmaxf(fmaxf(sacc[ct][2][0], sacc[ct][2][1]), fmaxf(sacc[ct][2][2], sacc[ct][2][3]));
+        float m3 = fmaxf(fmaxf(sacc[ct][3][0], sacc[ct][3][1]), fmaxf(sacc[ct][3][2], sacc[ct][3][3]));
+        mx[ct] = fa_rows_max(fmaxf(fmaxf(m0, m1), fmaxf(m2, m3)));
+        up[ct] = mx[ct] > thr[ct];
+      }
+      if (__any(up[0] || up[1])) {
+        // some column's reference moves to its maximum: shift its exponents
+        // and scale what it has accumulated (by 0 on its first visible tile)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          const float sh = up[ct] ? mx[ct] : 0.f;
+          const float alpha = !up[ct] ? 1.f : (thr[ct] == -INFINITY ? 0.f : seg_exp2(-sh));
+          nref[ct] -= sh;
+          if (up[ct]) thr[ct] = AKV_FA_TAU;
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sacc[ct][tt][j] -= sh;
+          lacc[ct] *= alpha;
 #pragma unroll
           for (int dt = 0; dt < NT; ++dt) acc[ct][dt] *= alpha;
         }
-        m[ct] = mnew;
-        float pj[4][4];
-        float psum = 0.f;
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            pj[tt][j] = seg_exp2(fmaf(sacc[ct][tt][j], scale, -mref));
-            psum += pj[tt][j];
-          }
-        lsum[ct] += psum;
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc)
-          pb[ct][kc] = bf16x8s{(__bf16)pj[2 * kc][0], (__bf16)pj[2 * kc][1], (__bf16)pj[2 * kc][2],
-                               (__bf16)pj[2 * kc][3], (__bf16)pj[2 * kc + 1][0], (__bf16)pj[2 * kc + 1][1],
-                               (__bf16)pj[2 * kc + 1][2], (__bf16)pj[2 * kc + 1][3]};
       }
+      bf16x8s pb[2][2];
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+          const floatx4s &a0 = sacc[ct][2 * kc], &a1 = sacc[ct][2 * kc + 1];
+          pb[ct][kc] = bf16x8s{(__bf16)seg_exp2(a0[0]), (__bf16)seg_exp2(a0[1]), (__bf16)seg_exp2(a0[2]),
+                               (__bf16)seg_exp2(a0[3]), (__bf16)seg_exp2(a1[0]), (__bf16)seg_exp2(a1[1]),
+                               (__bf16)seg_exp2(a1[2]), (__bf16)seg_exp2(a1[3])};
+          lacc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[ct][kc], lacc[ct], 0, 0, 0);
+        }
 #pragma unroll
       for (int dt = 0; dt < NT; ++dt)
 #pragma unroll
@@ -510,11 +567,8 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void segment_fa_kernel(
 
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
-    float ls = lsum[ct];
-    ls += __shfl_xor(ls, 16, 64);
-    ls += __shfl_xor(ls, 32, 64);
     if (!rok[ct]) continue;
-    const float inv = cok[ct] ? 1.f / ls : 0.f;   // an invalid segment's rows are zero
+    const float inv = cok[ct] ? 1.f / lacc[ct][0] : 0.f;   // an invalid segment's rows are zero
     uint16_t *orow = out + qrow[ct] * D + 4 * kg;
 #pragma unroll
     for (int dt = 0; dt < NT; ++dt) {
