@@ -513,18 +513,24 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void segment_fa_kernel(
         for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
           for (int j = 0; j < 4; ++j) sacc[ct][tt][j] = fmaf(sacc[ct][tt][j], scale, nref[ct]);
-        float m0 = fmaxf(fmaxf(sacc[ct][0][0], sacc[ct][0][1]), fmaxf(sacc[ct][0][2], sacc[ct][0][3]));
-        float m1 = fmaxf(fmaxf(sacc[ct][1][0], sacc[ct][1][1]), fmaxf(sacc[ct][1][2], sacc[ct][1][3]));
-        float m2 = fmaxf(fmaxf(sacc[ct][2][0], sacc[ct][2][1]), fmaxf(sacc[ct][2][2], sacc[ct][2][3]));
-        float m3 = fmaxf(fmaxf(sacc[ct][3][0], sacc[ct][3][1]), fmaxf(sacc[ct][3][2], sacc[ct][3][3]));
-        mx[ct] = fa_rows_max(fmaxf(fmaxf(m0, m1), fmaxf(m2, m3)));
+        // this lane's maximum (a quarter of the column)
+        const float m0 = fmaxf(fmaxf(sacc[ct][0][0], sacc[ct][0][1]), fmaxf(sacc[ct][0][2], sacc[ct][0][3]));
+        const float m1 = fmaxf(fmaxf(sacc[ct][1][0], sacc[ct][1][1]), fmaxf(sacc[ct][1][2], sacc[ct][1][3]));
+        const float m2 = fmaxf(fmaxf(sacc[ct][2][0], sacc[ct][2][1]), fmaxf(sacc[ct][2][2], sacc[ct][2][3]));
+        const float m3 = fmaxf(fmaxf(sacc[ct][3][0], sacc[ct][3][1]), fmaxf(sacc[ct][3][2], sacc[ct][3][3]));
+        mx[ct] = fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
         up[ct] = mx[ct] > thr[ct];
       }
+      // A column's reference moves only if one of its four lanes sees an
+      // exponent above the threshold; only then are the column maxima
+      // needed, reduced across the lane rows inside the (rare) branch.
       if (__any(up[0] || up[1])) {
         // some column's reference moves to its maximum: shift its exponents
         // and scale what it has accumulated (by 0 on its first visible tile)
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
+          mx[ct] = fa_rows_max(mx[ct]);
+          up[ct] = mx[ct] > thr[ct];
           const float sh = up[ct] ? mx[ct] : 0.f;
           const float alpha = !up[ct] ? 1.f : (thr[ct] == -INFINITY ? 0.f : seg_exp2(-sh));
           nref[ct] -= sh;
