@@ -323,11 +323,17 @@ __global__ __launch_bounds__(256) void commit_kernel(Dev d) {
     if (b == 0 && threadIdx.x == 0) *d.free_count = base + d.ctl[CTL_F_TOTAL];
     return;
   }
+  // The freed pages go onto the stack in reverse (sequence b's first page on
+  // top of b + 1's), so later pops hand them out in their old order: a
+  // sequence rebuilt from them keeps ascending page runs, and the move's
+  // blocks in flight keep reading and writing compact address ranges (a
+  // scattered page table costs the move ~11% on MI355X).
+  const int ftot = d.ctl[CTL_F_TOTAL];
   int32_t *trow = d.table + (size_t)b * d.maxpg;
   for (int k = threadIdx.x; k < nfreed; k += blockDim.x) {
     const int po = fbd + k;
     const int old = trow[po];
-    d.free_stack[base + foff + k] = old;
+    d.free_stack[base + ftot - 1 - (foff + k)] = old;
     trow[po] = (k < nmove) ? d.stage[moff + k] : -1;
   }
   if (threadIdx.x == 0) {
@@ -568,6 +574,17 @@ __global__ __launch_bounds__(kPlanThreads) void release_kernel(Dev d, const uint
   __syncthreads();
   if (!s_ok) return;
   const int fc = *d.free_count;
+  // total pages released, so they can be pushed in reverse (the first
+  // sequence's first page on top: later pops return them in their old order)
+  int all = 0;
+  for (int base = 0; base < d.B; base += kPlanThreads) {
+    const int b = base + t;
+    int np = 0;
+    if (b < d.B && sel[b]) np = (d.lens[b] + kPage - 1) / kPage;
+    int tot;
+    block_exclusive_scan<kPlanThreads>(np, s_wave, &tot);
+    all += tot;
+  }
   int run = 0;
   for (int base = 0; base < d.B; base += kPlanThreads) {
     const int b = base + t;
@@ -578,7 +595,7 @@ __global__ __launch_bounds__(kPlanThreads) void release_kernel(Dev d, const uint
     if (b < d.B && sel[b]) {
       int32_t *row = d.table + (size_t)b * d.maxpg;
       for (int k = 0; k < np; ++k) {
-        d.free_stack[fc + run + ex + k] = row[k];
+        d.free_stack[fc + all - 1 - (run + ex + k)] = row[k];
         row[k] = -1;
       }
       d.lens[b] = 0;

@@ -37,6 +37,12 @@ namespace akv {
 #ifndef AKV_MOVE_NT
 #define AKV_MOVE_NT 1          // nontemporal hint on the streamed KV accesses
 #endif
+#ifndef AKV_MOVE_FR64
+#define AKV_MOVE_FR64 1        // full-row thread mapping at d = 64 (full RoPE)
+#endif
+#ifndef AKV_MOVE_FR64_NT
+#define AKV_MOVE_FR64_NT 1     // nontemporal hint with the full-row mapping
+#endif
 
 constexpr int kMoveThreads = 256;
 
@@ -66,14 +72,24 @@ __device__ __forceinline__ void st_stream(uint16_t *p, u32x4 v) {
 // page) slices whatever the page count, and the per-page set-up (row
 // sources, deltas, cos/sin) is done once per page it touches.  One-shot
 // launch: block b takes page b mod pages at layer group b / pages.
-template <int D, bool NT, bool ONESHOT>
+//
+// Thread mapping.  Half rows (FR = false): a thread holds chunk pc of the x
+// half of a row and the matching chunk of the y half (8 NeoX pairs), loaded
+// by two instructions.  Full rows (FR = true; full RoPE at d = 64, where a
+// row is one 128-B line): a thread holds one chunk c of the row, so every
+// load instruction covers whole lines, and the partner chunk c ^ (d/16) is
+// read from the lane that holds it (the same row's lanes are adjacent).
+template <int D, bool NT, bool ONESHOT, bool FR>
 __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(Dev d, int mode,
                                                                                  int oneshot_cap) {
   constexpr int HALF = D / 2;
   constexpr int CH = D / 16;             // 16-B chunks per half row
-  constexpr int TPH = kPage * CH;        // threads per (layer, head) slice
+  constexpr int CPR = FR ? 2 * CH : CH;  // threads per row
+  constexpr int TPH = kPage * CPR;       // threads per (layer, head) slice
   constexpr int NS = kMoveThreads / TPH; // slices per pass
-  constexpr int U = AKV_MOVE_UNROLL;      // slices loaded before any store
+  // slices loaded before any store (a full-row thread holds half the bytes
+  // of a half-row thread per slice, so it takes twice as many)
+  constexpr int U = FR ? 2 * AKV_MOVE_UNROLL : AKV_MOVE_UNROLL;
   __shared__ int s_dst, s_mv;
   __shared__ int s_src[kPage], s_valid[kPage], s_delta[kPage], s_rep[kPage];
   __shared__ int s_repval[kPage], s_nrep;
@@ -108,14 +124,15 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
     u1 = units * (blockIdx.x + 1) / gridDim.x;
   }
   const int t = threadIdx.x;
-  const int r = (t % TPH) / CH, pc = t % CH, slot = t / TPH;
-  // Chunk pc of a row: a rotary chunk pairs dims [8pc, 8pc+8) with the same
-  // dims + RD/2; past the rotary part ([RD, D), partial RoPE) chunks are only
-  // copied, paired the same way over the tail.
+  const int r = (t % TPH) / CPR, pc = t % CPR, slot = t / TPH;
+  // Half rows: chunk pc of a row, a rotary chunk pairs dims [8pc, 8pc+8)
+  // with the same dims + RD/2; past the rotary part ([RD, D), partial RoPE)
+  // chunks are only copied, paired the same way over the tail.  Full rows
+  // (RD == D): chunk pc holds dims [8pc, 8pc+8); pc < CH is an x chunk.
   const int rch = d.RD / 16;
-  const bool rot_chunk = pc < rch;
-  const int xo = rot_chunk ? 8 * pc : d.RD + 8 * (pc - rch);
-  const int yoff = rot_chunk ? d.RD / 2 : (D - d.RD) / 2;
+  const bool rot_chunk = FR || pc < rch;
+  const int xo = (FR || rot_chunk) ? 8 * pc : d.RD + 8 * (pc - rch);
+  const int yoff = FR ? 0 : rot_chunk ? d.RD / 2 : (D - d.RD) / 2;
   const size_t S = (size_t)d.S;
   const PoolStrides ps = pool_strides(d.NB, d.H, D);
   const size_t hstride = ps.head, lstride = ps.layer;
@@ -212,7 +229,7 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
         lo[u] = hi[u] = u32x4{0u, 0u, 0u, 0u};
         if (on[u] && valid) {
           lo[u] = ld_stream<NT>(pool + src_row + off);
-          hi[u] = ld_stream<NT>(pool + src_row + off + yoff);
+          if constexpr (!FR) hi[u] = ld_stream<NT>(pool + src_row + off + yoff);
         }
       }
     };
@@ -230,16 +247,29 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
       __syncthreads();
     }
     // cos/sin of this thread's 8 pairs stay in LDS and are read per use
-    const double2 *cs_row = &s_cs[(rot_any && delta != 0) ? s_rep[r] : 0][rot_chunk ? 8 * pc : 0];
+    const double2 *cs_row = &s_cs[(rot_any && delta != 0) ? s_rep[r] : 0]
+                                 [FR ? 8 * (pc % CH) : rot_chunk ? 8 * pc : 0];
     while (more) {
       uint16_t *pool = plane ? d.v : d.k;
       const bool rot_plane = plane == 0 && turn;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (!on[u]) continue;
-        if (rot_plane) rotate8(lo[u], hi[u], cs_row);
-        st_stream<NT>(pool + dofs[u], lo[u]);
-        st_stream<NT>(pool + dofs[u] + yoff, hi[u]);
+        if constexpr (FR) {
+          if (rot_plane) {
+            // both lanes of a pair hold the same row, so they turn together
+            const u32x4 other = {(uint32_t)__shfl_xor((int)lo[u].x, CH, 64),
+                                 (uint32_t)__shfl_xor((int)lo[u].y, CH, 64),
+                                 (uint32_t)__shfl_xor((int)lo[u].z, CH, 64),
+                                 (uint32_t)__shfl_xor((int)lo[u].w, CH, 64)};
+            lo[u] = rotate8_side(lo[u], other, pc < CH, cs_row);
+          }
+          st_stream<NT>(pool + dofs[u], lo[u]);
+        } else {
+          if (rot_plane) rotate8(lo[u], hi[u], cs_row);
+          st_stream<NT>(pool + dofs[u], lo[u]);
+          st_stream<NT>(pool + dofs[u] + yoff, hi[u]);
+        }
       }
       i0 += NS * U;
       if (i0 >= nsl) {
@@ -252,32 +282,40 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
   }
 }
 
-template <bool NT, bool OS>
-static void launch_move_shape(const Dev &d, int mode, dim3 g, int oneshot_cap, hipStream_t st) {
+template <int D, bool NT, bool FR>
+static void launch_move_pair(const Dev &d, int mode, int grid, int oneshot_cap, hipStream_t st) {
   const dim3 b(kMoveThreads);
-  if (d.D == 128) hipLaunchKernelGGL((move_kernel<128, NT, OS>), g, b, 0, st, d, mode, oneshot_cap);
-  else hipLaunchKernelGGL((move_kernel<64, NT, OS>), g, b, 0, st, d, mode, oneshot_cap);
+  hipLaunchKernelGGL((move_kernel<D, NT, true, FR>), dim3(oneshot_cap), b, 0, st, d, mode,
+                     oneshot_cap);
+  if (grid > 0)
+    hipLaunchKernelGGL((move_kernel<D, NT, false, FR>), dim3(grid), b, 0, st, d, mode, oneshot_cap);
 }
 
 // The one-shot launch (oneshot_cap blocks), then the persistent grid (grid
 // workgroups; 0 when no op of this cache can exceed the one-shot launch);
-// each checks the planned unit count and only one of them moves.
+// each checks the planned unit count and only one of them moves.  Full RoPE
+// at d = 128 (half rows of whole lines) and at d = 64 (full rows) uses the
+// nontemporal hint; partial RoPE uses cached half-row accesses.
 hipError_t launch_move(const Dev &d, int mode, int grid, int oneshot_cap, hipStream_t st) {
-  if (AKV_MOVE_NT && d.RD == d.D && d.D == 128) {
-    launch_move_shape<true, true>(d, mode, dim3(oneshot_cap), oneshot_cap, st);
-    if (grid > 0) launch_move_shape<true, false>(d, mode, dim3(grid), oneshot_cap, st);
+  const bool full = d.RD == d.D;
+  if (d.D == 128) {
+    if (AKV_MOVE_NT && full) launch_move_pair<128, true, false>(d, mode, grid, oneshot_cap, st);
+    else launch_move_pair<128, false, false>(d, mode, grid, oneshot_cap, st);
   } else {
-    launch_move_shape<false, true>(d, mode, dim3(oneshot_cap), oneshot_cap, st);
-    if (grid > 0) launch_move_shape<false, false>(d, mode, dim3(grid), oneshot_cap, st);
+    if (AKV_MOVE_FR64 && full) launch_move_pair<64, AKV_MOVE_FR64_NT != 0, true>(d, mode, grid, oneshot_cap, st);
+    else launch_move_pair<64, false, false>(d, mode, grid, oneshot_cap, st);
   }
   return hipGetLastError();
 }
 
 int move_blocks_per_cu(int D) {
   int n = 0;
-  const hipError_t e = (D == 128)
-      ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, move_kernel<128, true, false>, kMoveThreads, 0)
-      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, move_kernel<64, true, false>, kMoveThreads, 0);
+  const hipError_t e =
+      (D == 128) ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, move_kernel<128, true, false, false>,
+                                                                kMoveThreads, 0)
+                 : hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                       &n, move_kernel<64, AKV_MOVE_FR64_NT != 0, false, AKV_MOVE_FR64 != 0>,
+                       kMoveThreads, 0);
   return (e == hipSuccess && n > 0) ? n : 2;
 }
 

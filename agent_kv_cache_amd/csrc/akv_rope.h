@@ -60,6 +60,31 @@ __device__ __forceinline__ void rotate8(u32x4 &lo, u32x4 &hi, const double2 *cs)
 }
 
 
+// One side of 8 NeoX pairs: `own` holds 8 values of one side (x_i when is_x,
+// else y_i = k[i + d/2]) and `other` the partner side.  x' = x cos - y sin,
+// y' = y cos + x sin: the same fp64 operations and single rounding as
+// rotate8, so both mappings give identical bits.
+__device__ __forceinline__ u32x4 rotate8_side(u32x4 own, u32x4 other, bool is_x,
+                                              const double2 *cs) {
+  const uint32_t a[4] = {own.x, own.y, own.z, own.w};
+  const uint32_t bb[4] = {other.x, other.y, other.z, other.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float r[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const double x = (double)bf16_to_f32((a[q] >> (16 * e)) & 0xFFFFu);
+      const double y = (double)bf16_to_f32((bb[q] >> (16 * e)) & 0xFFFFu);
+      const double2 v = cs[2 * q + e];
+      const double p = y * v.y;
+      r[e] = f64_to_f32_for_bf16(fma(x, v.x, is_x ? -p : p));
+    }
+    o[q] = f32x2_to_bf16x2(r[0], r[1]);
+  }
+  return u32x4{o[0], o[1], o[2], o[3]};
+}
+
 // sin and cos of x = delta * theta_i in fp64, for |x| < 2^31 (|delta| < 2^31,
 // 0 <= theta_i <= 1).  Cody-Waite reduction by pi/2, with pi/2 split into
 // three 22-bit parts and a double tail so that k * part is exact for

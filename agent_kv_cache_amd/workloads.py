@@ -167,6 +167,22 @@ class History:
     ops: List[tuple]
     total_tokens: int
 
+    def max_active(self) -> int:
+        """Largest number of active tokens at any point of the run (message
+        lengths only: appends add a message, drops remove listed ones)."""
+        alive, n, top = set(), 0, 0
+        for op in self.ops:
+            if op[0] == "append":
+                alive.add(op[1])
+                n += op[2]
+                top = max(top, n)
+            elif op[0] in ("drop", "drop_repos"):
+                for m in op[1]:
+                    if m in alive:
+                        alive.discard(m)
+                        n -= self.msg_len[m]
+        return top
+
 
 def c4_history(seed: int = 4, turns: int = 50, total: int = 131072,
                keep_turns: int = 3, repos_every: int = 3,

@@ -159,7 +159,10 @@ def run_history(args):
     sh = W.SHAPES["c4"]
     hist = W.c4_history()
     row = sh.n_layers * sh.n_kv_heads * sh.head_dim * 2
-    cache = Hn.make_cache(sh, [1], 4096, max_blocks_per_seq=4096)
+    # per-sequence page capacity: the run's largest active length, in whole
+    # plan chunks of 256 pages (it also bounds the move's one-shot grid)
+    maxpg = -(-Hn.pages_for(hist.max_active()) // 256) * 256
+    cache = Hn.make_cache(sh, [1], 4096, max_blocks_per_seq=maxpg)
     cache.reset()
     dev = cache.device
     tot_bytes = tot_ms = 0.0

@@ -159,3 +159,37 @@ def test_release_is_a_no_op_while_an_error_is_latched():
     assert int(cache.free_count) == fc
     for b in range(2):
         same_state(before[b], snapshot(cache, b))
+
+
+def test_freed_pages_are_handed_out_in_their_old_order():
+    """Pages freed by a drop or a release return to the stack so that later
+    pops hand them out in the order the sequence held them (a rebuilt or new
+    sequence keeps ascending page runs)."""
+    sh = W.Shape(2, 2, 64, 4, 1e4)
+    lens = [1024, 0]
+    cache = Hn.make_cache(sh, lens, 96, max_blocks_per_seq=64)
+    cache.reset()                                   # pages popped 0, 1, 2, ...
+    Hn.fill(cache, sh, lens, 70, gen_device="cpu")
+    assert cache.block_table[0, :64].tolist() == list(range(64))
+    say("case drop frees pages 10..63, append reuses them in order")
+    mask = np.zeros(1024, np.uint8)
+    mask[170:300] = 1                                # first dropped entry in page 10
+    cache.drop(Hn.mask_tensor(cache, [mask, None]))
+    assert cache.sync_status() == 0
+    r = 1024 - 130
+    assert cache.block_table[0, :10].tolist() == list(range(10))
+    assert cache.block_table[0, 10:Hn.pages_for(r)].tolist() == list(range(64, 64 + Hn.pages_for(r) - 10))
+    n_new = 16 * 20
+    k = W.randn_bf16((sh.n_layers, n_new, sh.n_kv_heads, sh.head_dim), 71).to(cache.device)
+    v = W.randn_bf16((sh.n_layers, n_new, sh.n_kv_heads, sh.head_dim), 72).to(cache.device)
+    cache.append(torch.tensor([0, n_new], dtype=torch.int32, device=cache.device), n_new, k, v,
+                 torch.arange(n_new, dtype=torch.int32, device=cache.device))
+    assert cache.sync_status() == 0
+    assert cache.block_table[1, :20].tolist() == list(range(10, 30))
+    say("case release of sequence 1 returns 10..29 for the next pops in order")
+    cache.release(torch.tensor([0, 1], dtype=torch.uint8, device=cache.device))
+    assert cache.sync_status() == 0
+    cache.append(torch.tensor([0, n_new], dtype=torch.int32, device=cache.device), n_new, k, v,
+                 torch.arange(n_new, dtype=torch.int32, device=cache.device))
+    assert cache.sync_status() == 0
+    assert cache.block_table[1, :20].tolist() == list(range(10, 30))

@@ -86,7 +86,10 @@ def test_c4_long_history_replay():
     hist = W.c4_history()
     layers = [0, 35]
     t0 = time.time()
-    cache = Hn.make_cache(sh, [1], 4096, max_blocks_per_seq=4096)
+    # per-sequence page capacity: the run's largest active length, in whole
+    # plan chunks of 256 pages (it also bounds the move's one-shot grid)
+    maxpg = -(-Hn.pages_for(hist.max_active()) // 256) * 256
+    cache = Hn.make_cache(sh, [1], 4096, max_blocks_per_seq=maxpg)
     cache.reset()
     meta = O.OracleCache(sh.n_layers, sh.n_kv_heads, sh.head_dim, sh.rope_base, with_kv=False)
     kvo = O.OracleCache(len(layers), sh.n_kv_heads, sh.head_dim, sh.rope_base)

@@ -48,3 +48,25 @@ def test_workloads_are_deterministic():
     ra, rb = W.restore_c2(), W.restore_c2()
     for (ma, na), (mb, nb) in zip(ra.versions, rb.versions):
         assert na == nb and np.array_equal(ma, mb)
+
+
+def test_c4_max_active_matches_a_metadata_replay():
+    """The page capacity of the long-history cache is sized from
+    History.max_active(); check it against the oracle's own replay of the
+    run (lengths after every op, token sets from the message ids)."""
+    h = W.c4_history()
+    oc = O.OracleCache(1, 1, 8, 1.5e5, n_seqs=1, with_kv=False)
+    top = 0
+    for op in h.ops:
+        if op[0] == "append":
+            mid, n = op[1], op[2]
+            oc.append(0, np.arange(h.msg_start[mid], h.msg_start[mid] + n))
+        elif op[0] == "repos":
+            oc.reposition(0)
+        else:
+            tok = oc.seqs[0].token_ids
+            mask = W.mask_for_messages(tok, h, op[1])
+            (oc.drop if op[0] == "drop" else oc.drop_reposition)(0, mask)
+        top = max(top, len(oc.seqs[0]))
+    assert h.max_active() == top
+    assert len(oc.seqs[0]) < top <= h.total_tokens
