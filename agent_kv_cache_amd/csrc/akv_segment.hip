@@ -239,6 +239,33 @@ constexpr int kFaWaves = 8, kFaKT = 64, kFaCols = 256;
 #ifndef AKV_FA_TAU
 #define AKV_FA_TAU 8.0f    // log2 of the largest weight allowed before a column's reference moves
 #endif
+#ifndef AKV_FA_XCD
+#define AKV_FA_XCD 1       // XCD-aware block order (see fa_block)
+#endif
+constexpr int kXcds = 8;   // MI355X: 8 accelerator dies, each with its own L2
+
+// Block order.  The hardware hands workgroup L (linear id) to die L mod 8,
+// in order of L; every query block of one (segment, layer, kv head) group
+// sweeps the same K/V pages from the start.  Consecutive ids are therefore
+// remapped so that die k runs whole groups one after another (groups k,
+// k + 8, k + 16, ...; all query blocks of a group in a row): the ~32 blocks
+// a die runs at once share one group's K/V tiles through that die's L2,
+// instead of every die fetching every group's pages.  Identity when the
+// group count is not a multiple of the die count.
+__device__ __forceinline__ void fa_block(int &bx, int &by, int &bz) {
+  bx = blockIdx.x;
+  by = blockIdx.y;
+  bz = blockIdx.z;
+  const int X = gridDim.x, Y = gridDim.y;
+  const long long groups = (long long)Y * gridDim.z;
+  if (!AKV_FA_XCD || groups % kXcds != 0) return;
+  const long long L = bx + (long long)X * (by + (long long)Y * bz);
+  const long long s = L / kXcds;                 // position in the die's order
+  const long long gg = (s / X) * kXcds + L % kXcds;
+  bx = (int)(s % X);
+  by = (int)(gg % Y);
+  bz = (int)(gg / Y);
+}
 
 // Maximum over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four 16-lane rows of a
 // wave, which hold the same MFMA column), with the gfx950 row-swap
@@ -268,21 +295,23 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void segment_fa_kernel(
 
   const int G = Hq / d.H;
   const int TBW = kFaCols / G;                            // query tokens per workgroup
-  const int sg = blockIdx.y;
-  const int li = blockIdx.z / d.H, g = blockIdx.z - li * d.H, l = l0 + li;
+  int bx, by, bz;
+  fa_block(bx, by, bz);
+  const int sg = by;
+  const int li = bz / d.H, g = bz - li * d.H, l = l0 + li;
   const int q0 = seg_q_off[sg];
   const int n = seg_q_off[sg + 1] - q0;
   if (n < 0 || n > max_q) {
-    if (threadIdx.x == 0 && blockIdx.x == 0 && blockIdx.z == 0)
+    if (threadIdx.x == 0 && bx == 0 && bz == 0)
       atomicCAS(&d.ctl[CTL_ERR], 0, (int)AKV_ERR_ARG);
     return;
   }
-  const int i0 = blockIdx.x * TBW;
+  const int i0 = bx * TBW;
   if (i0 >= n) return;
   const int seq = seg_seq[sg];
   const int len = (seq >= 0 && seq < d.B) ? d.lens[seq] : -1;
   const bool bad = len < n;
-  if (bad && threadIdx.x == 0 && blockIdx.x == 0 && blockIdx.z == 0)
+  if (bad && threadIdx.x == 0 && bx == 0 && bz == 0)
     atomicCAS(&d.ctl[CTL_ERR], 0, (int)AKV_ERR_ARG);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int cl = lane & 15, kg = lane >> 4;
