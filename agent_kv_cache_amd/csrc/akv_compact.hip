@@ -118,14 +118,23 @@ __global__ __launch_bounds__(kChunkPages) void plan_kernel(
       }
     }
     // survivor rank of the chunk's first page: the keep bits of the
-    // sequence's earlier chunks, recounted (one page per thread per chunk)
+    // sequence's earlier chunks, recounted (one page per thread per chunk;
+    // eight chunks' mask words are loaded before any is counted, so the
+    // loads overlap instead of costing one round trip per chunk)
     int acc = 0;
-    for (int cc = 0; cc < c; ++cc) {
-      const int pq = cc * kChunkPages + t;
-      unsigned kq = page_valid_bits(len, pq);
-      if (kq && (mode & M_DROP))
-        kq &= ~page_drop_bits(*reinterpret_cast<const uint4 *>(mask + b * S + (size_t)pq * kPage));
-      acc += __popc(kq);
+    for (int cc0 = 0; cc0 < c; cc0 += 8) {
+      unsigned kq[8];
+      uint4 mq[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int pq = (cc0 + u) * kChunkPages + t;
+        kq[u] = cc0 + u < c ? page_valid_bits(len, pq) : 0u;
+        mq[u] = (kq[u] && (mode & M_DROP))
+                    ? *reinterpret_cast<const uint4 *>(mask + b * S + (size_t)pq * kPage)
+                    : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc += __popc(kq[u] & ~page_drop_bits(mq[u]));
     }
     if (t == 0) s_fdrop = INT_MAX;
     int base;
@@ -217,10 +226,19 @@ __global__ __launch_bounds__(kChunkPages) void plan_kernel(
       const int P0 = (L0 + kPage - 1) / kPage;
       const int nch = (P0 + kChunkPages - 1) / kChunkPages;
       int rnew = 0, fdrop = INT_MAX;
-      for (int cc = 0; cc < nch; ++cc) {
-        const int *ci = d.chunk_info + ((size_t)bb * d.nchunk + cc) * 2;
-        rnew += __atomic_load_n(&ci[0], __ATOMIC_RELAXED);
-        fdrop = min(fdrop, __atomic_load_n(&ci[1], __ATOMIC_RELAXED));
+      for (int cc0 = 0; cc0 < nch; cc0 += 8) {
+        int cn[8], cf[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int *ci = d.chunk_info + ((size_t)bb * d.nchunk + cc0 + u) * 2;
+          cn[u] = cc0 + u < nch ? __atomic_load_n(&ci[0], __ATOMIC_RELAXED) : 0;
+          cf[u] = cc0 + u < nch ? __atomic_load_n(&ci[1], __ATOMIC_RELAXED) : INT_MAX;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          rnew += cn[u];
+          fdrop = min(fdrop, cf[u]);
+        }
       }
       const int fpos = nch ? __atomic_load_n(&si[SI_FPOS], __ATOMIC_RELAXED) : INT_MAX;
       const int e = nch ? __atomic_load_n(&si[SI_ERR], __ATOMIC_RELAXED) : 0;
