@@ -73,6 +73,7 @@ def lib() -> C.CDLL:
                                            _P, C.c_size_t, _P]),
         "akv_segment_attention": (C.c_int, [_P, _P, _P, _P, C.c_int32, C.c_int32, C.c_int32,
                                             C.c_int32, C.c_int32, _P, _P]),
+        "akv_query_state": (C.c_int, [_P, _P, _P, _P, _P, _P]),
         "akv_sync_status": (C.c_int, [_P, _P]),
         "akv_status_string": (C.c_char_p, [C.c_int]),
         "akv_profile_enable": (C.c_int, [_P, C.c_int]),
@@ -283,16 +284,27 @@ class AkvCache:
                                       int(reset)), "akv_profile_read")
         return ms.value, n.value
 
-    # -- state export (for checks; plain tensor reads) ----------------------
+    # -- state export (for checks) -------------------------------------------
+    def query_state(self, stream=None):
+        """akv_query_state: device int32 tensors (lens [B], next_pos [B],
+        positions [B][S], token_ids [B][S]) in active order, -1 past each length."""
+        import torch
+        mk = lambda *sh: torch.empty(sh, dtype=torch.int32, device=self.device)
+        lens, nxt, pos, tok = mk(self.B), mk(self.B), mk(self.B, self.S), mk(self.B, self.S)
+        _check(lib().akv_query_state(self.handle, _ptr(lens), _ptr(nxt), _ptr(pos), _ptr(tok),
+                                     _stream(stream)), "akv_query_state")
+        return lens, nxt, pos, tok
+
     def seq_state(self, b: int):
-        """(token_ids, positions, page ids) of sequence b's active entries, on the host."""
+        """(token_ids, positions, page ids) of sequence b's active entries, on the host
+        (ids and positions through akv_query_state; page ids read from the table)."""
         import numpy as np
-        n = int(self.seq_lens[b].item())
+        lens, _, pos, tok = self.query_state()
+        n = int(lens[b].item())
         npg = (n + PAGE - 1) // PAGE
         pages = self.block_table[b, :npg].cpu().numpy()
-        tok = self.token_ids[self.block_table[b, :npg].long()].reshape(-1)[:n].cpu().numpy()
-        pos = self.positions[self.block_table[b, :npg].long()].reshape(-1)[:n].cpu().numpy()
-        return tok.astype(np.int64), pos.astype(np.int64), pages
+        return (tok[b, :n].cpu().numpy().astype(np.int64),
+                pos[b, :n].cpu().numpy().astype(np.int64), pages)
 
     def gather_rows(self, b: int, layer: int, which: str = "k"):
         """bf16 rows [n, Hkv, d] of sequence b at `layer`, in active order (device tensor)."""

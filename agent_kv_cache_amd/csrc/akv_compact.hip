@@ -679,6 +679,37 @@ hipError_t launch_append(const Dev &d, const int32_t *counts, int64_t n_new,
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// state export: lengths, next positions, and every sequence's positions and
+// token ids in active order (slots past the length read -1)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void query_kernel(Dev d, int32_t *lens, int32_t *next,
+                                                     int32_t *pos, int32_t *tok) {
+  const int b = blockIdx.y;
+  const int len = d.lens[b];
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    if (lens) lens[b] = len;
+    if (next) next[b] = d.next_pos[b];
+  }
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= d.S || !(pos || tok)) return;
+  int p = -1, t = -1;
+  if (j < len) {
+    const size_t slot = (size_t)d.table[(size_t)b * d.maxpg + j / kPage] * kPage + j % kPage;
+    p = d.pos[slot];
+    t = d.tok[slot];
+  }
+  if (pos) pos[(size_t)b * d.S + j] = p;
+  if (tok) tok[(size_t)b * d.S + j] = t;
+}
+
+hipError_t launch_query(const Dev &d, int32_t *lens, int32_t *next, int32_t *pos, int32_t *tok,
+                        hipStream_t st) {
+  hipLaunchKernelGGL(query_kernel, dim3((unsigned)((d.S + 255) / 256), (unsigned)d.B), dim3(256),
+                     0, st, d, lens, next, pos, tok);
+  return hipGetLastError();
+}
+
 hipError_t launch_release(const Dev &d, const uint8_t *sel, hipStream_t st) {
   hipLaunchKernelGGL(release_kernel, dim3(1), dim3(kPlanThreads), 0, st, d, sel);
   return hipGetLastError();

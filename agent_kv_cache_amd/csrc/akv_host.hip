@@ -310,6 +310,15 @@ akv_status akv_release(akv_cache *c, const uint8_t *release, void *stream) {
   return AKV_OK;
 }
 
+akv_status akv_query_state(akv_cache *c, int32_t *seq_lens, int32_t *next_pos,
+                           int32_t *positions, int32_t *token_ids, void *stream) {
+  if (!c) return AKV_ERR_ARG;
+  if (!seq_lens && !next_pos && !positions && !token_ids) return AKV_OK;
+  AKV_HIP(akv::launch_query(c->dev, seq_lens, next_pos, positions, token_ids,
+                            reinterpret_cast<hipStream_t>(stream)));
+  return AKV_OK;
+}
+
 akv_status akv_drop(akv_cache *c, const uint8_t *drop_mask, void *stream) {
   if (!c || !drop_mask || !aligned(drop_mask, 16)) return AKV_ERR_ARG;
   return run_compaction(c, drop_mask, nullptr, nullptr, akv::M_DROP, stream);

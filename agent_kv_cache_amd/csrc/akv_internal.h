@@ -164,6 +164,8 @@ hipError_t launch_append(const Dev &d, const int32_t *counts, int64_t n_new,
                          const uint16_t *k_new, const uint16_t *v_new,
                          const int32_t *tok_new, bool rope, hipStream_t st);
 hipError_t launch_release(const Dev &d, const uint8_t *sel, hipStream_t st);
+hipError_t launch_query(const Dev &d, int32_t *lens, int32_t *next, int32_t *pos, int32_t *tok,
+                        hipStream_t st);
 hipError_t launch_reset(const Dev &d, const int32_t *order_dev, hipStream_t st);
 hipError_t launch_attention(const Dev &d, const uint16_t *q, const int32_t *active_len,
                             int l0, int nL, int Hq, uint16_t *out, float *part,

@@ -248,6 +248,21 @@ akv_status akv_segment_attention(akv_cache *c, const uint16_t *q, const int32_t 
                                  int32_t layer_begin, int32_t n_layers, int32_t n_q_heads,
                                  uint16_t *out, void *stream);
 
+/* Export of the state the server keeps per sequence ([AKV] sec. 5.3: the
+ * positions of the active tokens and the next position; [CE] sec. 3.1:
+ * active index, RoPE position and token are separate): one gather kernel on
+ * `stream`, outputs in active order.
+ *   seq_lens  : DEVICE int32 [B] or NULL
+ *   next_pos  : DEVICE int32 [B] or NULL
+ *   positions : DEVICE int32 [B][S] or NULL; entry j of sequence b at
+ *               [b][j], -1 past its length
+ *   token_ids : DEVICE int32 [B][S] or NULL; same layout
+ * All outputs are caller-owned; copy them to the host after the stream
+ * (the call does not synchronise).  Reads only; works while an error is
+ * latched.  Errors: AKV_ERR_ARG (null cache), AKV_ERR_HIP. */
+akv_status akv_query_state(akv_cache *c, int32_t *seq_lens, int32_t *next_pos,
+                           int32_t *positions, int32_t *token_ids, void *stream);
+
 /* Synchronise `stream`, return the latched device error (AKV_OK if none)
  * and clear it. */
 akv_status akv_sync_status(akv_cache *c, void *stream);
