@@ -120,6 +120,9 @@ void akv_cache_free(akv_cache *c);
  * free_count = NB, and the free stack such that pages are handed out in the
  * order page_order[0], page_order[1], ... (page_order: HOST int32 [NB], a
  * permutation of 0..NB-1; NULL = 0, 1, 2, ...).  Clears the error word.
+ * With page_order the call synchronises `stream` and copies the order to the
+ * device before the reset kernel (set-up only; every other call except
+ * akv_sync_status / akv_profile_read is asynchronous).
  * Errors: AKV_ERR_ARG (not a permutation), AKV_ERR_HIP. */
 akv_status akv_cache_reset(akv_cache *c, const int32_t *page_order, void *stream);
 
