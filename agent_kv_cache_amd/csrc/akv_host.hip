@@ -215,7 +215,7 @@ akv_status akv_cache_init(const akv_cache_desc *d, akv_cache **out) {
     delete c;
     return AKV_ERR_HIP;
   }
-  c->move_grid = akv::move_blocks_per_cu(d->head_dim) * c->n_cu;
+  c->move_grid = akv::move_blocks_per_cu(d->head_dim, rd) * c->n_cu;
   {
     // One-shot launch size: every block the op could need (one per layer
     // group of each page it could rebuild), at most AKV_MOVE_ONESHOT_CAP

@@ -159,7 +159,7 @@ hipError_t launch_plan(const Dev &d, const uint8_t *mask, const int32_t *new_pos
                        const int32_t *old_pos, int mode, hipStream_t st);
 hipError_t launch_move(const Dev &d, int mode, int grid, int oneshot_cap, hipStream_t st);
 hipError_t launch_commit(const Dev &d, hipStream_t st);
-int move_blocks_per_cu(int D);
+int move_blocks_per_cu(int D, int RD);
 hipError_t launch_append(const Dev &d, const int32_t *counts, int64_t n_new,
                          const uint16_t *k_new, const uint16_t *v_new,
                          const int32_t *tok_new, bool rope, hipStream_t st);

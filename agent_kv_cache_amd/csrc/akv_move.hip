@@ -38,10 +38,13 @@ namespace akv {
 #define AKV_MOVE_NT 1          // nontemporal hint on the streamed KV accesses
 #endif
 #ifndef AKV_MOVE_FR64
-#define AKV_MOVE_FR64 1        // full-row thread mapping at d = 64 (full RoPE)
+#define AKV_MOVE_FR64 1        // full-row thread mapping at d = 64
 #endif
-#ifndef AKV_MOVE_FR64_NT
-#define AKV_MOVE_FR64_NT 1     // nontemporal hint with the full-row mapping
+#ifndef AKV_MOVE_FR_PARTIAL
+#define AKV_MOVE_FR_PARTIAL 1  // full-row thread mapping for partial RoPE
+#endif
+#ifndef AKV_MOVE_FR_NT
+#define AKV_MOVE_FR_NT 1       // nontemporal hint with the full-row mapping
 #endif
 
 constexpr int kMoveThreads = 256;
@@ -73,12 +76,14 @@ __device__ __forceinline__ void st_stream(uint16_t *p, u32x4 v) {
 // sources, deltas, cos/sin) is done once per page it touches.  One-shot
 // launch: block b takes page b mod pages at layer group b / pages.
 //
-// Thread mapping.  Half rows (FR = false): a thread holds chunk pc of the x
-// half of a row and the matching chunk of the y half (8 NeoX pairs), loaded
-// by two instructions.  Full rows (FR = true; full RoPE at d = 64, where a
-// row is one 128-B line): a thread holds one chunk c of the row, so every
-// load instruction covers whole lines, and the partner chunk c ^ (d/16) is
-// read from the lane that holds it (the same row's lanes are adjacent).
+// Thread mapping.  Half rows (FR = false; full RoPE at d = 128): a thread
+// holds chunk pc of the x half of a row and the matching chunk of the y half
+// (8 NeoX pairs), loaded by two instructions that each cover whole 128-B
+// lines.  Full rows (FR = true; d = 64, where a row is one line, and partial
+// RoPE, where x and y chunks are 64-B pieces): a thread holds one chunk c of
+// the row, so every load instruction covers whole lines; a rotary chunk's
+// partner (c +- r/16) is read from the lane that holds it (the same row's
+// lanes are adjacent), tail chunks are only copied.
 template <int D, bool NT, bool ONESHOT, bool FR>
 __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(Dev d, int mode,
                                                                                  int oneshot_cap) {
@@ -127,12 +132,16 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
   const int r = (t % TPH) / CPR, pc = t % CPR, slot = t / TPH;
   // Half rows: chunk pc of a row, a rotary chunk pairs dims [8pc, 8pc+8)
   // with the same dims + RD/2; past the rotary part ([RD, D), partial RoPE)
-  // chunks are only copied, paired the same way over the tail.  Full rows
-  // (RD == D): chunk pc holds dims [8pc, 8pc+8); pc < CH is an x chunk.
+  // chunks are only copied, paired the same way over the tail.  Full rows:
+  // chunk pc holds dims [8pc, 8pc+8); chunks below RD/8 are rotary, an x
+  // chunk when pc < RD/16 (partner pc + RD/16), else a y chunk (partner
+  // pc - RD/16).
   const int rch = d.RD / 16;
-  const bool rot_chunk = FR || pc < rch;
+  const bool rot_chunk = FR ? pc < 2 * rch : pc < rch;
+  const bool x_chunk = pc < rch;
   const int xo = (FR || rot_chunk) ? 8 * pc : d.RD + 8 * (pc - rch);
   const int yoff = FR ? 0 : rot_chunk ? d.RD / 2 : (D - d.RD) / 2;
+  const int partner_lane = (int)(threadIdx.x & 63) + (x_chunk ? rch : -rch);
   const size_t S = (size_t)d.S;
   const PoolStrides ps = pool_strides(d.NB, d.H, D);
   const size_t hstride = ps.head, lstride = ps.layer;
@@ -248,7 +257,7 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
     }
     // cos/sin of this thread's 8 pairs stay in LDS and are read per use
     const double2 *cs_row = &s_cs[(rot_any && delta != 0) ? s_rep[r] : 0]
-                                 [FR ? 8 * (pc % CH) : rot_chunk ? 8 * pc : 0];
+                                 [!rot_chunk ? 0 : x_chunk ? 8 * pc : 8 * (pc - rch)];
     while (more) {
       uint16_t *pool = plane ? d.v : d.k;
       const bool rot_plane = plane == 0 && turn;
@@ -258,11 +267,11 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
         if constexpr (FR) {
           if (rot_plane) {
             // both lanes of a pair hold the same row, so they turn together
-            const u32x4 other = {(uint32_t)__shfl_xor((int)lo[u].x, CH, 64),
-                                 (uint32_t)__shfl_xor((int)lo[u].y, CH, 64),
-                                 (uint32_t)__shfl_xor((int)lo[u].z, CH, 64),
-                                 (uint32_t)__shfl_xor((int)lo[u].w, CH, 64)};
-            lo[u] = rotate8_side(lo[u], other, pc < CH, cs_row);
+            const u32x4 other = {(uint32_t)__shfl((int)lo[u].x, partner_lane, 64),
+                                 (uint32_t)__shfl((int)lo[u].y, partner_lane, 64),
+                                 (uint32_t)__shfl((int)lo[u].z, partner_lane, 64),
+                                 (uint32_t)__shfl((int)lo[u].w, partner_lane, 64)};
+            lo[u] = rotate8_side(lo[u], other, x_chunk, cs_row);
           }
           st_stream<NT>(pool + dofs[u], lo[u]);
         } else {
@@ -291,31 +300,46 @@ static void launch_move_pair(const Dev &d, int mode, int grid, int oneshot_cap, 
     hipLaunchKernelGGL((move_kernel<D, NT, false, FR>), dim3(grid), b, 0, st, d, mode, oneshot_cap);
 }
 
+// Whether a cache's moves use the full-row mapping.
+static bool move_full_rows(int D, int RD) {
+  return D == 64 ? AKV_MOVE_FR64 != 0 : (RD < D && AKV_MOVE_FR_PARTIAL != 0);
+}
+
 // The one-shot launch (oneshot_cap blocks), then the persistent grid (grid
 // workgroups; 0 when no op of this cache can exceed the one-shot launch);
-// each checks the planned unit count and only one of them moves.  Full RoPE
-// at d = 128 (half rows of whole lines) and at d = 64 (full rows) uses the
-// nontemporal hint; partial RoPE uses cached half-row accesses.
+// each checks the planned unit count and only one of them moves.  Every
+// mapping whose load instructions cover whole lines uses the nontemporal
+// hint (half rows of full RoPE at d = 128, full rows); the half-row mapping
+// of partial RoPE (64-B pieces) uses cached accesses.
 hipError_t launch_move(const Dev &d, int mode, int grid, int oneshot_cap, hipStream_t st) {
-  const bool full = d.RD == d.D;
-  if (d.D == 128) {
-    if (AKV_MOVE_NT && full) launch_move_pair<128, true, false>(d, mode, grid, oneshot_cap, st);
+  constexpr bool kFrNT = AKV_MOVE_FR_NT != 0;
+  if (move_full_rows(d.D, d.RD)) {
+    if (d.D == 128) launch_move_pair<128, kFrNT, true>(d, mode, grid, oneshot_cap, st);
+    else launch_move_pair<64, kFrNT, true>(d, mode, grid, oneshot_cap, st);
+  } else if (d.D == 128) {
+    if (AKV_MOVE_NT && d.RD == d.D) launch_move_pair<128, true, false>(d, mode, grid, oneshot_cap, st);
     else launch_move_pair<128, false, false>(d, mode, grid, oneshot_cap, st);
   } else {
-    if (AKV_MOVE_FR64 && full) launch_move_pair<64, AKV_MOVE_FR64_NT != 0, true>(d, mode, grid, oneshot_cap, st);
-    else launch_move_pair<64, false, false>(d, mode, grid, oneshot_cap, st);
+    launch_move_pair<64, false, false>(d, mode, grid, oneshot_cap, st);
   }
   return hipGetLastError();
 }
 
-int move_blocks_per_cu(int D) {
+int move_blocks_per_cu(int D, int RD) {
+  constexpr bool kFrNT = AKV_MOVE_FR_NT != 0;
+  const bool fr = move_full_rows(D, RD);
   int n = 0;
-  const hipError_t e =
-      (D == 128) ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, move_kernel<128, true, false, false>,
-                                                                kMoveThreads, 0)
-                 : hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                       &n, move_kernel<64, AKV_MOVE_FR64_NT != 0, false, AKV_MOVE_FR64 != 0>,
-                       kMoveThreads, 0);
+  hipError_t e;
+  if (D == 128)
+    e = fr ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, move_kernel<128, kFrNT, false, true>,
+                                                          kMoveThreads, 0)
+           : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, move_kernel<128, true, false, false>,
+                                                          kMoveThreads, 0);
+  else
+    e = fr ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, move_kernel<64, kFrNT, false, true>,
+                                                          kMoveThreads, 0)
+           : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, move_kernel<64, false, false, false>,
+                                                          kMoveThreads, 0);
   return (e == hipSuccess && n > 0) ? n : 2;
 }
 
