@@ -29,9 +29,9 @@ def _gpu():
     lib()  # fail loudly if the library is missing
 
 
-def _setup(shape, lens, seed=1, extra=None, order_seed=None, maxpg=None):
+def _setup(shape, lens, seed=1, extra=None, order_seed=None, maxpg=None, **cache_kw):
     cache = Hn.make_cache(shape, lens, sum(Hn.pages_for(n) for n in lens) if extra is None else extra,
-                          max_blocks_per_seq=maxpg)
+                          max_blocks_per_seq=maxpg, **cache_kw)
     order = None
     if order_seed is not None:
         order = np.random.default_rng(order_seed).permutation(cache.NB).astype(np.int32)
@@ -198,18 +198,22 @@ def test_fused_equals_sequential_bitwise():
     assert np.array_equal(a.next_pos.cpu().numpy(), b.next_pos.cpu().numpy())
 
 
-def test_move_launch_shapes_agree_bitwise(monkeypatch):
+@pytest.mark.parametrize("d,r", [(128, 128), (64, 64), (128, 64), (64, 48)])
+def test_move_launch_shapes_agree_bitwise(monkeypatch, d, r):
     """The one-shot and the persistent move grid give identical bytes: the
     same ops on two identically filled caches, the second with the one-shot
-    grid switched off (AKV_MOVE_ONESHOT_CAP=0, read at cache creation)."""
-    sh = W.Shape(3, 2, 128, 8, 5.0e5)
+    grid switched off (AKV_MOVE_ONESHOT_CAP=0, read at cache creation).  Head
+    sizes and rotary widths cover both thread mappings of the move (half rows
+    for full RoPE at d = 128, full rows otherwise)."""
+    sh = W.Shape(3, 2, d, 8, 5.0e5)
     lens = [700, 45, 1000, 0]
     rng = np.random.default_rng(17)
     masks = [(rng.uniform(size=n) < 0.35).astype(np.uint8) for n in lens]
-    say("case one-shot vs persistent move grid")
-    a = _setup(sh, lens, seed=5, extra=2 * sum(Hn.pages_for(n) for n in lens) + 8, order_seed=6)
+    say(f"case one-shot vs persistent move grid d={d} r={r}")
+    kw = {"rotary_dim": r} if r != d else {}
+    a = _setup(sh, lens, seed=5, extra=2 * sum(Hn.pages_for(n) for n in lens) + 8, order_seed=6, **kw)
     monkeypatch.setenv("AKV_MOVE_ONESHOT_CAP", "0")
-    b = _setup(sh, lens, seed=5, extra=2 * sum(Hn.pages_for(n) for n in lens) + 8, order_seed=6)
+    b = _setup(sh, lens, seed=5, extra=2 * sum(Hn.pages_for(n) for n in lens) + 8, order_seed=6, **kw)
     monkeypatch.delenv("AKV_MOVE_ONESHOT_CAP")
     for c in (a, b):
         c.drop_reposition(Hn.mask_tensor(c, masks))
