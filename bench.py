@@ -558,7 +558,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the hot path shards by kv head / layer with no exchange; see DESIGN.md).",
+              "(the hot path shards by kv head / layer with no exchange).",
               file=sys.stderr)
         sys.exit(2)
 

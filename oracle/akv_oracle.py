@@ -52,7 +52,7 @@ What is computed (every function below is the plain definition):
   in the window (positions, not indices, after a drop); frequencies may be
   replaced by a caller table (Llama 3.1 / YaRN rules below, not on the pages).
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
   pairing/sign of RoPE (NeoX half split, +p*theta), theta_i without scaling,
   one fp64 rounding to bf16 (round half to even) per rotated element, no
   self-token and no sinks in decode, scale 1/sqrt(d), 1 = drop in masks.
