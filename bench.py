@@ -557,7 +557,7 @@ def main():
                          "scale the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the hot path shards by kv head / layer with no exchange).",
               file=sys.stderr)
         sys.exit(2)
