@@ -92,31 +92,31 @@ def spans_to_mask(n: int, spans: List[Tuple[int, int]]) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
-# The five configurations
+# The workloads (named by what they are)
 # ---------------------------------------------------------------------------
 SHAPES: Dict[str, Shape] = {
-    "c1": Shape(1, 8, 128, 32, 1.0e4),
-    "c2": Shape(32, 8, 128, 32, 5.0e5),
-    "c3": Shape(32, 8, 128, 32, 5.0e5),
-    "c4": Shape(36, 8, 64, 64, 1.5e5),
-    "c5": Shape(80, 8, 128, 64, 5.0e5),
+    "one_layer_4k": Shape(1, 8, 128, 32, 1.0e4),
+    "llama8b_32k": Shape(32, 8, 128, 32, 5.0e5),
+    "ragged_batch_64": Shape(32, 8, 128, 32, 5.0e5),
+    "history_50_turns": Shape(36, 8, 64, 64, 1.5e5),
+    "llama70b_4x64k": Shape(80, 8, 128, 64, 5.0e5),
 }
 
 
-def c1() -> Workload:
+def one_layer_4k() -> Workload:
     """1 layer, 8 kv heads, d=128, 4096 tokens; drop [1024, 2048); 32 q heads."""
     n = 4096
     sp = [(1024, 1024)]
-    return Workload("c1", SHAPES["c1"], [n], [spans_to_mask(n, sp)], None, 101,
+    return Workload("one_layer_4k", SHAPES["one_layer_4k"], [n], [spans_to_mask(n, sp)], None, 101,
                     "single sequence, 1 layer, span [1024,2048) dropped", [sp])
 
 
-def c2() -> Workload:
+def llama8b_32k() -> Workload:
     """Llama-3.1-8B shape, 32768 tokens, six tool spans of 1024..4096 tokens."""
     rng = _rng(2)
     n = 32768
     sp = place_spans(n, 6, 1024, 4096, rng)
-    return Workload("c2", SHAPES["c2"], [n], [spans_to_mask(n, sp)], None, 102,
+    return Workload("llama8b_32k", SHAPES["llama8b_32k"], [n], [spans_to_mask(n, sp)], None, 102,
                     "Llama-8B shape, 32768 tokens, 6 tool spans dropped", [sp])
 
 
@@ -134,25 +134,25 @@ def _span_batch(name: str, lens: np.ndarray, frac: float, rng, shuffle: bool,
                     data_seed, desc, spans)
 
 
-def c3(n_seqs: int = 64) -> Workload:
+def ragged_batch_64(n_seqs: int = 64) -> Workload:
     """64 ragged sequences, lengths lognormal (median 16K, sigma 0.5, clipped
     to [8K, 64K]), shuffled page table, tool spans covering ~40% of tokens."""
     rng = _rng(3)
     z = rng.standard_normal(64)
     lens = np.clip(np.round(16384 * np.exp(0.5 * z)), 8192, 65536).astype(np.int64)
-    return _span_batch("c3", lens[:n_seqs], 0.4, rng, True, 103,
+    return _span_batch("ragged_batch_64", lens[:n_seqs], 0.4, rng, True, 103,
                        "64 ragged sequences, shuffled pages, ~40% dropped")
 
 
-def c5() -> Workload:
+def llama70b_4x64k() -> Workload:
     """Llama-3.1-70B shape, 4 x 65536 tokens, tool spans covering ~50%."""
     rng = _rng(5)
-    return _span_batch("c5", np.full(4, 65536, dtype=np.int64), 0.5, rng, False,
+    return _span_batch("llama70b_4x64k", np.full(4, 65536, dtype=np.int64), 0.5, rng, False,
                        105, "Llama-70B shape, 4 x 65536 tokens, ~50% dropped")
 
 
 # ---------------------------------------------------------------------------
-# Long operation history (config 4)
+# Long operation history of an agent run
 # ---------------------------------------------------------------------------
 @dataclass
 class History:
@@ -184,7 +184,7 @@ class History:
         return top
 
 
-def c4_history(seed: int = 4, turns: int = 50, total: int = 131072,
+def history_50_turns(seed: int = 4, turns: int = 50, total: int = 131072,
                keep_turns: int = 3, repos_every: int = 3,
                assistant_range: Tuple[int, int] = (64, 512),
                tool_range: Tuple[int, int] = (512, 8192)) -> History:
@@ -203,7 +203,7 @@ def c4_history(seed: int = 4, turns: int = 50, total: int = 131072,
     need = total - turns * (lo_a + lo_u)
     c = need / ((hi_a - lo_a) * a.sum() + (hi_u - lo_u) * u.sum())
     if not 0.0 < c <= 1.0:
-        raise ValueError("c4_history: lengths cannot reach the total within range")
+        raise ValueError("history_50_turns: lengths cannot reach the total within range")
     A = np.floor(lo_a + c * (hi_a - lo_a) * a).astype(np.int64)
     U = np.floor(lo_u + c * (hi_u - lo_u) * u).astype(np.int64)
     U[-1] += total - int(A.sum() + U.sum())
@@ -237,7 +237,8 @@ def mask_for_messages(token_ids: np.ndarray, hist: History, msg_ids) -> np.ndarr
     return m
 
 
-WORKLOADS = {"c1": c1, "c2": c2, "c3": c3, "c5": c5}
+WORKLOADS = {"one_layer_4k": one_layer_4k, "llama8b_32k": llama8b_32k,
+             "ragged_batch_64": ragged_batch_64, "llama70b_4x64k": llama70b_4x64k}
 
 
 @dataclass
@@ -256,14 +257,14 @@ class Restore:
     description: str = ""
 
 
-def restore_c2() -> Restore:
-    """The c2 request (32768 tokens, six tool spans) recomputed in seven
+def restore_llama8b_32k() -> Restore:
+    """The Llama-8B-shaped request (32768 tokens, six tool spans) recomputed in seven
     segments.  Segment 0 is the text before the first span; segment j >= 1
     is tool span j plus the text up to the next span.  Span j stays visible
     to its own segment and is dropped (with reposition) before the next one,
     so segment j attends over: the text of segments 0..j-1 without their
     spans, then its own tokens."""
-    wl = c2()
+    wl = llama8b_32k()
     n = wl.seq_lens[0]
     sp = sorted(wl.spans[0])
     starts = [0] + [s for s, _ in sp] + [n]
@@ -275,8 +276,8 @@ def restore_c2() -> Restore:
             m[s:s + ln] = 1
         m[hi:] = 1
         versions.append((m, hi - lo))
-    return Restore("restore_c2", wl.shape, n, versions, wl.data_seed,
-                   "c2 request restored in 7 segments over 7 position versions")
+    return Restore("restore_llama8b_32k", wl.shape, n, versions, wl.data_seed,
+                   "the Llama-8B-shaped request restored in 7 segments over 7 position versions")
 
 
 # ---------------------------------------------------------------------------

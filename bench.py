@@ -158,8 +158,8 @@ def run_history(args):
     from agent_kv_cache_amd import harness as Hn
     from agent_kv_cache_amd import workloads as W
 
-    sh = W.SHAPES["c4"]
-    hist = W.c4_history()
+    sh = W.SHAPES["history_50_turns"]
+    hist = W.history_50_turns()
     row = sh.n_layers * sh.n_kv_heads * sh.head_dim * 2
     # per-sequence page capacity: the run's largest active length, in whole
     # plan chunks of 256 pages (it also bounds the move's one-shot grid)
@@ -223,7 +223,7 @@ def run_history(args):
     att_ms = (cache.profile_read("attn")[0] + cache.profile_read("combine")[0]) / args.steps
     b_att = len(tok) * 2 * row + 2 * sh.n_layers * sh.n_q_heads * sh.head_dim * 2
     return {
-        "metric": METRIC, "workload": "c4: 50-turn history, 131072 tokens appended, "
+        "metric": METRIC, "workload": "history_50_turns: 50-turn history, 131072 tokens appended, "
         "L=36 Hkv=8 d=64, 47 drops / 16 repositions, decode 64 q heads",
         "ops": n_ops, "ops_ms_total": round(tot_ms, 4), "ops_bytes_total": int(tot_bytes),
         "drop_reposition_gbps": round(tot_bytes / (tot_ms * 1e-3) / 1e9, 1),
@@ -326,7 +326,7 @@ def restore_cpu_baseline(rs, rows_per_segment: int):
 
 
 def run_restore(args):
-    """Restore of the c2 request after eviction: one step = reset the cache
+    """Restore of the Llama-8B-shaped request after eviction: one step = reset the cache
     metadata, make the 7 position versions with akv_fork (drop + canonical
     reposition, source untouched), then one segment-batch attention launch
     over all 32 layers for the 7 segments (32768 query rows)."""
@@ -335,7 +335,7 @@ def run_restore(args):
     from agent_kv_cache_amd import harness as Hn
     from agent_kv_cache_amd import workloads as W
 
-    rs = W.restore_c2()
+    rs = W.restore_llama8b_32k()
     sh = rs.shape
     nv = len(rs.versions)
     cnt = restore_counts(rs)
@@ -395,7 +395,7 @@ def run_restore(args):
     move_b = sum(c["len"] * 2 * (sh.n_layers * sh.n_kv_heads * sh.head_dim * 2) * 2 for c in cnt)
     seg_tf = flops / (seg_ms * 1e-3) / 1e12
     peak_tf = 2500.0
-    traffic = counted_traffic("segment_fa_kernel_restore_c2_counters.json")
+    traffic = counted_traffic("segment_fa_kernel_restore_llama8b_32k_counters.json")
     res = {
         "metric": "restore: segment-batch attention TFLOP/s (bf16 MFMA) and fork GB/s, 1 GPU",
         "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
@@ -434,7 +434,7 @@ def run_restore(args):
 
 
 def run_append(args):
-    """Append of the c2 request's 32768 tokens in one call (a prefill's KV
+    """Append of the Llama-8B-shaped request's 32768 tokens in one call (a prefill's KV
     write), plain (keys already rotated) and with the RoPE step fused in
     (akv_append_rope).  One step = reset the cache metadata + one append.
     Algorithmic bytes: K and V of every new token read once and written once,
@@ -444,7 +444,7 @@ def run_append(args):
     from agent_kv_cache_amd import harness as Hn
     from agent_kv_cache_amd import workloads as W
 
-    wl = W.c2()
+    wl = W.llama8b_32k()
     sh = wl.shape
     n = wl.seq_lens[0]
     ropt = rope_options(args, sh)
@@ -532,8 +532,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c2",
-                    choices=["c1", "c2", "c3", "c4", "c5", "restore", "append"])
+    ap.add_argument("--workload", default="llama8b_32k",
+                    choices=["one_layer_4k", "llama8b_32k", "ragged_batch_64", "history_50_turns",
+                             "llama70b_4x64k", "restore", "append"])
     ap.add_argument("--cpu-rows", type=int, default=256,
                     help="restore: rows per segment in the oracle sample")
     ap.add_argument("--rotary-dim", type=int, default=0,
@@ -549,7 +550,7 @@ def main():
                     help="also time the step captured once in a HIP graph and replayed "
                          "(reported as graph_ms_per_step; per-kernel times stay eager)")
     ap.add_argument("--cpu-layer-stride", type=int, default=0,
-                    help="oracle sample: every n-th layer (0 = all layers for c1/c2, "
+                    help="oracle sample: every n-th layer (0 = all layers for one_layer_4k / llama8b_32k, "
                          "every 8th for the larger workloads)")
     ap.add_argument("--calibrate", type=int, default=0, metavar="BYTES",
                     help="instead of the workload, time plain device copy / fill / read "
@@ -573,7 +574,7 @@ def main():
         print(json.dumps(calibrate(args.calibrate, args.steps)), flush=True)
         return
     lib()
-    if args.workload == "c4":
+    if args.workload == "history_50_turns":
         print(json.dumps(run_history(args)), flush=True)
         return
     if args.workload == "restore":
@@ -718,7 +719,7 @@ def main():
         res["graph_ms_per_step"] = round(gms, 4)
         res["graph_value"] = round((ab["b_dr"] + ab["b_att"]) / (gms * 1e-3) / 1e9, 2)
     if not args.no_cpu_baseline and not ropt:
-        stride = args.cpu_layer_stride or (1 if wl.name in ("c1", "c2") else 8)
+        stride = args.cpu_layer_stride or (1 if wl.name in ("one_layer_4k", "llama8b_32k") else 8)
         res["cpu_baseline"] = cpu_baseline(wl, stride)
     print(json.dumps(res), flush=True)
 

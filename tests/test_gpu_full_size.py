@@ -69,21 +69,21 @@ def _batch_config(wl, seqs, layers):
 
 
 @pytest.mark.timeout(600)
-def test_c5_llama70b_shape_full():
-    _batch_config(W.c5(), seqs=[0, 3], layers=[0, 40, 79])
+def test_llama70b_shape_full():
+    _batch_config(W.llama70b_4x64k(), seqs=[0, 3], layers=[0, 40, 79])
 
 
 @pytest.mark.timeout(900)
-def test_c3_ragged_batch_full():
-    _batch_config(W.c3(), seqs=[0, 21, 63], layers=[0, 31])
+def test_ragged_batch_full():
+    _batch_config(W.ragged_batch_64(), seqs=[0, 21, 63], layers=[0, 31])
 
 
 @pytest.mark.timeout(600)
-def test_c4_long_history_replay():
+def test_long_history_replay():
     """50-turn history (131072 tokens appended, 47 drops, 16 repositions):
     GPU replay vs oracle replay after every op; final decode with 64 heads."""
-    sh = W.SHAPES["c4"]
-    hist = W.c4_history()
+    sh = W.SHAPES["history_50_turns"]
+    hist = W.history_50_turns()
     layers = [0, 35]
     t0 = time.time()
     # per-sequence page capacity: the run's largest active length, in whole
@@ -129,11 +129,11 @@ def test_c4_long_history_replay():
             check_meta(cache, meta)
             worst = check_kv(cache, kvo, layers=layers, k_ulp=max(1, n_rot))
         if step % 20 == 0:
-            say(f"c4 op {step}/{len(hist.ops)} {op[0]} active {len(meta.seqs[0])} "
+            say(f"history op {step}/{len(hist.ops)} {op[0]} active {len(meta.seqs[0])} "
                 f"next_pos {meta.seqs[0].next_pos} ({time.time() - t0:.0f}s)")
-    say(f"c4 final: active {len(meta.seqs[0])}, next_pos {meta.seqs[0].next_pos}, "
+    say(f"history final: active {len(meta.seqs[0])}, next_pos {meta.seqs[0].next_pos}, "
         f"worst K ulp {worst}")
     q = q_tensor(sh, 1, sh.n_layers, 204, device="cuda")
     out = _decode(cache, q)
     err = check_attention(cache, kvo, q, out, layers=layers)
-    say(f"c4 attention max abs err {err:.2e}")
+    say(f"history attention max abs err {err:.2e}")

@@ -53,10 +53,10 @@ def _decode(cache, q, active=None):
 # ---------------------------------------------------------------------------
 # configuration 1, full
 # ---------------------------------------------------------------------------
-def test_c1_drop_reposition_decode():
-    wl = W.c1()
+def test_one_layer_drop_reposition_decode():
+    wl = W.one_layer_4k()
     sh = wl.shape
-    say("case c1: append 4096, drop [1024,2048) + repos, decode 32 heads")
+    say("case one_layer_4k: append 4096, drop [1024,2048) + repos, decode 32 heads")
     cache = _setup(sh, wl.seq_lens, seed=wl.data_seed)
     oc = oracle_for(sh, wl.seq_lens, wl.data_seed)
     check_meta(cache, oc)
@@ -67,11 +67,11 @@ def test_c1_drop_reposition_decode():
     check_meta(cache, oc)
     assert int(cache.next_pos[0]) == 3072
     worst = check_kv(cache, oc, k_ulp=1)
-    say("c1 worst K ulp", worst)
+    say("one_layer_4k worst K ulp", worst)
     q = q_tensor(sh, 1, 1, 201).to(cache.device)
     out = _decode(cache, q)
     err = check_attention(cache, oc, q, out)
-    say("c1 attention max abs err", err)
+    say("one_layer_4k attention max abs err", err)
 
 
 # ---------------------------------------------------------------------------
@@ -319,27 +319,27 @@ def test_decode_sharp_softmax():
 # configuration 2 at full size (Llama-3.1-8B shape, 32768 tokens)
 # ---------------------------------------------------------------------------
 @pytest.mark.timeout(400)
-def test_c2_full_size_sampled():
-    wl = W.c2()
+def test_llama8b_full_size_sampled():
+    wl = W.llama8b_32k()
     sh = wl.shape
-    say("case c2 full size: fill 32768 tokens x 32 layers")
+    say("case llama8b_32k full size: fill 32768 tokens x 32 layers")
     extra = Hn.moved_pages(wl.seq_lens[0], wl.masks[0])
     cache = Hn.make_cache(sh, wl.seq_lens, extra)
     cache.reset()
     Hn.fill(cache, sh, wl.seq_lens, wl.data_seed, gen_device="cuda")
     layers = [0, 17, 31]
     oc = oracle_for(sh, wl.seq_lens, wl.data_seed, layers=layers, gen_device="cuda")
-    say("c2 drop+repos")
+    say("llama8b_32k drop+repos")
     cache.drop_reposition(Hn.mask_tensor(cache, wl.masks))
     assert cache.sync_status() == 0
     oc.drop_reposition(0, wl.masks[0])
     check_meta(cache, oc)
     worst = check_kv(cache, oc, layers=layers, k_ulp=1)
-    say("c2 worst K ulp on sampled layers", worst)
+    say("llama8b_32k worst K ulp on sampled layers", worst)
     q = q_tensor(sh, 1, sh.n_layers, 202, device="cuda")
     out = _decode(cache, q)
     err = check_attention(cache, oc, q, out, layers=layers)
-    say("c2 attention max abs err (sampled layers)", err)
+    say("llama8b_32k attention max abs err (sampled layers)", err)
 
 
 def test_degenerate_masks_and_positions():

@@ -384,8 +384,8 @@ def test_drop_then_attend_equals_subset_attention():
 # replay (eq. 6)
 # ---------------------------------------------------------------------------
 def test_replay_is_deterministic_and_metadata_only_agrees():
-    from agent_kv_cache_amd.workloads import c4_history, mask_for_messages
-    h = c4_history(turns=12, total=900, assistant_range=(8, 40), tool_range=(16, 120))
+    from agent_kv_cache_amd.workloads import history_50_turns, mask_for_messages
+    h = history_50_turns(turns=12, total=900, assistant_range=(8, 40), tool_range=(16, 120))
 
     def run(with_kv):
         c = O.OracleCache(1, 1, 4, 1.5e5, with_kv=with_kv)

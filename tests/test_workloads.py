@@ -5,9 +5,9 @@ from agent_kv_cache_amd import workloads as W
 from oracle import akv_oracle as O
 
 
-def test_restore_c2_segments_cover_the_request_once():
-    r = W.restore_c2()
-    wl = W.c2()
+def test_restore_segments_cover_the_request_once():
+    r = W.restore_llama8b_32k()
+    wl = W.llama8b_32k()
     n = r.n_tokens
     spans = sorted(wl.spans[0])
     oc = O.OracleCache(1, 1, 8, 1e4, n_seqs=1 + len(r.versions), with_kv=False)
@@ -45,16 +45,16 @@ def test_workloads_are_deterministic():
         assert a.seq_lens == b.seq_lens, name
         for x, y in zip(a.masks, b.masks):
             assert np.array_equal(x, y), name
-    ra, rb = W.restore_c2(), W.restore_c2()
+    ra, rb = W.restore_llama8b_32k(), W.restore_llama8b_32k()
     for (ma, na), (mb, nb) in zip(ra.versions, rb.versions):
         assert na == nb and np.array_equal(ma, mb)
 
 
-def test_c4_max_active_matches_a_metadata_replay():
+def test_history_max_active_matches_a_metadata_replay():
     """The page capacity of the long-history cache is sized from
     History.max_active(); check it against the oracle's own replay of the
     run (lengths after every op, token sets from the message ids)."""
-    h = W.c4_history()
+    h = W.history_50_turns()
     oc = O.OracleCache(1, 1, 8, 1.5e5, n_seqs=1, with_kv=False)
     top = 0
     for op in h.ops:
