@@ -250,8 +250,10 @@ constexpr int kXcds = 8;   // MI355X: 8 accelerator dies, each with its own L2
 // remapped so that die k runs whole groups one after another (groups k,
 // k + 8, k + 16, ...; all query blocks of a group in a row): the ~32 blocks
 // a die runs at once share one group's K/V tiles through that die's L2,
-// instead of every die fetching every group's pages.  Identity when the
-// group count is not a multiple of the die count.
+// instead of every die fetching every group's pages.  Within a group the
+// query blocks run longest first (later rows see more entries), which
+// trims the end of the launch.  Identity when the group count is not a
+// multiple of the die count.
 __device__ __forceinline__ void fa_block(int &bx, int &by, int &bz) {
   bx = blockIdx.x;
   by = blockIdx.y;
@@ -262,7 +264,7 @@ __device__ __forceinline__ void fa_block(int &bx, int &by, int &bz) {
   const long long L = bx + (long long)X * (by + (long long)Y * bz);
   const long long s = L / kXcds;                 // position in the die's order
   const long long gg = (s / X) * kXcds + L % kXcds;
-  bx = (int)(s % X);
+  bx = X - 1 - (int)(s % X);   // a group's longest (latest) query blocks first
   by = (int)(gg % Y);
   bz = (int)(gg / Y);
 }
