@@ -18,7 +18,8 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
                       "include", "akv.h")
 
 STATUS = {0: "AKV_OK", 1: "AKV_ERR_ARG", 2: "AKV_ERR_ORDER", 3: "AKV_ERR_POS_MISMATCH",
-          4: "AKV_ERR_NO_BLOCKS", 5: "AKV_ERR_CAPACITY", 6: "AKV_ERR_HIP"}
+          4: "AKV_ERR_NO_BLOCKS", 5: "AKV_ERR_CAPACITY", 6: "AKV_ERR_HIP",
+          7: "AKV_ERR_SCRATCH"}
 KERNELS = {"plan": 0, "move": 1, "commit": 2, "attn": 3, "combine": 4, "append": 5,
            "segment": 6, "release": 7}
 PAGE = 16
@@ -71,6 +72,8 @@ def lib() -> C.CDLL:
         "akv_decode_workspace_bytes": (C.c_size_t, [_P, C.c_int32, C.c_int32]),
         "akv_decode_attention": (C.c_int, [_P, _P, _P, C.c_int32, C.c_int32, C.c_int32, _P,
                                            _P, C.c_size_t, _P]),
+        "akv_decode_attention_noalloc": (C.c_int, [_P, _P, _P, C.c_int32, C.c_int32, C.c_int32,
+                                                   _P, _P]),
         "akv_segment_attention": (C.c_int, [_P, _P, _P, _P, C.c_int32, C.c_int32, C.c_int32,
                                             C.c_int32, C.c_int32, _P, _P]),
         "akv_query_state": (C.c_int, [_P, _P, _P, _P, _P, _P]),
@@ -258,6 +261,16 @@ class AkvCache:
                                           workspace.numel() * workspace.element_size()
                                           if workspace is not None else 0, _stream(stream)),
                "akv_decode_attention")
+
+    def decode_attention_noalloc(self, q, out, active_len=None, layer_begin: int = 0,
+                                 n_layers: Optional[int] = None, stream=None):
+        """akv_decode_attention with the library's static per-GPU workspace
+        (allocates nothing; concurrent calls on one GPU race)."""
+        nL = self.L - layer_begin if n_layers is None else n_layers
+        _check(lib().akv_decode_attention_noalloc(self.handle, _ptr(q), _ptr(active_len),
+                                                  layer_begin, nL, q.shape[-2], _ptr(out),
+                                                  _stream(stream)),
+               "akv_decode_attention_noalloc")
 
     def segment_attention(self, q, seg_seq, seg_q_off, max_q: int, out, layer_begin: int = 0,
                           n_layers: Optional[int] = None, stream=None):

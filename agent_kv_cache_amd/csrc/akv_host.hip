@@ -6,12 +6,49 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 #include <vector>
 
 #include "akv_internal.h"
 
 using akv::Dev;
+
+// Decode workspace of akv_decode_attention_noalloc, for callers that cannot
+// allocate: one fixed array in the library's code object, so every GPU the
+// library runs on holds its own copy until the process ends.  In host code
+// this name is only a stand-in for the symbol; the device address of each
+// GPU's copy comes from hipGetSymbolAddress (static_scratch_ptr below) and is
+// the only form ever passed to a kernel.
+static __device__ __align__(256) char scratch[AKV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on `device`, looked up once per device with
+// that device current (akv_cache_init calls it for the caller's device).
+hipError_t static_scratch_ptr(int device, void **out) {
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != device) return hipErrorInvalidDevice;
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[device] = p;
+  }
+  *out = g_scratch_ptr[device];
+  return hipSuccess;
+}
+
+}  // namespace
 
 struct akv_cache {
   akv_cache_desc desc;
@@ -24,6 +61,7 @@ struct akv_cache {
   bool move_persistent = true;   // some op could be too large for the one-shot launch
   int attn_per_cu = 2;
   int n_full_layers = 0;   // layers without a sliding window
+  void *noalloc_ws = nullptr;   // this device's copy of `scratch`
   bool profile = false;
   struct Rec {
     int kernel;
@@ -211,7 +249,8 @@ akv_status akv_cache_init(const akv_cache_desc *d, akv_cache **out) {
 
   if (hipGetDevice(&c->device) != hipSuccess ||
       hipDeviceGetAttribute(&c->n_cu, hipDeviceAttributeMultiprocessorCount, c->device) !=
-          hipSuccess) {
+          hipSuccess ||
+      static_scratch_ptr(c->device, &c->noalloc_ws) != hipSuccess) {
     delete c;
     return AKV_ERR_HIP;
   }
@@ -382,10 +421,10 @@ size_t akv_decode_workspace_bytes(const akv_cache *c, int32_t n_layers, int32_t 
                        (size_t)(c->desc.head_dim + 2) * sizeof(float));
 }
 
-akv_status akv_decode_attention(akv_cache *c, const uint16_t *q, const int32_t *active_len,
-                                int32_t layer_begin, int32_t n_layers, int32_t n_q_heads,
-                                uint16_t *out, void *workspace, size_t workspace_bytes,
-                                void *stream) {
+static akv_status decode_impl(akv_cache *c, const uint16_t *q, const int32_t *active_len,
+                              int32_t layer_begin, int32_t n_layers, int32_t n_q_heads,
+                              uint16_t *out, void *workspace, size_t workspace_bytes,
+                              bool static_ws, void *stream) {
   if (!c || !q || !out) return AKV_ERR_ARG;
   if (layer_begin < 0 || n_layers < 1 || layer_begin + n_layers > c->desc.n_layers)
     return AKV_ERR_ARG;
@@ -395,8 +434,16 @@ akv_status akv_decode_attention(akv_cache *c, const uint16_t *q, const int32_t *
   if (!aligned(q, 16) || !aligned(out, 2)) return AKV_ERR_ARG;
   if ((long long)c->desc.n_seqs * n_layers > 65535) return AKV_ERR_ARG;
   const int ns = nsplit_for(c, n_layers);
-  if (ns > 1 && (!workspace || workspace_bytes < akv_decode_workspace_bytes(c, n_layers, n_q_heads)))
-    return AKV_ERR_ARG;
+  if (ns > 1) {
+    const size_t need = akv_decode_workspace_bytes(c, n_layers, n_q_heads);
+    if (static_ws) {
+      if (need > (size_t)AKV_NOALLOC_SCRATCH_BYTES) return AKV_ERR_SCRATCH;
+      if (!c->noalloc_ws) return AKV_ERR_HIP;
+      workspace = c->noalloc_ws;
+    } else if (!workspace || workspace_bytes < need) {
+      return AKV_ERR_ARG;
+    }
+  }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   {
     Timed tm(c, AKV_KERNEL_ATTN, st);
@@ -409,6 +456,22 @@ akv_status akv_decode_attention(akv_cache *c, const uint16_t *q, const int32_t *
                                 c->desc.n_seqs * n_layers * n_q_heads, ns, c->desc.head_dim, st));
   }
   return AKV_OK;
+}
+
+akv_status akv_decode_attention(akv_cache *c, const uint16_t *q, const int32_t *active_len,
+                                int32_t layer_begin, int32_t n_layers, int32_t n_q_heads,
+                                uint16_t *out, void *workspace, size_t workspace_bytes,
+                                void *stream) {
+  return decode_impl(c, q, active_len, layer_begin, n_layers, n_q_heads, out, workspace,
+                     workspace_bytes, false, stream);
+}
+
+akv_status akv_decode_attention_noalloc(akv_cache *c, const uint16_t *q,
+                                        const int32_t *active_len, int32_t layer_begin,
+                                        int32_t n_layers, int32_t n_q_heads, uint16_t *out,
+                                        void *stream) {
+  return decode_impl(c, q, active_len, layer_begin, n_layers, n_q_heads, out, nullptr, 0, true,
+                     stream);
 }
 
 akv_status akv_segment_attention(akv_cache *c, const uint16_t *q, const int32_t *seg_seq,
@@ -458,6 +521,7 @@ const char *akv_status_string(akv_status s) {
     case AKV_ERR_NO_BLOCKS: return "free page pool too small";
     case AKV_ERR_CAPACITY: return "sequence exceeds max_blocks_per_seq";
     case AKV_ERR_HIP: return "HIP runtime error";
+    case AKV_ERR_SCRATCH: return "call needs more than the library's static scratch";
   }
   return "unknown status";
 }

@@ -67,8 +67,13 @@ typedef enum {
   AKV_ERR_POS_MISMATCH = 3, /* old_pos differs from the stored positions */
   AKV_ERR_NO_BLOCKS = 4,    /* free pool too small for the new pages */
   AKV_ERR_CAPACITY = 5,     /* a sequence would exceed max_blocks_per_seq */
-  AKV_ERR_HIP = 6           /* a HIP runtime call failed */
+  AKV_ERR_HIP = 6,          /* a HIP runtime call failed */
+  AKV_ERR_SCRATCH = 7       /* the call needs more than the library's static scratch */
 } akv_status;
+
+/* Bytes of the static decode workspace each GPU holds for
+ * akv_decode_attention_noalloc (8 MiB). */
+#define AKV_NOALLOC_SCRATCH_BYTES (8u << 20)
 
 typedef struct akv_cache akv_cache; /* opaque host-side handle */
 
@@ -226,6 +231,26 @@ akv_status akv_decode_attention(akv_cache *c, const uint16_t *q,
                                 int32_t n_layers, int32_t n_q_heads,
                                 uint16_t *out, void *workspace,
                                 size_t workspace_bytes, void *stream);
+
+/* akv_decode_attention for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, kernels and results as akv_decode_attention
+ * (bit-identical output), without the workspace: the split-K partials go to
+ * a fixed array of AKV_NOALLOC_SCRATCH_BYTES in the library's code object,
+ * one per GPU, held until the process ends (its address is looked up once
+ * per device by akv_cache_init).  The call allocates nothing and never
+ * synchronises.  Every split record is written before it is read, so the
+ * array needs no clearing; it keeps the last call's contents.
+ * All calls on one GPU share that GPU's array: two calls whose work overlaps
+ * in time on one GPU (other streams, other caches, other threads) race and
+ * give wrong results; serialise them on one stream.
+ * Errors: as akv_decode_attention, plus AKV_ERR_SCRATCH (host-checked, before
+ * any launch) when akv_decode_workspace_bytes(c, n_layers, n_q_heads) exceeds
+ * AKV_NOALLOC_SCRATCH_BYTES. */
+akv_status akv_decode_attention_noalloc(akv_cache *c, const uint16_t *q,
+                                        const int32_t *active_len, int32_t layer_begin,
+                                        int32_t n_layers, int32_t n_q_heads, uint16_t *out,
+                                        void *stream);
 
 /* Segment-batch attention ([CE] Appendix A.1.1, Figure 10; Section 4.2.2):
  * the queries of a restore forward, split at drop / reposition boundaries
