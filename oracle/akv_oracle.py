@@ -456,10 +456,27 @@ class OracleCache:
         out = np.zeros((L, Hq, d))
         for l in range(L):
             vis = self.visible(b, n, s.next_pos, l)
-            for h in range(Hq):
-                g = h // G
-                out[l, h] = attend(q[l, h], s.k[vis, l, g], s.v[vis, l, g])
+            rng = _contiguous_range(vis)
+            for g in range(self.n_kv_heads):
+                if rng is None:
+                    k, v = s.k[vis, l, g], s.v[vis, l, g]
+                else:
+                    k = np.ascontiguousarray(s.k[rng[0]:rng[1], l, g])
+                    v = np.ascontiguousarray(s.v[rng[0]:rng[1], l, g])
+                for h in range(g * G, (g + 1) * G):
+                    out[l, h] = attend(q[l, h], k, v)
         return out
+
+
+def _contiguous_range(vis: np.ndarray):
+    """(a, z) when the index set `vis` is the range [a, z), else None.  A
+    visible set always is one (positions strictly increase, so a window keeps
+    a suffix of the prefix); rows are then sliced, not gathered row by row --
+    the same values in the same order."""
+    if vis.size == 0:
+        return 0, 0
+    a, z = int(vis[0]), int(vis[-1]) + 1
+    return (a, z) if z - a == vis.size else None
 
 
 def segment_attention(cache: "OracleCache", segments) -> list:
@@ -480,12 +497,18 @@ def segment_attention(cache: "OracleCache", segments) -> list:
         L, Hq, d = q.shape[1:]
         G = Hq // cache.n_kv_heads
         o = np.zeros_like(q)
-        for i in range(n):
-            me = len(s) - n + i                       # this row's own entry
-            for l in range(L):
-                vis = cache.visible(b, me + 1, int(s.pos[me]), l)
-                for h in range(Hq):
-                    o[i, l, h] = attend(q[i, l, h], s.k[vis, l, h // G], s.v[vis, l, h // G])
+        for l in range(L):
+            for g in range(cache.n_kv_heads):
+                kc = np.ascontiguousarray(s.k[:, l, g])     # [len, d], one copy per head
+                vc = np.ascontiguousarray(s.v[:, l, g])
+                for i in range(n):
+                    me = len(s) - n + i                       # this row's own entry
+                    vis = cache.visible(b, me + 1, int(s.pos[me]), l)
+                    rng = _contiguous_range(vis)
+                    k, v = (kc[vis], vc[vis]) if rng is None else (kc[rng[0]:rng[1]],
+                                                                   vc[rng[0]:rng[1]])
+                    for h in range(g * G, (g + 1) * G):
+                        o[i, l, h] = attend(q[i, l, h], k, v)
         out.append(o)
     return out
 
