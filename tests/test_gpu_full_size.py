@@ -15,8 +15,8 @@ from agent_kv_cache_amd import harness as Hn  # noqa: E402
 from agent_kv_cache_amd import workloads as W  # noqa: E402
 from oracle import akv_oracle as O  # noqa: E402
 
-from gpu_util import (bits, check_attention, check_kv, check_meta, oracle_for,  # noqa: E402
-                      q_tensor, say, to_f64)
+from gpu_util import (attn_errors, bits, check_attention, check_kv, check_meta,  # noqa: E402
+                      oracle_for, oracle_from_device, q_tensor, say, to_f64)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -81,10 +81,16 @@ def test_ragged_batch_full():
 @pytest.mark.timeout(600)
 def test_long_history_replay():
     """50-turn history (131072 tokens appended, 47 drops, 16 repositions):
-    GPU replay vs oracle replay after every op; final decode with 64 heads."""
+    GPU replay vs oracle replay after every op (indices and positions bit-exact
+    end to end).  Keys are held to 1 bf16 step PER OP: before each drop /
+    reposition the sampled layers' K/V bytes are read from the GPU, the oracle
+    applies the same op to those bytes, and the GPU's result must match it
+    (K within 1 step, V bit for bit).  The end-to-end K distance from the
+    oracle's own chain is reported (and bounded by the number of non-identity
+    rotations).  Final decode with 64 query heads."""
     sh = W.SHAPES["history_50_turns"]
     hist = W.history_50_turns()
-    layers = [0, 35]
+    layers = [0, 17, 35]
     t0 = time.time()
     # per-sequence page capacity: the run's largest active length, in whole
     # plan chunks of 256 pages (it also bounds the move's one-shot grid)
@@ -94,6 +100,8 @@ def test_long_history_replay():
     meta = O.OracleCache(sh.n_layers, sh.n_kv_heads, sh.head_dim, sh.rope_base, with_kv=False)
     kvo = O.OracleCache(len(layers), sh.n_kv_heads, sh.head_dim, sh.rope_base)
     n_rot = 0
+    per_op_worst = chain_worst = 0
+    n_checked = 0
     dev = cache.device
     for step, op in enumerate(hist.ops):
         if op[0] == "append":
@@ -108,32 +116,135 @@ def test_long_history_replay():
                        to_f64(v[layers].permute(1, 0, 2, 3)))
         else:
             gtok, _, _ = cache.seq_state(0)
+            pre = oracle_from_device(cache, 0, layers, sh.rope_base)
             if op[0] == "repos":
                 cache.reposition()
-                meta.reposition(0)
-                kvo.reposition(0)
+                for o in (meta, kvo, pre):
+                    o.reposition(0)
             else:
                 gm = W.mask_for_messages(gtok, hist, op[1])
                 om = W.mask_for_messages(meta.seqs[0].token_ids, hist, op[1])
+                assert np.array_equal(gm, om), step
                 if op[0] == "drop":
                     cache.drop(Hn.mask_tensor(cache, [gm]))
-                    meta.drop(0, om)
-                    kvo.drop(0, om)
+                    for o in (meta, kvo, pre):
+                        o.drop(0, om)
                 else:
                     cache.drop_reposition(Hn.mask_tensor(cache, [gm]))
-                    meta.drop_reposition(0, om)
-                    kvo.drop_reposition(0, om)
+                    for o in (meta, kvo, pre):
+                        o.drop_reposition(0, om)
             n_rot += op[0] != "drop"
         assert cache.sync_status() == 0, (step, op)
+        if op[0] != "append":
+            # per op: the GPU result vs the oracle applied to the same bytes
+            check_meta(cache, pre)
+            per_op_worst = max(per_op_worst, check_kv(cache, pre, layers=layers, k_ulp=1))
+            n_checked += 1
         if op[0] != "append" or step == len(hist.ops) - 1:
             check_meta(cache, meta)
-            worst = check_kv(cache, kvo, layers=layers, k_ulp=max(1, n_rot))
+            chain_worst = max(chain_worst, check_kv(cache, kvo, layers=layers,
+                                                    k_ulp=max(1, n_rot)))
         if step % 20 == 0:
             say(f"history op {step}/{len(hist.ops)} {op[0]} active {len(meta.seqs[0])} "
                 f"next_pos {meta.seqs[0].next_pos} ({time.time() - t0:.0f}s)")
-    say(f"history final: active {len(meta.seqs[0])}, next_pos {meta.seqs[0].next_pos}, "
-        f"worst K ulp {worst}")
+    say(f"history final: active {len(meta.seqs[0])}, next_pos {meta.seqs[0].next_pos}; "
+        f"{n_checked} ops each within {per_op_worst} bf16 step(s) of the oracle on the same "
+        f"input bytes (layers {layers}); end-to-end chain distance {chain_worst} step(s) "
+        f"after {n_rot} repositions")
+    assert n_checked == 48
     q = q_tensor(sh, 1, sh.n_layers, 204, device="cuda")
     out = _decode(cache, q)
-    err = check_attention(cache, kvo, q, out, layers=layers)
-    say(f"history attention max abs err {err:.2e}")
+    check_attention(cache, kvo, q, out, layers=layers, what="history decode")
+
+
+def _segment_refs(oc, jobs):
+    """O.segment_attention for each (sequence, q rows) job, one thread per job
+    (the oracle only reads its arrays; BLAS held to one thread per job)."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1), ThreadPoolExecutor(min(8, os.cpu_count() or 1)) as ex:
+        return list(ex.map(lambda job: O.segment_attention(oc, [job])[0], jobs))
+
+
+@pytest.mark.timeout(900)
+def test_restore_full_size():
+    """The timed restore workload at full size: the Llama-8B-shaped request
+    (32768 tokens, 32 layers) forked into its 7 position versions (drop +
+    canonical reposition, source untouched), then one segment-attention
+    launch over all 32 layers for the 7 segments (32768 query rows).
+    Versions' token ids, positions, lengths and next positions are compared
+    bit for bit; K (1 step) and V (bit for bit) on layers 0 and 31; the
+    attention on layers 0 and 31, all 32 query heads, for the last 64 rows of
+    every segment (the longest prefixes) and its first 16 rows (an oracle copy
+    of the version cut after them, positions kept)."""
+    rs = W.restore_llama8b_32k()
+    sh = rs.shape
+    nv = len(rs.versions)
+    layers = [0, sh.n_layers - 1]
+    t0 = time.time()
+    vlen = [int((m == 0).sum()) for m, _ in rs.versions]
+    rows = [n for _, n in rs.versions]
+    lens = [rs.n_tokens] + [0] * nv
+    cache = Hn.make_cache(sh, lens, sum(Hn.pages_for(n) for n in vlen) + 8,
+                          max_blocks_per_seq=Hn.pages_for(rs.n_tokens))
+    cache.reset()
+    Hn.fill(cache, sh, lens, rs.data_seed, gen_device="cuda")
+    dev = cache.device
+    for j, (m, _) in enumerate(rs.versions):
+        dst = [-1] * (1 + nv)
+        dst[0] = 1 + j
+        cache.fork(dst, Hn.mask_tensor(cache, [m]), reposition=True)
+    nq = sum(rows)
+    q = W.randn_bf16((nq, sh.n_layers, sh.n_q_heads, sh.head_dim), 203, device="cuda")
+    out = torch.full_like(q, float("nan"))
+    seg_seq = torch.arange(1, 1 + nv, dtype=torch.int32, device=dev)
+    seg_off = torch.tensor(np.concatenate([[0], np.cumsum(rows)]).astype(np.int32), device=dev)
+    cache.segment_attention(q, seg_seq, seg_off, max(rows), out)
+    assert cache.sync_status() == 0
+    q2 = to_f64(q[:, layers])
+    o2 = to_f64(out[:, layers])
+    del q, out
+    say(f"restore: forks + segment attention on the GPU done ({time.time() - t0:.0f}s)")
+    # the oracle: the source (layers 0 and 31), its 7 versions, and the metadata of all
+    meta = oracle_for(sh, lens, rs.data_seed, with_kv=False)
+    oc = oracle_for(sh, lens, rs.data_seed, layers=layers, gen_device="cuda")
+    for j, (m, _) in enumerate(rs.versions):
+        meta.fork(0, 1 + j, m, reposition=True)
+        oc.fork(0, 1 + j, m, reposition=True)
+    check_meta(cache, meta)
+    worst = check_kv(cache, oc, layers=layers, k_ulp=1, seqs=list(range(1 + nv)))
+    say(f"restore: {nv} versions {vlen}: ids / positions exact, K within {worst} step(s), "
+        f"V exact ({time.time() - t0:.0f}s)")
+    # last 64 rows of every segment: a segment of its own over the same version
+    jobs, picks = [], []
+    o = 0
+    for j, n in enumerate(rows):
+        k = min(64, n)
+        jobs.append((1 + j, q2[o + n - k:o + n]))
+        picks.append(o2[o + n - k:o + n])
+        o += n
+    # first 16 rows: the version cut after them (its positions kept), whose
+    # last 16 entries are then those rows
+    base = len(oc.seqs)
+    oc.seqs.extend(O.SeqState(k=np.zeros((0,) + oc.seqs[0].k.shape[1:]),
+                              v=np.zeros((0,) + oc.seqs[0].v.shape[1:])) for _ in range(nv))
+    o = 0
+    for j, n in enumerate(rows):
+        k = min(16, n)
+        keep = vlen[j] - n + k
+        cut = np.zeros(vlen[j], dtype=np.uint8)
+        cut[keep:] = 1
+        oc.fork(1 + j, base + j, cut)
+        jobs.append((base + j, q2[o:o + k]))
+        picks.append(o2[o:o + k])
+        o += n
+    refs = _segment_refs(oc, jobs)
+    raw = bar = 0.0
+    for got, ref in zip(picks, refs):
+        r, e = attn_errors(got, ref)
+        raw, bar = max(raw, r), max(bar, e)
+    say(f"restore segments (layers {layers}, 80 rows x 32 heads per segment): max |got - ref| "
+        f"{raw:.3e}; less the output's bf16 half-spacing {bar:.3e} ({time.time() - t0:.0f}s)")
+    assert bar <= 1e-2
