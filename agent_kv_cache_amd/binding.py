@@ -76,7 +76,7 @@ def lib() -> C.CDLL:
                                                    _P, _P]),
         "akv_segment_attention": (C.c_int, [_P, _P, _P, _P, C.c_int32, C.c_int32, C.c_int32,
                                             C.c_int32, C.c_int32, _P, _P]),
-        "akv_query_state": (C.c_int, [_P, _P, _P, _P, _P, _P]),
+        "akv_query_state": (C.c_int, [_P, _P, _P, _P, _P, _P, _P]),
         "akv_sync_status": (C.c_int, [_P, _P]),
         "akv_status_string": (C.c_char_p, [C.c_int]),
         "akv_profile_enable": (C.c_int, [_P, C.c_int]),
@@ -298,15 +298,26 @@ class AkvCache:
         return ms.value, n.value
 
     # -- state export (for checks) -------------------------------------------
-    def query_state(self, stream=None):
+    def query_state(self, stream=None, with_last_src: bool = False):
         """akv_query_state: device int32 tensors (lens [B], next_pos [B],
-        positions [B][S], token_ids [B][S]) in active order, -1 past each length."""
+        positions [B][S], token_ids [B][S]) in active order, -1 past each
+        length; with_last_src adds the gather map of the last drop /
+        reposition / fork ([B][S], -1 where the call wrote nothing)."""
         import torch
         mk = lambda *sh: torch.empty(sh, dtype=torch.int32, device=self.device)
         lens, nxt, pos, tok = mk(self.B), mk(self.B), mk(self.B, self.S), mk(self.B, self.S)
+        lsrc = mk(self.B, self.S) if with_last_src else None
         _check(lib().akv_query_state(self.handle, _ptr(lens), _ptr(nxt), _ptr(pos), _ptr(tok),
-                                     _stream(stream)), "akv_query_state")
-        return lens, nxt, pos, tok
+                                     _ptr(lsrc), _stream(stream)), "akv_query_state")
+        return (lens, nxt, pos, tok, lsrc) if with_last_src else (lens, nxt, pos, tok)
+
+    def last_src(self, b: int):
+        """Host int64 array: sequence b's gather map of the last drop /
+        reposition / fork (up to its first -1)."""
+        import numpy as np
+        row = self.query_state(with_last_src=True)[4][b].cpu().numpy().astype(np.int64)
+        neg = np.flatnonzero(row < 0)
+        return row[:neg[0]] if neg.size else row
 
     def seq_state(self, b: int):
         """(token_ids, positions, page ids) of sequence b's active entries, on the host

@@ -17,6 +17,7 @@
 #include "akv_internal.h"
 #include "akv_rope.h"
 
+#include <algorithm>
 #include <climits>
 
 namespace akv {
@@ -87,10 +88,11 @@ __device__ __forceinline__ unsigned page_valid_bits(int len, int pg) {
 
 __global__ __launch_bounds__(kChunkPages) void plan_kernel(
     Dev d, const uint8_t *__restrict__ mask, const int32_t *__restrict__ new_pos,
-    const int32_t *__restrict__ old_pos, int mode) {
+    const int32_t *__restrict__ old_pos, int mode, int max_groups) {
   __shared__ int s_wave[kChunkPages / 64 + 1];
-  __shared__ int s_last, s_gerr, s_fdrop;
+  __shared__ int s_last, s_gerr, s_fdrop, s_ok;
   __shared__ int s_src[kChunkPages * kPage], s_dlt[kChunkPages * kPage];
+  __shared__ int s_lsrc[kChunkPages * kPage];
   const int c = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
   const size_t S = (size_t)d.S;
   const int len = ((mode & M_FORK) && d.fork_dst[b] < 0) ? 0 : d.lens[b];
@@ -176,6 +178,7 @@ __global__ __launch_bounds__(kChunkPages) void plan_kernel(
 #pragma unroll
       for (int r = 0; r < kPage; ++r) {
         if (!((keep >> r) & 1u)) continue;
+        s_lsrc[j - base] = pg * kPage + r;                                 // pre-op index
         if (mode & (M_DROP | M_FORK)) s_src[j - base] = tb * kPage + r;   // physical slot
         if (mode & M_REPOS) {
           if ((mode & M_OLDPOS) && o[r] != p[r]) err = max(err, (int)AKV_ERR_POS_MISMATCH);
@@ -196,6 +199,7 @@ __global__ __launch_bounds__(kChunkPages) void plan_kernel(
     for (int i = t; i < total; i += kChunkPages) {
       if (mode & (M_DROP | M_FORK)) d.src_map[b * S + base + i] = s_src[i];
       if (mode & M_REPOS) d.delta_map[b * S + base + i] = s_dlt[i];
+      d.last_src[b * S + base + i] = s_lsrc[i];
     }
     int *si = d.seq_info + (size_t)b * kSeqInfo;
     if (err) atomicMax(&si[SI_ERR], err);
@@ -295,36 +299,96 @@ __global__ __launch_bounds__(kChunkPages) void plan_kernel(
   if (t == 0) {
     int e = s_gerr;
     const int fc = *d.free_count;
-    if (!e && run_m > fc) e = AKV_ERR_NO_BLOCKS;
     const int latched = d.ctl[CTL_ERR];
+    int ng = 0;
+    if (!e && !latched) {
+      if (run_m <= fc) {
+        int *gr = d.groups;
+        gr[GR_S0] = 0; gr[GR_S1] = d.B; gr[GR_TM] = run_m; gr[GR_TI] = run_i; gr[GR_FC] = fc;
+        gr[GR_MOFF] = 0; gr[GR_IOFF] = 0; gr[GR_FOFF] = 0; gr[GR_F] = run_f;
+        ng = 1;
+      } else if (max_groups > 1 && !(mode & M_FORK)) {
+        // Too few free pages for the whole op: consecutive sequences are
+        // grouped greedily, each group taking what is free when it starts
+        // (the free count then grows by the pages the group drops).  Only a
+        // sequence that does not fit on its own, or more groups than the
+        // host launches rounds for, rejects the op.
+        int fcur = fc, s0 = 0, gm = 0, gi = 0, gf = 0;
+        auto close = [&](int s1) {
+          const int *si0 = d.seq_info + (size_t)s0 * kSeqInfo;
+          int *gr = d.groups + (size_t)ng * kGroupRec;
+          gr[GR_S0] = s0; gr[GR_S1] = s1; gr[GR_TM] = gm; gr[GR_TI] = gi; gr[GR_FC] = fcur;
+          gr[GR_MOFF] = si0[SI_MOVE_OFF]; gr[GR_IOFF] = si0[SI_INPLACE_OFF];
+          gr[GR_FOFF] = si0[SI_FREED_OFF]; gr[GR_F] = gf;
+          ++ng;
+          fcur += gf - gm;
+          s0 = s1;
+          gm = gi = gf = 0;
+        };
+        for (int bb = 0; bb < d.B && !e; ++bb) {
+          const int *si = d.seq_info + (size_t)bb * kSeqInfo;
+          const int nm = si[SI_N_MOVE];
+          if (gm + nm > fcur && bb > s0) {
+            if (ng + 1 >= max_groups) e = AKV_ERR_NO_BLOCKS;
+            else close(bb);
+          }
+          if (!e && nm > fcur) e = AKV_ERR_NO_BLOCKS;
+          gm += nm;
+          gi += si[SI_N_INPLACE];
+          gf += si[SI_N_FREED];
+        }
+        if (!e) close(d.B);
+      } else {
+        e = AKV_ERR_NO_BLOCKS;
+      }
+    }
     if (e || latched) {
       if (!latched) d.ctl[CTL_ERR] = e;
       d.ctl[CTL_OP_OK] = 0;
-      d.ctl[CTL_T_MOVE] = 0;
-      d.ctl[CTL_T_INPLACE] = 0;
+      d.ctl[CTL_NGROUPS] = 0;
     } else {
       d.ctl[CTL_OP_OK] = 1;
-      d.ctl[CTL_T_MOVE] = run_m;
-      d.ctl[CTL_T_INPLACE] = run_i;
-      d.ctl[CTL_F_TOTAL] = run_f;
-      d.ctl[CTL_FC_OLD] = fc;
-      d.ctl[CTL_BASE] = fc - run_m;
+      d.ctl[CTL_NGROUPS] = ng;
       d.ctl[CTL_MODE] = mode;
     }
     d.ctl[CTL_DONE] = 0;
+    s_ok = !(e || latched);
   }
+  __syncthreads();
+  // Gather map of this op for akv_query_state: sequence b's row of last_src
+  // (a fork destination reads its source's row); none after a rejected op.
+  for (int bb = t; bb < d.B; bb += kChunkPages) {
+    int *si = d.seq_info + (size_t)bb * kSeqInfo;
+    const bool own = s_ok && !(mode & M_FORK);
+    si[SI_LSRC_ROW] = own ? bb : -1;
+    si[SI_LSRC_LEN] = own ? si[SI_NEW_LEN] : 0;
+  }
+  __syncthreads();
+  if (s_ok && (mode & M_FORK))
+    for (int bb = t; bb < d.B; bb += kChunkPages) {
+      const int dst = d.fork_dst[bb];
+      if (dst >= 0) {
+        int *sd = d.seq_info + (size_t)dst * kSeqInfo;
+        sd[SI_LSRC_ROW] = bb;
+        sd[SI_LSRC_LEN] = d.seq_info[(size_t)bb * kSeqInfo + SI_NEW_LEN];
+      }
+    }
 }
 
 // ---------------------------------------------------------------------------
 // commit
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void commit_kernel(Dev d) {
-  if (d.ctl[CTL_OP_OK] == 0) return;
+__global__ __launch_bounds__(256) void commit_kernel(Dev d, int group) {
+  if (d.ctl[CTL_OP_OK] == 0 || group >= d.ctl[CTL_NGROUPS]) return;
+  const int *gr = d.groups + (size_t)group * kGroupRec;
   const int b = blockIdx.x;
+  const int s0 = gr[GR_S0];
+  if (b < s0 || b >= gr[GR_S1]) return;
   const int *si = d.seq_info + (size_t)b * kSeqInfo;
   const int fbd = si[SI_FBD], nmove = si[SI_N_MOVE], nfreed = si[SI_N_FREED];
-  const int moff = si[SI_MOVE_OFF], foff = si[SI_FREED_OFF];
-  const int base = d.ctl[CTL_BASE];
+  const int moff = si[SI_MOVE_OFF], foff = si[SI_FREED_OFF] - gr[GR_FOFF];
+  const int base = gr[GR_FC] - gr[GR_TM];   // the group's fresh pages came from [base, GR_FC)
+  const int ftot = gr[GR_F];
   const int dst = si[SI_DST];
   if (dst >= 0) {
     // fork: the new version takes the fresh pages; the source is untouched
@@ -334,11 +398,11 @@ __global__ __launch_bounds__(256) void commit_kernel(Dev d) {
       d.lens[dst] = si[SI_NEW_LEN];
       d.next_pos[dst] = si[SI_NEW_NEXT];
     }
-    if (b == 0 && threadIdx.x == 0) *d.free_count = base + d.ctl[CTL_F_TOTAL];
+    if (b == s0 && threadIdx.x == 0) *d.free_count = base + ftot;
     return;
   }
   if (d.ctl[CTL_MODE] & M_FORK) {
-    if (b == 0 && threadIdx.x == 0) *d.free_count = base + d.ctl[CTL_F_TOTAL];
+    if (b == s0 && threadIdx.x == 0) *d.free_count = base + ftot;
     return;
   }
   // The freed pages go onto the stack in reverse (sequence b's first page on
@@ -346,7 +410,6 @@ __global__ __launch_bounds__(256) void commit_kernel(Dev d) {
   // sequence rebuilt from them keeps ascending page runs, and the move's
   // blocks in flight keep reading and writing compact address ranges (a
   // scattered page table costs the move ~11% on MI355X).
-  const int ftot = d.ctl[CTL_F_TOTAL];
   int32_t *trow = d.table + (size_t)b * d.maxpg;
   for (int k = threadIdx.x; k < nfreed; k += blockDim.x) {
     const int po = fbd + k;
@@ -357,8 +420,20 @@ __global__ __launch_bounds__(256) void commit_kernel(Dev d) {
   if (threadIdx.x == 0) {
     d.lens[b] = si[SI_NEW_LEN];
     d.next_pos[b] = si[SI_NEW_NEXT];
-    if (b == 0) *d.free_count = base + d.ctl[CTL_F_TOTAL];
+    if (b == s0) *d.free_count = base + ftot;
   }
+}
+
+// akv_fork's destination map, carried in the kernel's arguments (copied by
+// the runtime at launch, so the caller's host array may go away at once).
+constexpr int kForkMapChunk = 512;
+struct ForkMapChunk {
+  int32_t v[kForkMapChunk];
+};
+__global__ __launch_bounds__(kForkMapChunk) void fork_map_kernel(Dev d, int off, int n,
+                                                                 ForkMapChunk m) {
+  const int i = threadIdx.x;
+  if (i < n) d.fork_dst[off + i] = m.v[i];
 }
 
 // ---------------------------------------------------------------------------
@@ -637,6 +712,8 @@ __global__ void reset_kernel(Dev d, const int32_t *order) {
     d.next_pos[i] = 0;
     d.seq_info[i * kSeqInfo + SI_FPOS] = INT_MAX;   // plan accumulators, re-armed by every plan
     d.seq_info[i * kSeqInfo + SI_ERR] = 0;
+    d.seq_info[i * kSeqInfo + SI_LSRC_ROW] = -1;     // no gather map yet
+    d.seq_info[i * kSeqInfo + SI_LSRC_LEN] = 0;
   }
   if (i < d.NB) d.free_stack[d.NB - 1 - i] = order ? order[i] : (int)i;
   if (i == 0) {
@@ -649,15 +726,28 @@ __global__ void reset_kernel(Dev d, const int32_t *order) {
 // launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_plan(const Dev &d, const uint8_t *mask, const int32_t *new_pos,
-                       const int32_t *old_pos, int mode, hipStream_t st) {
+                       const int32_t *old_pos, int mode, int max_groups, hipStream_t st) {
   const dim3 grid(d.nchunk, d.B);
-  hipLaunchKernelGGL(plan_kernel, grid, dim3(kChunkPages), 0, st, d, mask, new_pos, old_pos, mode);
+  hipLaunchKernelGGL(plan_kernel, grid, dim3(kChunkPages), 0, st, d, mask, new_pos, old_pos, mode,
+                     max_groups);
   return hipGetLastError();
 }
 
-hipError_t launch_commit(const Dev &d, hipStream_t st) {
-  hipLaunchKernelGGL(commit_kernel, dim3(d.B), dim3(256), 0, st, d);
+hipError_t launch_commit(const Dev &d, int group, hipStream_t st) {
+  hipLaunchKernelGGL(commit_kernel, dim3(d.B), dim3(256), 0, st, d, group);
   return hipGetLastError();
+}
+
+hipError_t launch_fork_map(const Dev &d, const int32_t *dst_of_host, hipStream_t st) {
+  for (int off = 0; off < d.B; off += kForkMapChunk) {
+    ForkMapChunk m;
+    const int n = std::min(kForkMapChunk, d.B - off);
+    for (int i = 0; i < n; ++i) m.v[i] = dst_of_host[off + i];
+    hipLaunchKernelGGL(fork_map_kernel, dim3(1), dim3(kForkMapChunk), 0, st, d, off, n, m);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_append(const Dev &d, const int32_t *counts, int64_t n_new,
@@ -684,7 +774,8 @@ hipError_t launch_append(const Dev &d, const int32_t *counts, int64_t n_new,
 // token ids in active order (slots past the length read -1)
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void query_kernel(Dev d, int32_t *lens, int32_t *next,
-                                                     int32_t *pos, int32_t *tok) {
+                                                     int32_t *pos, int32_t *tok,
+                                                     int32_t *last_src) {
   const int b = blockIdx.y;
   const int len = d.lens[b];
   if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -692,21 +783,29 @@ __global__ __launch_bounds__(256) void query_kernel(Dev d, int32_t *lens, int32_
     if (next) next[b] = d.next_pos[b];
   }
   const int j = blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= d.S || !(pos || tok)) return;
-  int p = -1, t = -1;
-  if (j < len) {
-    const size_t slot = (size_t)d.table[(size_t)b * d.maxpg + j / kPage] * kPage + j % kPage;
-    p = d.pos[slot];
-    t = d.tok[slot];
+  if (j >= d.S) return;
+  if (pos || tok) {
+    int p = -1, t = -1;
+    if (j < len) {
+      const size_t slot = (size_t)d.table[(size_t)b * d.maxpg + j / kPage] * kPage + j % kPage;
+      p = d.pos[slot];
+      t = d.tok[slot];
+    }
+    if (pos) pos[(size_t)b * d.S + j] = p;
+    if (tok) tok[(size_t)b * d.S + j] = t;
   }
-  if (pos) pos[(size_t)b * d.S + j] = p;
-  if (tok) tok[(size_t)b * d.S + j] = t;
+  if (last_src) {
+    const int *si = d.seq_info + (size_t)b * kSeqInfo;
+    const int row = si[SI_LSRC_ROW];
+    last_src[(size_t)b * d.S + j] =
+        (row >= 0 && j < si[SI_LSRC_LEN]) ? d.last_src[(size_t)row * d.S + j] : -1;
+  }
 }
 
 hipError_t launch_query(const Dev &d, int32_t *lens, int32_t *next, int32_t *pos, int32_t *tok,
-                        hipStream_t st) {
+                        int32_t *last_src, hipStream_t st) {
   hipLaunchKernelGGL(query_kernel, dim3((unsigned)((d.S + 255) / 256), (unsigned)d.B), dim3(256),
-                     0, st, d, lens, next, pos, tok);
+                     0, st, d, lens, next, pos, tok, last_src);
   return hipGetLastError();
 }
 

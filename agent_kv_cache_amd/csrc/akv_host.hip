@@ -60,6 +60,7 @@ struct akv_cache {
   int oneshot_cap = 1;     // blocks of the one-shot move launch (the largest op it moves)
   bool move_persistent = true;   // some op could be too large for the one-shot launch
   int attn_per_cu = 2;
+  int op_groups = 1;       // (move, commit) rounds of a drop / reposition (1: the pool always fits)
   int n_full_layers = 0;   // layers without a sliding window
   void *noalloc_ws = nullptr;   // this device's copy of `scratch`
   bool profile = false;
@@ -146,21 +147,28 @@ int nsplit_for(const akv_cache *c, int nL) {
   return (int)best;
 }
 
+// One drop / reposition / fork: the plan, then one (move, commit) round per
+// sequence group.  A fork copies without freeing anything, so it is never
+// split; other ops get c->op_groups rounds (rounds past the groups the plan
+// made exit at once).
 akv_status run_compaction(akv_cache *c, const uint8_t *mask, const int32_t *new_pos,
                           const int32_t *old_pos, int mode, void *stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int rounds = (mode & akv::M_FORK) ? 1 : c->op_groups;
   {
     Timed tm(c, AKV_KERNEL_PLAN, st);
-    AKV_HIP(akv::launch_plan(c->dev, mask, new_pos, old_pos, mode, st));
+    AKV_HIP(akv::launch_plan(c->dev, mask, new_pos, old_pos, mode, rounds, st));
   }
-  {
-    Timed tm(c, AKV_KERNEL_MOVE, st);
-    AKV_HIP(akv::launch_move(c->dev, mode, c->move_persistent ? c->move_grid : 0,
-                             c->oneshot_cap, st));
-  }
-  {
-    Timed tm(c, AKV_KERNEL_COMMIT, st);
-    AKV_HIP(akv::launch_commit(c->dev, st));
+  for (int g = 0; g < rounds; ++g) {
+    {
+      Timed tm(c, AKV_KERNEL_MOVE, st);
+      AKV_HIP(akv::launch_move(c->dev, mode, (c->move_persistent || g > 0) ? c->move_grid : 0,
+                               c->oneshot_cap, g, st));
+    }
+    {
+      Timed tm(c, AKV_KERNEL_COMMIT, st);
+      AKV_HIP(akv::launch_commit(c->dev, g, st));
+    }
   }
   return AKV_OK;
 }
@@ -233,6 +241,8 @@ akv_status akv_cache_init(const akv_cache_desc *d, akv_cache **out) {
   v.chunk_info = reinterpret_cast<int32_t *>(sb + c->layout.chunk_info);
   v.fork_dst = reinterpret_cast<int32_t *>(sb + c->layout.fork_dst);
   v.window = reinterpret_cast<const int32_t *>(sb + c->layout.window);
+  v.last_src = reinterpret_cast<int32_t *>(sb + c->layout.last_src);
+  v.groups = reinterpret_cast<int32_t *>(sb + c->layout.groups);
   v.RD = rd;
   v.any_window = any_window;
   c->n_full_layers = d->n_layers;
@@ -270,6 +280,17 @@ akv_status akv_cache_init(const akv_cache_desc *d, akv_cache **out) {
     c->move_persistent = pages * groups > c->oneshot_cap;
   }
   c->attn_per_cu = akv::attn_blocks_per_cu(d->head_dim);
+  {
+    // A drop / reposition needs at most as many fresh pages as the sequences
+    // hold; when the table can address more than half the pool, the pool may
+    // run short and the op may have to run in sequence groups: up to
+    // AKV_MAX_OP_GROUPS rounds (environment, else the compile-time default).
+    long long g = AKV_MAX_OP_GROUPS;
+    if (const char *e = getenv("AKV_MAX_OP_GROUPS")) g = atoll(e);
+    g = std::max(1LL, std::min<long long>({g, (long long)akv::kMaxOpGroups, d->n_seqs}));
+    const bool may_run_short = 2LL * d->n_seqs * d->max_blocks_per_seq > d->n_blocks;
+    c->op_groups = may_run_short ? (int)g : 1;
+  }
 
   // theta_i over the rotary dims: the caller's table, else base^(-2i/r);
   // double, uploaded once.  Per-layer windows likewise.
@@ -350,10 +371,11 @@ akv_status akv_release(akv_cache *c, const uint8_t *release, void *stream) {
 }
 
 akv_status akv_query_state(akv_cache *c, int32_t *seq_lens, int32_t *next_pos,
-                           int32_t *positions, int32_t *token_ids, void *stream) {
+                           int32_t *positions, int32_t *token_ids, int32_t *last_src,
+                           void *stream) {
   if (!c) return AKV_ERR_ARG;
-  if (!seq_lens && !next_pos && !positions && !token_ids) return AKV_OK;
-  AKV_HIP(akv::launch_query(c->dev, seq_lens, next_pos, positions, token_ids,
+  if (!seq_lens && !next_pos && !positions && !token_ids && !last_src) return AKV_OK;
+  AKV_HIP(akv::launch_query(c->dev, seq_lens, next_pos, positions, token_ids, last_src,
                             reinterpret_cast<hipStream_t>(stream)));
   return AKV_OK;
 }
@@ -405,7 +427,8 @@ akv_status akv_fork(akv_cache *c, const int32_t *dst_of, const uint8_t *drop_mas
     if (is_dst[b] && is_src[b]) return AKV_ERR_ARG;   // a destination may not be forked from
   if (n == 0) return AKV_OK;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  AKV_HIP(hipMemcpyAsync(c->dev.fork_dst, dst_of, sizeof(int32_t) * B, hipMemcpyHostToDevice, st));
+  // the map travels in kernel arguments: nothing reads dst_of after return
+  AKV_HIP(akv::launch_fork_map(c->dev, dst_of, st));
   int mode = akv::M_FORK;
   if (drop_mask) mode |= akv::M_DROP;
   if (reposition) mode |= akv::M_REPOS;

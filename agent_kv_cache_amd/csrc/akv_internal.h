@@ -17,14 +17,31 @@ enum Ctl : int {
   CTL_ERR = 0,        // latched error code (sticky until akv_sync_status)
   CTL_DONE = 1,       // last-block ticket of the plan kernels
   CTL_OP_OK = 2,      // 1 when the planned op may commit
-  CTL_T_MOVE = 3,     // pages moved out of place (all sequences)
-  CTL_T_INPLACE = 4,  // pages re-rotated in place
-  CTL_F_TOTAL = 5,    // pages returned to the free stack
-  CTL_BASE = 6,       // free_count before the op minus CTL_T_MOVE
-  CTL_FC_OLD = 7,     // free_count before the op
+  CTL_NGROUPS = 3,    // sequence groups of the planned op (move + commit rounds that run)
   CTL_MODE = 8,       // mode bits of the planned op
   CTL_COUNT = 64
 };
+
+// A drop / reposition whose new pages do not fit the free pool at once runs
+// in groups of consecutive sequences, one (move, commit) round per group in
+// stream order; a group's commit returns its old pages before the next group
+// takes fresh ones.  Group record (int32 x kGroupRec), filled by the plan:
+enum GroupRec : int {
+  GR_S0 = 0,       // first sequence of the group
+  GR_S1 = 1,       // one past its last sequence
+  GR_TM = 2,       // pages moved out of place
+  GR_TI = 3,       // pages re-rotated in place
+  GR_FC = 4,       // free_count when the group starts
+  GR_MOFF = 5,     // global move offset of its first moved page (SI_MOVE_OFF)
+  GR_IOFF = 6,     // global in-place offset (SI_INPLACE_OFF)
+  GR_FOFF = 7,     // global freed offset (SI_FREED_OFF)
+  GR_F = 8,        // pages it returns to the free stack
+  kGroupRec = 16
+};
+constexpr int kMaxOpGroups = 64;       // capacity of the group table
+#ifndef AKV_MAX_OP_GROUPS
+#define AKV_MAX_OP_GROUPS 8            // default rounds when the pool may run short
+#endif
 
 // Per-sequence plan record (int32 x kSeqInfo).
 enum SeqInfo : int {
@@ -44,7 +61,9 @@ enum SeqInfo : int {
   SI_APP_OFF = 13,   // append: offset of this sequence's tokens in the input
   SI_FPOS = 14,      // first survivor rank whose position changes (atomic min)
   SI_DST = 15,       // fork: destination sequence (-1 = none)
-  kSeqInfo = 16
+  SI_LSRC_ROW = 16,  // row of last_src holding this sequence's gather map (-1: none)
+  SI_LSRC_LEN = 17,  // entries of that map
+  kSeqInfo = 24
 };
 
 // Ops that need at most this many one-shot blocks (one per layer group of
@@ -72,6 +91,8 @@ struct Dev {
   uint16_t *k, *v;
   int32_t *table, *lens, *next_pos, *pos, *tok, *free_stack, *free_count;
   int32_t *ctl, *seq_info, *src_map, *delta_map, *stage, *chunk_info, *fork_dst;
+  int32_t *last_src;          // [B][S] gather map of the last drop / reposition / fork
+  int32_t *groups;            // [kMaxOpGroups][kGroupRec] sequence groups of the planned op
   const double *theta;        // [RD/2] rotation frequencies
   const int32_t *window;      // [L] sliding-window length per layer, 0 = full attention
   int L, H, D, NB, B, maxpg, S, nchunk;   // nchunk: plan chunks per sequence
@@ -129,7 +150,8 @@ __device__ inline int first_pos_at_least(const Dev &d, const int32_t *trow, int 
 
 // Scratch layout (byte offsets from the scratch base, each 256-B aligned).
 struct ScratchLayout {
-  size_t ctl, theta, seq_info, src_map, delta_map, stage, chunk_info, fork_dst, window, total;
+  size_t ctl, theta, seq_info, src_map, delta_map, stage, chunk_info, fork_dst, window, last_src,
+      groups, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -150,22 +172,28 @@ inline ScratchLayout scratch_layout(int B, int S, int NB, int L) {
   s.chunk_info = o; o = align256(o + size_t(B) * plan_chunks(S / kPage) * 2 * 4);
   s.fork_dst = o;  o = align256(o + size_t(B) * 4);
   s.window = o;    o = align256(o + size_t(L) * 4);
+  s.last_src = o;  o = align256(o + size_t(B) * S * 4);
+  s.groups = o;    o = align256(o + size_t(kMaxOpGroups) * kGroupRec * 4);
   s.total = o;
   return s;
 }
 
 // Launchers (each in the .hip file that defines its kernels).
 hipError_t launch_plan(const Dev &d, const uint8_t *mask, const int32_t *new_pos,
-                       const int32_t *old_pos, int mode, hipStream_t st);
-hipError_t launch_move(const Dev &d, int mode, int grid, int oneshot_cap, hipStream_t st);
-hipError_t launch_commit(const Dev &d, hipStream_t st);
+                       const int32_t *old_pos, int mode, int max_groups, hipStream_t st);
+// group 0: the one-shot launch (oneshot_cap blocks) and, if grid > 0, the
+// persistent one; group >= 1: the persistent launch only
+hipError_t launch_move(const Dev &d, int mode, int grid, int oneshot_cap, int group,
+                       hipStream_t st);
+hipError_t launch_commit(const Dev &d, int group, hipStream_t st);
+hipError_t launch_fork_map(const Dev &d, const int32_t *dst_of_host, hipStream_t st);
 int move_blocks_per_cu(int D, int RD);
 hipError_t launch_append(const Dev &d, const int32_t *counts, int64_t n_new,
                          const uint16_t *k_new, const uint16_t *v_new,
                          const int32_t *tok_new, bool rope, hipStream_t st);
 hipError_t launch_release(const Dev &d, const uint8_t *sel, hipStream_t st);
 hipError_t launch_query(const Dev &d, int32_t *lens, int32_t *next, int32_t *pos, int32_t *tok,
-                        hipStream_t st);
+                        int32_t *last_src, hipStream_t st);
 hipError_t launch_reset(const Dev &d, const int32_t *order_dev, hipStream_t st);
 hipError_t launch_attention(const Dev &d, const uint16_t *q, const int32_t *active_len,
                             int l0, int nL, int Hq, uint16_t *out, float *part,

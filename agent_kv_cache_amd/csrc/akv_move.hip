@@ -86,7 +86,8 @@ __device__ __forceinline__ void st_stream(uint16_t *p, u32x4 v) {
 // lanes are adjacent), tail chunks are only copied.
 template <int D, bool NT, bool ONESHOT, bool FR>
 __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(Dev d, int mode,
-                                                                                 int oneshot_cap) {
+                                                                                 int oneshot_cap,
+                                                                                 int group) {
   constexpr int HALF = D / 2;
   constexpr int CH = D / 16;             // 16-B chunks per half row
   constexpr int CPR = FR ? 2 * CH : CH;  // threads per row
@@ -100,11 +101,14 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
   __shared__ int s_repval[kPage], s_nrep;
   __shared__ double2 s_cs[kPage][HALF];
 
-  if (d.ctl[CTL_OP_OK] == 0) return;
-  const int Tm = d.ctl[CTL_T_MOVE], Ti = d.ctl[CTL_T_INPLACE];
+  if (d.ctl[CTL_OP_OK] == 0 || group >= d.ctl[CTL_NGROUPS]) return;
+  // this round's group of sequences: its moved pages take the fresh pages
+  // below the group's free count, its rebuilt pages are numbered from 0
+  const int *gr = d.groups + (size_t)group * kGroupRec;
+  const int Tm = gr[GR_TM], Ti = gr[GR_TI];
   const long long npages = (long long)Tm + Ti;
   if (npages == 0) return;
-  const int fc_old = d.ctl[CTL_FC_OLD];
+  const int fc_old = gr[GR_FC], moff = gr[GR_MOFF], ioff = gr[GR_IOFF];
   const long long units = npages * d.L;
   // Two launches share the work.  An op of at most oneshot_cap blocks runs in
   // the one-shot launch: one block per LPB layers of a page, in layer-major
@@ -157,7 +161,7 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
     // and delta, then rank the page's distinct deltas among themselves.
     if (t < kPage) {
       const bool mv = pg < Tm;
-      const int key = mv ? pg : pg - Tm;
+      const int key = mv ? moff + pg : ioff + (pg - Tm);   // global offsets over sequences
       const int of = mv ? SI_MOVE_OFF : SI_INPLACE_OFF;
       int lo = 0, hi = d.B - 1;
       while (lo < hi) {
@@ -181,7 +185,7 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
       if (t == 0) {
         s_dst = dst;
         s_mv = mv;
-        if (mv && l0 == 0) d.stage[pg] = dst;
+        if (mv && l0 == 0) d.stage[moff + pg] = dst;
       }
       if (l0 == 0) {
         const size_t dn = (size_t)dst * kPage + t;
@@ -291,13 +295,23 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
   }
 }
 
+// Group 0: the one-shot launch, then (grid > 0) the persistent one; each
+// checks the group's unit count and only one of them moves.  Later groups (an
+// op split because the free pool was short): the persistent launch alone,
+// with a one-shot cap of 0 so that it always moves.
 template <int D, bool NT, bool FR>
-static void launch_move_pair(const Dev &d, int mode, int grid, int oneshot_cap, hipStream_t st) {
+static void launch_move_pair(const Dev &d, int mode, int grid, int oneshot_cap, int group,
+                             hipStream_t st) {
   const dim3 b(kMoveThreads);
-  hipLaunchKernelGGL((move_kernel<D, NT, true, FR>), dim3(oneshot_cap), b, 0, st, d, mode,
-                     oneshot_cap);
-  if (grid > 0)
-    hipLaunchKernelGGL((move_kernel<D, NT, false, FR>), dim3(grid), b, 0, st, d, mode, oneshot_cap);
+  if (group == 0) {
+    hipLaunchKernelGGL((move_kernel<D, NT, true, FR>), dim3(oneshot_cap), b, 0, st, d, mode,
+                       oneshot_cap, 0);
+    if (grid > 0)
+      hipLaunchKernelGGL((move_kernel<D, NT, false, FR>), dim3(grid), b, 0, st, d, mode,
+                         oneshot_cap, 0);
+  } else {
+    hipLaunchKernelGGL((move_kernel<D, NT, false, FR>), dim3(grid), b, 0, st, d, mode, 0, group);
+  }
 }
 
 // Whether a cache's moves use the full-row mapping.
@@ -311,16 +325,18 @@ static bool move_full_rows(int D, int RD) {
 // mapping whose load instructions cover whole lines uses the nontemporal
 // hint (half rows of full RoPE at d = 128, full rows); the half-row mapping
 // of partial RoPE (64-B pieces) uses cached accesses.
-hipError_t launch_move(const Dev &d, int mode, int grid, int oneshot_cap, hipStream_t st) {
+hipError_t launch_move(const Dev &d, int mode, int grid, int oneshot_cap, int group,
+                       hipStream_t st) {
   constexpr bool kFrNT = AKV_MOVE_FR_NT != 0;
   if (move_full_rows(d.D, d.RD)) {
-    if (d.D == 128) launch_move_pair<128, kFrNT, true>(d, mode, grid, oneshot_cap, st);
-    else launch_move_pair<64, kFrNT, true>(d, mode, grid, oneshot_cap, st);
+    if (d.D == 128) launch_move_pair<128, kFrNT, true>(d, mode, grid, oneshot_cap, group, st);
+    else launch_move_pair<64, kFrNT, true>(d, mode, grid, oneshot_cap, group, st);
   } else if (d.D == 128) {
-    if (AKV_MOVE_NT && d.RD == d.D) launch_move_pair<128, true, false>(d, mode, grid, oneshot_cap, st);
-    else launch_move_pair<128, false, false>(d, mode, grid, oneshot_cap, st);
+    if (AKV_MOVE_NT && d.RD == d.D)
+      launch_move_pair<128, true, false>(d, mode, grid, oneshot_cap, group, st);
+    else launch_move_pair<128, false, false>(d, mode, grid, oneshot_cap, group, st);
   } else {
-    launch_move_pair<64, false, false>(d, mode, grid, oneshot_cap, st);
+    launch_move_pair<64, false, false>(d, mode, grid, oneshot_cap, group, st);
   }
   return hipGetLastError();
 }

@@ -43,6 +43,19 @@
  *     mutating call on the cache is a no-op until akv_sync_status() reads
  *     and clears it.  This mirrors whole-request rejection in [AKV] sec. 3
  *     and 5.3.
+ *   - Free pages: a drop / reposition rebuilds survivors from the first
+ *     dropped page on in fresh pages before their old pages return to the
+ *     stack.  When the free pool cannot hold the fresh pages of every
+ *     sequence at once, the op runs in groups of consecutive sequences, one
+ *     group after another in stream order, each group's old pages freed
+ *     before the next group takes fresh ones (the result is the same).  The
+ *     host never reads device state, so it enqueues the rounds up front:
+ *     one when the page table cannot address more than half the pool
+ *     (2 * n_seqs * max_blocks_per_seq <= n_blocks: every op fits), else
+ *     min(n_seqs, AKV_MAX_OP_GROUPS) (environment, read by akv_cache_init;
+ *     default 8), rounds past the groups an op needs exiting at once.
+ *     AKV_ERR_NO_BLOCKS comes only when one sequence alone does not fit the
+ *     pages free at its turn or the op needs more groups than that.
  *   - Concurrent calls on one cache from different streams race; callers
  *     serialise them on one stream.
  *   - Environment (read by akv_cache_init): AKV_MOVE_ONESHOT_CAP=<n> caps
@@ -110,18 +123,24 @@ typedef struct {
                                  reads the entries whose position is >= P - W + 1 */
 } akv_cache_desc;
 
-/* Device scratch the cache needs (compaction plan, error word, RoPE
- * frequencies).  Owned by the caller, lives as long as the cache. */
+/* Device scratch the cache needs: the compaction plan (per-survivor gather
+ * map and old -> new position transitions, [AKV] sec. 5.3), the error word,
+ * the RoPE frequencies.  Owned by the caller, lives as long as the cache. */
 size_t akv_scratch_bytes(const akv_cache_desc *desc);
 
-/* Validate `desc`, upload theta_i (computed on the host in double) into the
- * scratch and return a host handle in *out.  Does not touch the pools or
- * metadata; call akv_cache_reset before first use.  Errors: AKV_ERR_ARG,
- * AKV_ERR_HIP. */
+/* Validate `desc`, upload the rotation frequencies theta_i of R(p) ([CE]
+ * sec. 3.3 eq. 5; [AKV] sec. 5.5 for partial RoPE and windows), computed on
+ * the host in double, into the scratch and return a host handle in *out.
+ * Does not touch the pools or metadata; call akv_cache_reset before first
+ * use.  Errors: AKV_ERR_ARG, AKV_ERR_HIP. */
 akv_status akv_cache_init(const akv_cache_desc *desc, akv_cache **out);
+/* Frees the host handle only (library housekeeping; the device memory stays
+ * the caller's).  NULL is a no-op. */
 void akv_cache_free(akv_cache *c);
 
-/* Empty every sequence: seq_lens = next_pos = 0, block_table = -1,
+/* A resident page pool with nothing active ([CE] sec. 3.1: resident,
+ * active and logical KV are separate).
+ * Empty every sequence: seq_lens = next_pos = 0, block_table = -1,
  * free_count = NB, and the free stack such that pages are handed out in the
  * order page_order[0], page_order[1], ... (page_order: HOST int32 [NB], a
  * permutation of 0..NB-1; NULL = 0, 1, 2, ...).  Clears the error word.
@@ -156,7 +175,8 @@ akv_status akv_append_rope(akv_cache *c, const int32_t *counts, int64_t n_new,
                            const uint16_t *k_raw, const uint16_t *v_new,
                            const int32_t *token_ids, void *stream);
 
-/* End of a request: every sequence b with release[b] != 0 returns all its
+/* End of a request ([CE] sec. 3.1: the request's resident KV is released):
+ * every sequence b with release[b] != 0 returns all its
  * pages to the device free stack and becomes empty with next_pos = 0, ready
  * for a new request (or as the destination of akv_fork).  release: DEVICE
  * uint8 [B].  A no-op while a device error is latched. */
@@ -168,7 +188,10 @@ akv_status akv_release(akv_cache *c, const uint8_t *release, void *stream);
  * next_pos is unchanged.  Survivors from the first dropped entry's page on
  * are moved into fresh pages (out of place); pages before it are untouched;
  * the old pages return to the free stack.  Needs up to ceil(len/16) free
- * pages per sequence while it runs (device-detected AKV_ERR_NO_BLOCKS). */
+ * pages per sequence while it runs; the op is split into sequence groups
+ * when the pool is short (see Free pages above; AKV_ERR_NO_BLOCKS only when
+ * a sequence alone does not fit).  The gather map of the call (pre-call
+ * index of each survivor) is exported by akv_query_state. */
 akv_status akv_drop(akv_cache *c, const uint8_t *drop_mask, void *stream);
 
 /* [CE] eq. (5): move every active entry from its position p to q.
@@ -201,18 +224,23 @@ akv_status akv_drop_reposition(akv_cache *c, const uint8_t *drop_mask,
  * source sequence is not modified (copy on transform).
  *   dst_of    : HOST int32 [B]; -1 = no fork.  Host-checked: destinations
  *               in range, distinct, not equal to their source, and not
- *               themselves sources.
+ *               themselves sources.  Read during the call only (the map is
+ *               passed to the device in kernel arguments), so the array may
+ *               be freed or reused as soon as the call returns.
  *   drop_mask : DEVICE uint8 [B][S] (row b applies to source b) or NULL
  *   new_pos   : DEVICE int32 [B][S] by survivor rank of source b, or NULL;
  *               only with reposition != 0
  * next_pos of the copy: the source's (no reposition) or last new position
  * + 1.  Device-checked: a destination that is not empty (AKV_ERR_ARG),
- * new positions (AKV_ERR_ORDER), free pages (AKV_ERR_NO_BLOCKS). */
+ * new positions (AKV_ERR_ORDER), free pages (AKV_ERR_NO_BLOCKS: a fork
+ * frees nothing, so it is never split into groups). */
 akv_status akv_fork(akv_cache *c, const int32_t *dst_of, const uint8_t *drop_mask,
                     int reposition, const int32_t *new_pos, void *stream);
 
-/* Decode attention over the active KV for layers
- * [layer_begin, layer_begin + n_layers):
+/* Decode attention over the active KV ([CE] sec. 3.1 and 3.3: after a drop
+ * only the surviving, active entries are read; Appendix A.4.1: this is the
+ * full-attention time AKV cuts) for layers [layer_begin, layer_begin +
+ * n_layers):
  *   q          : DEVICE bf16 [B][n_layers][n_q_heads][d], already rotated at
  *                the query's position by the caller
  *   active_len : DEVICE int32 [B] or NULL (= seq_lens).  Values outside
@@ -223,7 +251,9 @@ akv_status akv_fork(akv_cache *c, const int32_t *dst_of, const uint8_t *drop_mas
  * head h reads kv head h / (n_q_heads / n_kv_heads); no entry beyond
  * active_len and no self token; an empty sequence gives zeros.
  * Host-checked: n_q_heads multiple of n_kv_heads with ratio <= 16, layer
- * range inside [0, L). */
+ * range inside [0, L).
+ * akv_decode_workspace_bytes: bytes of `workspace` a call with these sizes
+ * needs (its split-K partials; 256 when it runs unsplit), 0 for bad sizes. */
 size_t akv_decode_workspace_bytes(const akv_cache *c, int32_t n_layers,
                                   int32_t n_q_heads);
 akv_status akv_decode_attention(akv_cache *c, const uint16_t *q,
@@ -277,27 +307,38 @@ akv_status akv_segment_attention(akv_cache *c, const uint16_t *q, const int32_t 
                                  uint16_t *out, void *stream);
 
 /* Export of the state the server keeps per sequence ([AKV] sec. 5.3: the
- * positions of the active tokens and the next position; [CE] sec. 3.1:
- * active index, RoPE position and token are separate): one gather kernel on
- * `stream`, outputs in active order.
+ * positions of the active tokens, the next position and the transition of
+ * the last plan; [CE] sec. 3.1: active index, RoPE position and token are
+ * separate): one gather kernel on `stream`, outputs in active order.
  *   seq_lens  : DEVICE int32 [B] or NULL
  *   next_pos  : DEVICE int32 [B] or NULL
  *   positions : DEVICE int32 [B][S] or NULL; entry j of sequence b at
  *               [b][j], -1 past its length
  *   token_ids : DEVICE int32 [B][S] or NULL; same layout
+ *   last_src  : DEVICE int32 [B][S] or NULL: the gather map of the last
+ *               akv_drop / akv_reposition / akv_drop_reposition / akv_fork
+ *               ([CE] eq. 4: the survivors in order): last_src[b][j] = the
+ *               index, before that call, of the entry it placed at slot j of
+ *               sequence b (for a fork destination, an index into its
+ *               source); -1 past the call's output length of b, for rows the
+ *               call did not write (fork sources and sequences not forked),
+ *               before any such call, and after a rejected one.  Appends and
+ *               releases leave it as it was.
  * All outputs are caller-owned; copy them to the host after the stream
  * (the call does not synchronise).  Reads only; works while an error is
  * latched.  Errors: AKV_ERR_ARG (null cache), AKV_ERR_HIP. */
 akv_status akv_query_state(akv_cache *c, int32_t *seq_lens, int32_t *next_pos,
-                           int32_t *positions, int32_t *token_ids, void *stream);
+                           int32_t *positions, int32_t *token_ids, int32_t *last_src,
+                           void *stream);
 
 /* Synchronise `stream`, return the latched device error (AKV_OK if none)
- * and clear it. */
+ * and clear it (the error of a rejected request, [AKV] sec. 3 / 5.3). */
 akv_status akv_sync_status(akv_cache *c, void *stream);
+/* Static text naming a status code (library housekeeping). */
 const char *akv_status_string(akv_status s);
 
-/* Optional per-kernel timing with HIP events recorded on the launch stream.
- * Kernel ids: */
+/* Optional per-kernel timing with HIP events recorded on the launch stream
+ * (measurement housekeeping, no operation of the pages).  Kernel ids: */
 enum {
   AKV_KERNEL_PLAN = 0,     /* keep-scan / compaction plan */
   AKV_KERNEL_MOVE = 1,     /* fused move + re-rotation */
