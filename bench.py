@@ -4,15 +4,22 @@
 One step = restore the per-sequence state (page table, lengths, next
 positions, free stack: one small device copy) + fused drop+reposition
 (plan, move/re-rotate, commit kernels) + decode attention over all layers
-(split-K kernel + combine).  The default workload is the Llama-3.1-8B-shaped
-cache (32 layers, 8 kv heads, d=128, 32768 tokens, six seeded tool spans of
-1024..4096 tokens dropped, canonical reposition, 32 query heads).
+(split-K kernel + combine).
 
-Prints ONE JSON line.  `value` = algorithmic KV bytes of the whole step
-(drop+reposition and decode) / wall time per step, in GB/s.  The `roofline`
-object covers the dominant kernel (per-launch algorithmic bytes / average
-launch time from HIP events recorded on the launch stream); `parts` gives
-both parts; `cpu_baseline` times the fp64 oracle on a bounded sample.
+The default run measures every configuration of the method's workloads and
+prints ONE JSON line.  The headline (`value`, `roofline`, `cpu_baseline`) is
+the largest single-GPU configuration, the ragged batch (64 sequences of
+8K..64K tokens, Llama-8B KV shape, shuffled pages, ~40% dropped, ~155 GB of
+KV); the Llama-8B-shaped single sequence, the one-layer 4K case, the
+Llama-70B shape and the 50-turn history follow under `configs`.
+`--workload NAME` runs one of them (or the restore / append workloads) alone.
+
+`value` = algorithmic KV bytes of the whole step (drop+reposition and
+decode) / wall time per step, in GB/s.  The `roofline` object covers the
+dominant kernel (per-launch algorithmic bytes / average launch time from HIP
+events recorded on the launch stream); `parts` gives both parts;
+`cpu_baseline` times the fp64 oracle on a bounded sample in a process pool
+on the host's cores.
 """
 from __future__ import annotations
 
@@ -97,54 +104,181 @@ def rope_options(args, shape):
     return kw
 
 
-def cpu_baseline(wl, layer_stride: int):
-    """The fp64 oracle (as it stands) on a layer sample of the same workload
-    (every layer_stride-th layer, all tokens; one host core)."""
-    from threadpoolctl import threadpool_limits
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle (as it stands) in a process pool on the host
+# ---------------------------------------------------------------------------
+def host_info():
+    """CPU model, logical cores this process may run on, host RAM."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    ram = None
+    try:
+        for line in open("/proc/meminfo"):
+            if line.startswith("MemTotal"):
+                ram = round(int(line.split()[1]) / 2 ** 20, 1)
+                break
+    except OSError:
+        pass
+    return {"cpu_model": model, "cpus_available": len(os.sched_getaffinity(0)),
+            "host_ram_gib": ram}
+
+
+MAX_POOL = 16       # worker processes (a one-GPU share of the host)
+
+
+def _pool(n_units):
+    """A spawn-context process pool (fresh interpreters that never touch the
+    GPU) of min(16, available cores, units) workers, BLAS one thread each."""
+    import multiprocessing as mp
+    n = max(1, min(MAX_POOL, len(os.sched_getaffinity(0)), n_units))
+    keys = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")
+    old = {k: os.environ.get(k) for k in keys}
+    for k in keys:
+        os.environ[k] = "1"
+    try:
+        return mp.get_context("spawn").Pool(n), n
+    finally:
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+
+
+def _pool_map(fn, tasks, timeout=600.0):
+    """Run fn over tasks in the pool; (results, pool wall seconds, workers).
+    A pool whose workers cannot start or do not finish within `timeout` is
+    terminated and the failure raised (the benchmark never waits forever)."""
+    pool, nw = _pool(len(tasks))
+    try:
+        t0 = time.perf_counter()
+        res = pool.map_async(fn, tasks, chunksize=1).get(timeout=timeout)
+        wall = time.perf_counter() - t0
+        pool.close()
+    except BaseException:
+        pool.terminate()
+        raise
+    finally:
+        pool.join()
+    return res, wall, nw
+
+
+def _critical_path(results):
+    """results: (pid, seconds...) per unit.  Per part, the largest per-worker
+    sum of op seconds: the time the pool needs for the op work (the untimed
+    conversion of each unit's inputs into the oracle's arrays excluded)."""
+    per = {}
+    for r in results:
+        acc = per.setdefault(r[0], [0.0] * (len(r) - 1))
+        for i, t in enumerate(r[1:]):
+            acc[i] += t
+    parts = [max(v[i] for v in per.values()) for i in range(len(results[0]) - 1)]
+    total = max(sum(v) for v in per.values())
+    return parts, total, len(per)
+
+
+def _cpu_step_unit(task):
+    """One (sequence, layer) unit in a pool worker: the oracle holds that
+    layer of the sequence, applies the fused drop + reposition and the decode
+    attention; returns (pid, seconds of each)."""
+    from oracle import akv_oracle as O
+    n = task["k"].shape[0]
+    oc = O.OracleCache(1, task["H"], task["D"], task["base"])
+    oc.append(0, np.arange(n), O.bf16_from_bits(task["k"])[:, None],
+              O.bf16_from_bits(task["v"])[:, None])
+    t0 = time.perf_counter()
+    oc.drop_reposition(0, task["mask"])
+    t1 = time.perf_counter()
+    oc.decode_attention(0, task["q"][None])
+    t2 = time.perf_counter()
+    return os.getpid(), t1 - t0, t2 - t1
+
+
+def _u16(t):
+    """Host uint16 bit patterns of a bf16 tensor."""
+    import torch
+    return t.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def cpu_baseline(wl, layers, seqs=None):
+    """The fp64 oracle as it stands, on a bounded sample of the workload
+    (the listed layers of the listed sequences, every token), one (sequence,
+    layer) unit per task of a process pool; bytes are the sample's share of
+    the same algorithmic bytes as the GPU figure."""
+    import torch
 
     from agent_kv_cache_amd import harness as Hn
     from agent_kv_cache_amd.workloads import randn_bf16
-    from oracle import akv_oracle as O
-    import torch
 
     sh = wl.shape
-    layers = list(range(0, sh.n_layers, layer_stride))
-    oc = O.OracleCache(len(layers), sh.n_kv_heads, sh.head_dim, sh.rope_base, n_seqs=wl.n_seqs)
-    gen = "cuda" if torch.cuda.is_available() else "cpu"
-    for b, n in enumerate(wl.seq_lens):
+    seqs = list(range(wl.n_seqs)) if seqs is None else list(seqs)
+    q = randn_bf16((wl.n_seqs, sh.n_layers, sh.n_q_heads, sh.head_dim), 202, device="cuda")
+    tasks = []
+    for b in seqs:
+        n = wl.seq_lens[b]
+        ks, vs = [], []
         for c in range((n + Hn.CHUNK - 1) // Hn.CHUNK):
             m = min(Hn.CHUNK, n - c * Hn.CHUNK)
-            k = Hn.seq_chunk(sh, wl.data_seed, b, c, m, "k", gen)[layers]
-            v = Hn.seq_chunk(sh, wl.data_seed, b, c, m, "v", gen)[layers]
-            oc.append(b, (b << 24) + c * Hn.CHUNK + np.arange(m),
-                      k.permute(1, 0, 2, 3).cpu().double().numpy(),
-                      v.permute(1, 0, 2, 3).cpu().double().numpy())
-    q = randn_bf16((wl.n_seqs, len(layers), sh.n_q_heads, sh.head_dim), 202,
-                   device=gen).cpu().double().numpy()
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        for b in range(wl.n_seqs):
-            oc.drop_reposition(b, wl.masks[b])
-        t1 = time.perf_counter()
-        for b in range(wl.n_seqs):
-            oc.decode_attention(b, q[b])
-        t2 = time.perf_counter()
-    ab = algorithmic_bytes(sh, wl.seq_lens, wl.masks)
+            ks.append(_u16(Hn.seq_chunk(sh, wl.data_seed, b, c, m, "k", "cuda")[layers]))
+            vs.append(_u16(Hn.seq_chunk(sh, wl.data_seed, b, c, m, "v", "cuda")[layers]))
+        k, v = np.concatenate(ks, axis=1), np.concatenate(vs, axis=1)
+        for i, l in enumerate(layers):
+            tasks.append(dict(H=sh.n_kv_heads, D=sh.head_dim, base=sh.rope_base,
+                              k=np.ascontiguousarray(k[i]), v=np.ascontiguousarray(v[i]),
+                              mask=np.asarray(wl.masks[b][:n]),
+                              q=q[b, l].double().cpu().numpy()))
+    del q
+    torch.cuda.empty_cache()
+    res, wall, nw = _pool_map(_cpu_step_unit, tasks)
+    (t_dr, t_dec), t_all, used = _critical_path(res)
+    ab = algorithmic_bytes(sh, [wl.seq_lens[b] for b in seqs], [wl.masks[b] for b in seqs])
     frac = len(layers) / sh.n_layers
-    b_total = (ab["b_dr"] + ab["b_att"]) * frac
+    cpu_s = sum(r[1] + r[2] for r in res)
     return {
-        "value": round(b_total / (t2 - t0) / 1e9, 4),
+        "value": round((ab["b_dr"] + ab["b_att"]) * frac / t_all / 1e9, 4),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": used,
         "kind": "oracle",
-        "sample": f"{wl.name}: layers {layers[0]}..{layers[-1]} step {layer_stride} "
-                  f"({len(layers)} of {sh.n_layers}), all tokens; fused drop+reposition "
-                  f"{t1 - t0:.2f} s + decode {t2 - t1:.2f} s on one host core"
-                  + (", bytes scaled by the layer fraction" if len(layers) < sh.n_layers
-                     else ""),
-        "drop_reposition_gbps": round(ab["b_dr"] * frac / (t1 - t0) / 1e9, 4),
-        "decode_gbps": round(ab["b_att"] * frac / (t2 - t1) / 1e9, 4),
+        "sample": f"{wl.name}: layer(s) {layers} of {sh.n_layers} x {len(seqs)} of {wl.n_seqs} "
+                  f"sequence(s), every token ({len(tasks)} (sequence, layer) units); fused "
+                  f"drop+reposition then decode per unit in a {nw}-process pool: "
+                  f"{cpu_s:.1f} s of op work, {t_all:.2f} s on the busiest worker "
+                  f"({wall:.1f} s pool wall time including unpacking the inputs); bytes are "
+                  f"the sample's share of the algorithmic bytes",
+        "drop_reposition_gbps": round(ab["b_dr"] * frac / t_dr / 1e9, 4),
+        "decode_gbps": round(ab["b_att"] * frac / t_dec / 1e9, 4),
+        **host_info(),
     }
+
+
+def _cpu_history_unit(task):
+    """One layer of the 50-turn history in a pool worker: the oracle replays
+    every op on that layer (appends untimed), then the final decode."""
+    from oracle import akv_oracle as O
+    oc = O.OracleCache(1, task["H"], task["D"], task["base"])
+    t_ops = 0.0
+    for op in task["ops"]:
+        if op[0] == "append":
+            _, tid, k, v = op
+            oc.append(0, tid, O.bf16_from_bits(k)[:, None], O.bf16_from_bits(v)[:, None])
+            continue
+        t0 = time.perf_counter()
+        if op[0] == "drop":
+            oc.drop(0, op[1])
+        elif op[0] == "repos":
+            oc.reposition(0)
+        else:
+            oc.drop_reposition(0, op[1])
+        t_ops += time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oc.decode_attention(0, task["q"][None])
+    return os.getpid(), t_ops, time.perf_counter() - t0
 
 
 def run_history(args):
@@ -167,9 +301,11 @@ def run_history(args):
     cache = Hn.make_cache(sh, [1], 4096, max_blocks_per_seq=maxpg)
     cache.reset()
     dev = cache.device
-    tot_bytes = tot_ms = 0.0
+    tot_bytes = tot_ms = mv_bytes = mv_ms = 0.0
     n_ops = 0
     per_op = []
+    cpu_layers = [0, sh.n_layers - 1]            # the CPU baseline's layer sample
+    cpu_ops = []                                 # the same op list for the oracle
     for op in hist.ops:
         if op[0] == "append":
             mid, n = op[1], op[2]
@@ -178,10 +314,15 @@ def run_history(args):
             tid = torch.arange(hist.msg_start[mid], hist.msg_start[mid] + n, dtype=torch.int32,
                                device=dev)
             cache.append(torch.tensor([n], dtype=torch.int32, device=dev), n, k, v, tid)
+            if not args.no_cpu_baseline:
+                cpu_ops.append(("append", tid.cpu().numpy().astype(np.int64),
+                                _u16(k[cpu_layers]), _u16(v[cpu_layers])))
             continue
         tok0, pos0, _ = cache.seq_state(0)
         mask = (W.mask_for_messages(tok0, hist, op[1]) if op[0] != "repos"
                 else np.zeros(len(tok0), np.uint8))
+        if not args.no_cpu_baseline:
+            cpu_ops.append((op[0], mask))
         mt = Hn.mask_tensor(cache, [mask])
         torch.cuda.synchronize()
         cache.profile_read("plan", reset=True)
@@ -196,6 +337,7 @@ def run_history(args):
         if cache.sync_status() != 0:
             raise RuntimeError(f"device status after {op}")
         ms = sum(cache.profile_read(k)[0] for k in ("plan", "move", "commit"))
+        mv_ms += cache.profile_read("move")[0]
         keep = mask == 0
         r = int(keep.sum())
         f = int(np.flatnonzero(mask)[0]) if mask.any() else len(mask)
@@ -203,6 +345,7 @@ def run_history(args):
         new_pos = np.arange(r) if op[0] != "drop" else pos0[keep]
         inplace = int((new_pos[:int(keep[:f].sum())] != pos0[:f][keep[:f]]).sum())
         b = moved * 4 * row + 12 * moved + inplace * 2 * row + len(mask) + 4 * r
+        mv_bytes += moved * 4 * row + 12 * moved + inplace * 2 * row
         tot_bytes += b
         tot_ms += ms
         n_ops += 1
@@ -222,10 +365,44 @@ def run_history(args):
     cache.profile_enable(False)
     att_ms = (cache.profile_read("attn")[0] + cache.profile_read("combine")[0]) / args.steps
     b_att = len(tok) * 2 * row + 2 * sh.n_layers * sh.n_q_heads * sh.head_dim * 2
-    return {
+    cpu = None
+    if not args.no_cpu_baseline:
+        del cache, ws, out
+        torch.cuda.empty_cache()
+        tasks = []
+        for i, l in enumerate(cpu_layers):
+            ops = [("append", o[1], np.ascontiguousarray(o[2][i]), np.ascontiguousarray(o[3][i]))
+                   if o[0] == "append" else o for o in cpu_ops]
+            tasks.append(dict(H=sh.n_kv_heads, D=sh.head_dim, base=sh.rope_base, ops=ops,
+                              q=q[0, l].double().cpu().numpy()))
+        res, wall, nw = _pool_map(_cpu_history_unit, tasks)
+        (t_ops, t_dec), t_all, used = _critical_path(res)
+        frac = len(cpu_layers) / sh.n_layers
+        cpu = {
+            "value": round((tot_bytes + b_att) * frac / t_all / 1e9, 4),
+            "unit": "GB/s", "cores": used, "kind": "oracle",
+            "sample": f"history_50_turns: layers {cpu_layers} of {sh.n_layers}, the whole "
+                      f"history replayed per layer ({n_ops} drop / reposition ops timed, appends "
+                      f"untimed) then the decode, one layer per process of a {nw}-process pool: "
+                      f"{t_all:.2f} s on the busiest worker ({wall:.1f} s pool wall time with "
+                      f"the appends); bytes are the sample's share of the algorithmic bytes",
+            "drop_reposition_gbps": round(tot_bytes * frac / t_ops / 1e9, 4),
+            "decode_gbps": round(b_att * frac / t_dec / 1e9, 4),
+            **host_info(),
+        }
+    out_d = {
         "metric": METRIC, "workload": "history_50_turns: 50-turn history, 131072 tokens appended, "
         "L=36 Hkv=8 d=64, 47 drops / 16 repositions, decode 64 q heads",
+        "value": round((tot_bytes + b_att) / ((tot_ms + att_ms) * 1e-3) / 1e9, 2), "unit": "GB/s",
+        "roofline": {"bound": "hbm", "kernel": "move_kernel",
+                     "achieved": round(mv_bytes / (mv_ms * 1e-3) / 1e9, 1),
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(mv_bytes / (mv_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                     "traffic": counted_traffic("move_kernel_history_50_turns_counters.json"),
+                     "launch_bytes_note": "per-op launches of different sizes: achieved = "
+                                          "moved bytes of all ops / move kernel time of all ops"},
         "ops": n_ops, "ops_ms_total": round(tot_ms, 4), "ops_bytes_total": int(tot_bytes),
+        "move_ms_total": round(mv_ms, 4),
         "drop_reposition_gbps": round(tot_bytes / (tot_ms * 1e-3) / 1e9, 1),
         "drop_reposition_frac_of_peak": round(tot_bytes / (tot_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
         "decode_ms": round(att_ms, 4), "decode_bytes": b_att,
@@ -234,6 +411,9 @@ def run_history(args):
         "final_active": len(tok),
         "per_op": per_op[-6:],
     }
+    if cpu:
+        out_d["cpu_baseline"] = cpu
+    return out_d
 
 
 def counted_traffic(name):
@@ -527,63 +707,25 @@ def calibrate(nbytes: int, reps: int):
     return {"calibration": out, "buffer_bytes": nbytes}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="llama8b_32k",
-                    choices=["one_layer_4k", "llama8b_32k", "ragged_batch_64", "history_50_turns",
-                             "llama70b_4x64k", "restore", "append"])
-    ap.add_argument("--cpu-rows", type=int, default=256,
-                    help="restore: rows per segment in the oracle sample")
-    ap.add_argument("--rotary-dim", type=int, default=0,
-                    help="partial RoPE: rotate only the first R dims of each head")
-    ap.add_argument("--freq", default="base", choices=["base", "llama3", "yarn"],
-                    help="RoPE frequency schedule (Llama 3.1 or YaRN tables)")
-    ap.add_argument("--window", type=int, default=0,
-                    help="sliding-window length for decode in all but every "
-                         "--window-every-th layer")
-    ap.add_argument("--window-every", type=int, default=2)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--graph", action="store_true",
-                    help="also time the step captured once in a HIP graph and replayed "
-                         "(reported as graph_ms_per_step; per-kernel times stay eager)")
-    ap.add_argument("--cpu-layer-stride", type=int, default=0,
-                    help="oracle sample: every n-th layer (0 = all layers for one_layer_4k / llama8b_32k, "
-                         "every 8th for the larger workloads)")
-    ap.add_argument("--calibrate", type=int, default=0, metavar="BYTES",
-                    help="instead of the workload, time plain device copy / fill / read "
-                         "kernels over BYTES (the reference kernels whose counter readings "
-                         "scale the HBM byte counters)")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: the library has no multi-GPU path "
-              "(the hot path shards by kv head / layer with no exchange).",
-              file=sys.stderr)
-        sys.exit(2)
+# Oracle sample per workload: (layers, sequences or None = all), about
+# 10-40 s of single-core oracle work, spread over the pool.
+CPU_SAMPLE = {
+    "one_layer_4k": ([0], None),
+    "llama8b_32k": (list(range(0, 32, 2)), None),
+    "ragged_batch_64": ([0], None),
+    "llama70b_4x64k": ([0, 40], None),
+}
 
+
+def run_step(name, args):
+    """One drop+reposition + decode workload: set up, time the steps, and
+    return its JSON line (GPU memory released before returning)."""
     import torch
 
     from agent_kv_cache_amd import harness as Hn
     from agent_kv_cache_amd import workloads as W
-    from agent_kv_cache_amd.binding import lib
 
-    torch.cuda.set_device(0)
-    if args.calibrate:
-        print(json.dumps(calibrate(args.calibrate, args.steps)), flush=True)
-        return
-    lib()
-    if args.workload == "history_50_turns":
-        print(json.dumps(run_history(args)), flush=True)
-        return
-    if args.workload == "restore":
-        print(json.dumps(run_restore(args)), flush=True)
-        return
-    if args.workload == "append":
-        print(json.dumps(run_append(args)), flush=True)
-        return
-    wl = W.WORKLOADS[args.workload]()
+    wl = W.WORKLOADS[name]()
     sh = wl.shape
     extra = sum(Hn.moved_pages(n, m) for n, m in zip(wl.seq_lens, wl.masks)) + 8
     ropt = rope_options(args, sh)
@@ -719,8 +861,90 @@ def main():
         res["graph_ms_per_step"] = round(gms, 4)
         res["graph_value"] = round((ab["b_dr"] + ab["b_att"]) / (gms * 1e-3) / 1e9, 2)
     if not args.no_cpu_baseline and not ropt:
-        stride = args.cpu_layer_stride or (1 if wl.name in ("one_layer_4k", "llama8b_32k") else 8)
-        res["cpu_baseline"] = cpu_baseline(wl, stride)
+        layers, seqs = CPU_SAMPLE[wl.name]
+        res["cpu_baseline"] = cpu_baseline(wl, layers, seqs)
+    del cache, q, out, ws, mask, snap
+    torch.cuda.empty_cache()
+    return res
+
+
+def compact(line):
+    """The fields of a workload line kept under the default run's `configs`."""
+    keep = ("value", "unit", "ms_per_step", "steps", "warmup", "roofline", "parts",
+            "cpu_baseline", "ops", "ops_ms_total", "ops_bytes_total", "drop_reposition_gbps",
+            "drop_reposition_frac_of_peak", "decode_ms", "decode_gbps", "decode_frac_of_peak",
+            "final_active")
+    out = {k: line[k] for k in keep if k in line}
+    out["workload"] = line.get("config", {}).get("workload", line.get("workload"))
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="all",
+                    choices=["all", "one_layer_4k", "llama8b_32k", "ragged_batch_64",
+                             "history_50_turns", "llama70b_4x64k", "restore", "append"],
+                    help="all (default): the ragged batch as the headline, the other "
+                         "configurations under `configs`")
+    ap.add_argument("--cpu-rows", type=int, default=256,
+                    help="restore: rows per segment in the oracle sample")
+    ap.add_argument("--rotary-dim", type=int, default=0,
+                    help="partial RoPE: rotate only the first R dims of each head")
+    ap.add_argument("--freq", default="base", choices=["base", "llama3", "yarn"],
+                    help="RoPE frequency schedule (Llama 3.1 or YaRN tables)")
+    ap.add_argument("--window", type=int, default=0,
+                    help="sliding-window length for decode in all but every "
+                         "--window-every-th layer")
+    ap.add_argument("--window-every", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured once in a HIP graph and replayed "
+                         "(reported as graph_ms_per_step; per-kernel times stay eager)")
+    ap.add_argument("--calibrate", type=int, default=0, metavar="BYTES",
+                    help="instead of the workload, time plain device copy / fill / read "
+                         "kernels over BYTES (the reference kernels whose counter readings "
+                         "scale the HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(the hot path shards by kv head / layer with no exchange).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from agent_kv_cache_amd.binding import lib
+
+    torch.cuda.set_device(0)
+    if args.calibrate:
+        print(json.dumps(calibrate(args.calibrate, args.steps)), flush=True)
+        return
+    lib()
+    if args.workload == "history_50_turns":
+        print(json.dumps(run_history(args)), flush=True)
+        return
+    if args.workload == "restore":
+        print(json.dumps(run_restore(args)), flush=True)
+        return
+    if args.workload == "append":
+        print(json.dumps(run_append(args)), flush=True)
+        return
+    if args.workload != "all":
+        print(json.dumps(run_step(args.workload, args)), flush=True)
+        return
+    # default: every configuration, the largest single-GPU one as the headline
+    t0 = time.time()
+    res = run_step("ragged_batch_64", args)
+    print(f"[bench] ragged_batch_64 done ({time.time() - t0:.0f} s)", file=sys.stderr, flush=True)
+    res["configs"] = {}
+    for name in ("llama8b_32k", "one_layer_4k", "llama70b_4x64k"):
+        res["configs"][name] = compact(run_step(name, args))
+        print(f"[bench] {name} done ({time.time() - t0:.0f} s)", file=sys.stderr, flush=True)
+    res["configs"]["history_50_turns"] = compact(run_history(args))
+    print(f"[bench] history_50_turns done ({time.time() - t0:.0f} s)", file=sys.stderr, flush=True)
     print(json.dumps(res), flush=True)
 
 
