@@ -21,7 +21,7 @@ STATUS = {0: "AKV_OK", 1: "AKV_ERR_ARG", 2: "AKV_ERR_ORDER", 3: "AKV_ERR_POS_MIS
           4: "AKV_ERR_NO_BLOCKS", 5: "AKV_ERR_CAPACITY", 6: "AKV_ERR_HIP",
           7: "AKV_ERR_SCRATCH"}
 KERNELS = {"plan": 0, "move": 1, "commit": 2, "attn": 3, "combine": 4, "append": 5,
-           "segment": 6, "release": 7}
+           "segment": 6, "release": 7, "rounds": 8}
 PAGE = 16
 
 

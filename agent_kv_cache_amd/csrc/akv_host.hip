@@ -159,14 +159,19 @@ akv_status run_compaction(akv_cache *c, const uint8_t *mask, const int32_t *new_
     Timed tm(c, AKV_KERNEL_PLAN, st);
     AKV_HIP(akv::launch_plan(c->dev, mask, new_pos, old_pos, mode, rounds, st));
   }
-  for (int g = 0; g < rounds; ++g) {
-    {
-      Timed tm(c, AKV_KERNEL_MOVE, st);
-      AKV_HIP(akv::launch_move(c->dev, mode, (c->move_persistent || g > 0) ? c->move_grid : 0,
-                               c->oneshot_cap, g, st));
-    }
-    {
-      Timed tm(c, AKV_KERNEL_COMMIT, st);
+  {
+    Timed tm(c, AKV_KERNEL_MOVE, st);
+    AKV_HIP(akv::launch_move(c->dev, mode, c->move_persistent ? c->move_grid : 0,
+                             c->oneshot_cap, 0, st));
+  }
+  {
+    Timed tm(c, AKV_KERNEL_COMMIT, st);
+    AKV_HIP(akv::launch_commit(c->dev, 0, st));
+  }
+  if (rounds > 1) {
+    Timed tm(c, AKV_KERNEL_ROUNDS, st);
+    for (int g = 1; g < rounds; ++g) {
+      AKV_HIP(akv::launch_move(c->dev, mode, c->move_grid, c->oneshot_cap, g, st));
       AKV_HIP(akv::launch_commit(c->dev, g, st));
     }
   }

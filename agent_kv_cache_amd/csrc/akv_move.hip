@@ -85,9 +85,7 @@ __device__ __forceinline__ void st_stream(uint16_t *p, u32x4 v) {
 // partner (c +- r/16) is read from the lane that holds it (the same row's
 // lanes are adjacent), tail chunks are only copied.
 template <int D, bool NT, bool ONESHOT, bool FR>
-__global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(Dev d, int mode,
-                                                                                 int oneshot_cap,
-                                                                                 int group) {
+__device__ __forceinline__ void move_body(const Dev &d, int mode, int oneshot_cap, int group) {
   constexpr int HALF = D / 2;
   constexpr int CH = D / 16;             // 16-B chunks per half row
   constexpr int CPR = FR ? 2 * CH : CH;  // threads per row
@@ -295,6 +293,23 @@ __global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(
   }
 }
 
+// The first round of an op (every op that fits the free pool at once).
+template <int D, bool NT, bool ONESHOT, bool FR>
+__global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_kernel(Dev d, int mode,
+                                                                                 int oneshot_cap) {
+  move_body<D, NT, ONESHOT, FR>(d, mode, oneshot_cap, 0);
+}
+
+// Later rounds of an op split into sequence groups (persistent shape).  A
+// kernel of its own, so that profiles keep the first round's launches apart
+// from these, which exit at once whenever the op needed fewer groups.
+template <int D, bool NT, bool FR>
+__global__ __launch_bounds__(kMoveThreads, AKV_MOVE_MIN_WAVES) void move_round_kernel(Dev d,
+                                                                                       int mode,
+                                                                                       int group) {
+  move_body<D, NT, false, FR>(d, mode, 0, group);
+}
+
 // Group 0: the one-shot launch, then (grid > 0) the persistent one; each
 // checks the group's unit count and only one of them moves.  Later groups (an
 // op split because the free pool was short): the persistent launch alone,
@@ -305,12 +320,12 @@ static void launch_move_pair(const Dev &d, int mode, int grid, int oneshot_cap, 
   const dim3 b(kMoveThreads);
   if (group == 0) {
     hipLaunchKernelGGL((move_kernel<D, NT, true, FR>), dim3(oneshot_cap), b, 0, st, d, mode,
-                       oneshot_cap, 0);
+                       oneshot_cap);
     if (grid > 0)
       hipLaunchKernelGGL((move_kernel<D, NT, false, FR>), dim3(grid), b, 0, st, d, mode,
-                         oneshot_cap, 0);
+                         oneshot_cap);
   } else {
-    hipLaunchKernelGGL((move_kernel<D, NT, false, FR>), dim3(grid), b, 0, st, d, mode, 0, group);
+    hipLaunchKernelGGL((move_round_kernel<D, NT, FR>), dim3(grid), b, 0, st, d, mode, group);
   }
 }
 

@@ -348,7 +348,8 @@ enum {
   AKV_KERNEL_APPEND = 5,   /* append plan + copy */
   AKV_KERNEL_SEGMENT = 6,  /* segment-batch attention */
   AKV_KERNEL_RELEASE = 7,  /* page release */
-  AKV_KERNEL_COUNT = 8
+  AKV_KERNEL_ROUNDS = 8,   /* later (move, commit) rounds of an op split into sequence groups */
+  AKV_KERNEL_COUNT = 9
 };
 akv_status akv_profile_enable(akv_cache *c, int on);
 /* Synchronises the recorded events; *total_ms and *launches accumulate
