@@ -90,7 +90,7 @@ __global__ __launch_bounds__(kChunkPages) void plan_kernel(
     Dev d, const uint8_t *__restrict__ mask, const int32_t *__restrict__ new_pos,
     const int32_t *__restrict__ old_pos, int mode, int max_groups) {
   __shared__ int s_wave[kChunkPages / 64 + 1];
-  __shared__ int s_last, s_gerr, s_fdrop, s_ok;
+  __shared__ int s_last, s_gerr, s_fdrop, s_ok, s_nextra;
   __shared__ int s_src[kChunkPages * kPage], s_dlt[kChunkPages * kPage];
   __shared__ int s_lsrc[kChunkPages * kPage];
   const int c = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
@@ -217,12 +217,15 @@ __global__ __launch_bounds__(kChunkPages) void plan_kernel(
   } else {
     __syncthreads();
   }
-  if (t == 0) s_gerr = 0;
+  if (t == 0) {
+    s_gerr = 0;
+    s_nextra = 0;
+  }
   __syncthreads();
   int run_m = 0, run_i = 0, run_f = 0;
   for (int b0 = 0; b0 < d.B; b0 += kChunkPages) {
     const int bb = b0 + t;
-    int nm = 0, ni = 0, nf = 0;
+    int nm = 0, ni = 0, nf = 0, nfx = 0;
     int *si = d.seq_info + (size_t)bb * kSeqInfo;
     if (bb < d.B) {
       const int dst = (mode & M_FORK) ? d.fork_dst[bb] : -1;
@@ -250,12 +253,20 @@ __global__ __launch_bounds__(kChunkPages) void plan_kernel(
       si[SI_FPOS] = INT_MAX;
       si[SI_ERR] = 0;
       const int Pn = (rnew + kPage - 1) / kPage;
+      const int nsh = si[SI_NSHARED];   // pages [0, nsh) may be shared
       int fbd = P0;
       int ee = e;
+      int sh_new = nsh;
       if (mode & M_FORK) {
-        // every survivor goes to fresh pages of the (empty) destination
-        fbd = 0;
-        nm = dst >= 0 ? Pn : 0;
+        // The version shares the source's leading full pages whose entries it
+        // leaves as they are (before the first dropped entry and the first
+        // changed position; ranks equal indices there); every other survivor
+        // goes to fresh pages of the (empty) destination.
+        int keep_n = min(fdrop, L0);
+        if ((mode & M_REPOS) && fpos < keep_n) keep_n = fpos;
+        fbd = dst >= 0 ? keep_n / kPage : 0;
+        nm = dst >= 0 ? Pn - fbd : 0;
+        if (dst >= 0) sh_new = max(nsh, fbd);
         if (dst >= 0 && d.lens[dst] != 0) ee = max(ee, (int)AKV_ERR_ARG);
       } else if ((mode & M_DROP) && fdrop < L0) {
         fbd = fdrop / kPage;
@@ -268,15 +279,34 @@ __global__ __launch_bounds__(kChunkPages) void plan_kernel(
         if (fpos < rnew && !(mode & M_FORK)) {
           fip = fpos / kPage;
           ni = max(0, min(fbd, Pn) - fip);
+          if (ni > 0 && fip < nsh) {
+            // copy on write: a page another sequence may hold is never turned
+            // in place; from the first changed page on, the sequence is
+            // rebuilt in fresh pages
+            fbd = fip;
+            nm = max(0, Pn - fbd);
+            nf = P0 - fbd;
+            ni = 0;
+          }
         }
         nnext = rnew == 0 ? 0 : ((mode & M_NEWPOS) ? new_pos[(size_t)bb * S + rnew - 1] + 1 : rnew);
       }
+      // released pages [fbd, fbd + nf): the first ms may be held by other
+      // sequences too (reference-counted), the rest return to the free stack
+      int ms = 0;
+      if (!(mode & M_FORK)) {
+        ms = max(0, min(nsh, fbd + nf) - fbd);
+        sh_new = min(nsh, fbd);
+      }
+      nfx = nf - ms;
       si[SI_NEW_LEN] = rnew;
       si[SI_FBD] = fbd;
       si[SI_FIP] = fip;
       si[SI_N_MOVE] = nm;
       si[SI_N_INPLACE] = ni;
       si[SI_N_FREED] = nf;
+      si[SI_N_SHREL] = ms;
+      si[SI_SH_NEW] = sh_new;
       si[SI_NEW_NEXT] = nnext;
       si[SI_OLD_LEN] = L0;
       si[SI_DST] = dst;
@@ -285,7 +315,7 @@ __global__ __launch_bounds__(kChunkPages) void plan_kernel(
     int tm, ti, tf;
     const int em = block_exclusive_scan<kChunkPages>(nm, s_wave, &tm);
     const int ei = block_exclusive_scan<kChunkPages>(ni, s_wave, &ti);
-    const int ef = block_exclusive_scan<kChunkPages>(nf, s_wave, &tf);
+    const int ef = block_exclusive_scan<kChunkPages>(nfx, s_wave, &tf);   // pages pushed
     if (bb < d.B) {
       si[SI_MOVE_OFF] = run_m + em;
       si[SI_INPLACE_OFF] = run_i + ei;
@@ -335,7 +365,7 @@ __global__ __launch_bounds__(kChunkPages) void plan_kernel(
           if (!e && nm > fcur) e = AKV_ERR_NO_BLOCKS;
           gm += nm;
           gi += si[SI_N_INPLACE];
-          gf += si[SI_N_FREED];
+          gf += si[SI_N_FREED] - si[SI_N_SHREL];
         }
         if (!e) close(d.B);
       } else {
@@ -373,54 +403,162 @@ __global__ __launch_bounds__(kChunkPages) void plan_kernel(
         sd[SI_LSRC_LEN] = d.seq_info[(size_t)bb * kSeqInfo + SI_NEW_LEN];
       }
     }
+  if (s_ok) {
+    // shared prefixes: every planned sequence's bound after the op; a fork's
+    // destination shares its source's first SI_FBD pages
+    for (int bb = t; bb < d.B; bb += kChunkPages) {
+      int *si = d.seq_info + (size_t)bb * kSeqInfo;
+      if (!(mode & M_FORK) || d.fork_dst[bb] >= 0) si[SI_NSHARED] = si[SI_SH_NEW];
+    }
+    __syncthreads();
+    if (mode & M_FORK) {
+      for (int bb = t; bb < d.B; bb += kChunkPages) {
+        const int dst = d.fork_dst[bb];
+        if (dst >= 0)
+          d.seq_info[(size_t)dst * kSeqInfo + SI_NSHARED] = d.seq_info[(size_t)bb * kSeqInfo + SI_FBD];
+      }
+    } else {
+      // Released pages that may be shared lose one reference; a page whose
+      // last reference this was goes on the list the op's last commit round
+      // pushes (after every move has read its fresh page ids).  The list's
+      // order follows the atomics; the pages are the same either way.
+      for (int bb = t; bb < d.B; bb += kChunkPages) {
+        const int *si = d.seq_info + (size_t)bb * kSeqInfo;
+        const int ms = si[SI_N_SHREL];
+        const int32_t *trow = d.table + (size_t)bb * d.maxpg + si[SI_FBD];
+        for (int k0 = 0; k0 < ms; k0 += 8) {
+          int pgs[8], old[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) pgs[u] = k0 + u < ms ? trow[k0 + u] : -1;
+#pragma unroll
+          for (int u = 0; u < 8; ++u) old[u] = pgs[u] >= 0 ? atomicSub(&d.share[pgs[u]], 1) : 1;
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (old[u] == 0) {
+              d.share[pgs[u]] = 0;
+              d.ex_list[atomicAdd(&s_nextra, 1)] = pgs[u];
+            }
+        }
+      }
+    }
+    __syncthreads();
+    if (t == 0) d.ctl[CTL_NEXTRA] = s_nextra;
+  }
+  if (s_ok && (mode & M_STAGED)) {
+    // One-sequence cache (one group, no fork): commit here.  The fresh page
+    // ids go to the staging array first (the move reads them there, not from
+    // the free stack), then the old pages are pushed over the region they
+    // came from, so nothing of the commit waits for the move; the move runs
+    // after this kernel in stream order and reads only plan records, source
+    // slots and the untouched prefix of the page table.
+    // (each thread loads a batch of 8 before storing any: independent loads
+    // in flight instead of one round trip per entry)
+    constexpr int kB = 8;
+    const int *gr = d.groups;
+    const int Tm = gr[GR_TM], fc0 = gr[GR_FC], F = gr[GR_F];
+    for (int k0 = t; k0 < Tm; k0 += kChunkPages * kB) {
+      int v[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        const int k = k0 + u * kChunkPages;
+        v[u] = k < Tm ? d.free_stack[fc0 - 1 - k] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        const int k = k0 + u * kChunkPages;
+        if (k < Tm) d.stage[k] = v[u];
+      }
+    }
+    __syncthreads();
+    const int *si = d.seq_info;
+    const int fbd = si[SI_FBD], nmove = si[SI_N_MOVE], nfreed = si[SI_N_FREED];
+    const int base = fc0 - Tm;
+    int32_t *trow = d.table;
+    for (int k0 = t; k0 < nfreed; k0 += kChunkPages * kB) {
+      int old[kB], fresh[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        const int k = k0 + u * kChunkPages;
+        old[u] = k < nfreed ? trow[fbd + k] : 0;
+        fresh[u] = k < nmove ? d.stage[k] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        const int k = k0 + u * kChunkPages;
+        if (k < nfreed) {
+          d.free_stack[base + F - 1 - k] = old[u];   // reversed, as in commit_kernel
+          trow[fbd + k] = fresh[u];
+        }
+      }
+    }
+    if (t == 0) {
+      d.lens[0] = si[SI_NEW_LEN];
+      d.next_pos[0] = si[SI_NEW_NEXT];
+      *d.free_count = base + F;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
 // commit
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void commit_kernel(Dev d, int group) {
-  if (d.ctl[CTL_OP_OK] == 0 || group >= d.ctl[CTL_NGROUPS]) return;
+  const int ng = d.ctl[CTL_NGROUPS];
+  if (d.ctl[CTL_OP_OK] == 0 || group >= ng) return;
   const int *gr = d.groups + (size_t)group * kGroupRec;
   const int b = blockIdx.x;
   const int s0 = gr[GR_S0];
   if (b < s0 || b >= gr[GR_S1]) return;
   const int *si = d.seq_info + (size_t)b * kSeqInfo;
   const int fbd = si[SI_FBD], nmove = si[SI_N_MOVE], nfreed = si[SI_N_FREED];
+  const int ms = si[SI_N_SHREL];
   const int moff = si[SI_MOVE_OFF], foff = si[SI_FREED_OFF] - gr[GR_FOFF];
   const int base = gr[GR_FC] - gr[GR_TM];   // the group's fresh pages came from [base, GR_FC)
   const int ftot = gr[GR_F];
+  // The op's last round also pushes the shared pages the plan saw released
+  // for the last time, above the group's own.
+  const int nx = (group == ng - 1) ? d.ctl[CTL_NEXTRA] : 0;
+  if (b == s0) {
+    for (int i = threadIdx.x; i < nx; i += blockDim.x) d.free_stack[base + ftot + i] = d.ex_list[i];
+    if (threadIdx.x == 0) *d.free_count = base + ftot + nx;
+  }
   const int dst = si[SI_DST];
   if (dst >= 0) {
-    // fork: the new version takes the fresh pages; the source is untouched
+    // fork: the new version holds the source's first fbd pages too (one more
+    // reference each) and takes the fresh pages after them; the source's
+    // page table is untouched
+    const int32_t *srow = d.table + (size_t)b * d.maxpg;
     int32_t *drow = d.table + (size_t)dst * d.maxpg;
-    for (int k = threadIdx.x; k < nmove; k += blockDim.x) drow[k] = d.stage[moff + k];
+    for (int k = threadIdx.x; k < fbd; k += blockDim.x) {
+      const int pg = srow[k];
+      drow[k] = pg;
+      atomicAdd(&d.share[pg], 1);
+    }
+    for (int k = threadIdx.x; k < nmove; k += blockDim.x) drow[fbd + k] = d.stage[moff + k];
     if (threadIdx.x == 0) {
       d.lens[dst] = si[SI_NEW_LEN];
       d.next_pos[dst] = si[SI_NEW_NEXT];
     }
-    if (b == s0 && threadIdx.x == 0) *d.free_count = base + ftot;
     return;
   }
-  if (d.ctl[CTL_MODE] & M_FORK) {
-    if (b == s0 && threadIdx.x == 0) *d.free_count = base + ftot;
-    return;
-  }
+  if (d.ctl[CTL_MODE] & M_FORK) return;
   // The freed pages go onto the stack in reverse (sequence b's first page on
   // top of b + 1's), so later pops hand them out in their old order: a
   // sequence rebuilt from them keeps ascending page runs, and the move's
   // blocks in flight keep reading and writing compact address ranges (a
-  // scattered page table costs the move ~11% on MI355X).
+  // scattered page table costs the move ~11% on MI355X).  The first ms
+  // released pages may be held by other sequences: the plan has already
+  // counted their references down.
   int32_t *trow = d.table + (size_t)b * d.maxpg;
   for (int k = threadIdx.x; k < nfreed; k += blockDim.x) {
     const int po = fbd + k;
     const int old = trow[po];
-    d.free_stack[base + ftot - 1 - (foff + k)] = old;
+    if (k >= ms) d.free_stack[base + ftot - 1 - (foff + k - ms)] = old;
     trow[po] = (k < nmove) ? d.stage[moff + k] : -1;
   }
   if (threadIdx.x == 0) {
     d.lens[b] = si[SI_NEW_LEN];
     d.next_pos[b] = si[SI_NEW_NEXT];
-    if (b == s0) *d.free_count = base + ftot;
   }
 }
 
@@ -661,43 +799,74 @@ __global__ __launch_bounds__(256) void append_copy_kernel(Dev d, int64_t n_new, 
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kPlanThreads) void release_kernel(Dev d, const uint8_t *sel) {
   __shared__ int s_wave[kPlanThreads / 64 + 1];
-  __shared__ int s_ok;
+  __shared__ int s_ok, s_nx;
+  __shared__ int s_np[kPlanThreads], s_ms[kPlanThreads], s_off[kPlanThreads];
   const int t = threadIdx.x;
-  if (t == 0) s_ok = d.ctl[CTL_ERR] == 0;    // a latched error makes mutating calls no-ops
+  if (t == 0) {
+    s_ok = d.ctl[CTL_ERR] == 0;    // a latched error makes mutating calls no-ops
+    s_nx = 0;
+  }
   __syncthreads();
   if (!s_ok) return;
   const int fc = *d.free_count;
-  // total pages released, so they can be pushed in reverse (the first
-  // sequence's first page on top: later pops return them in their old order)
+  // pages a flagged sequence holds alone (at or past its shared bound) are
+  // pushed in reverse (the first sequence's first page on top: later pops
+  // return them in their old order); `all` counts them
   int all = 0;
   for (int base = 0; base < d.B; base += kPlanThreads) {
     const int b = base + t;
-    int np = 0;
-    if (b < d.B && sel[b]) np = (d.lens[b] + kPage - 1) / kPage;
+    int nx = 0;
+    if (b < d.B && sel[b]) {
+      const int np = (d.lens[b] + kPage - 1) / kPage;
+      nx = np - min(np, d.seq_info[(size_t)b * kSeqInfo + SI_NSHARED]);
+    }
     int tot;
-    block_exclusive_scan<kPlanThreads>(np, s_wave, &tot);
+    block_exclusive_scan<kPlanThreads>(nx, s_wave, &tot);
     all += tot;
   }
   int run = 0;
   for (int base = 0; base < d.B; base += kPlanThreads) {
     const int b = base + t;
-    int np = 0;
-    if (b < d.B && sel[b]) np = (d.lens[b] + kPage - 1) / kPage;
-    int tot;
-    const int ex = block_exclusive_scan<kPlanThreads>(np, s_wave, &tot);
+    int np = 0, msb = 0;
     if (b < d.B && sel[b]) {
-      int32_t *row = d.table + (size_t)b * d.maxpg;
-      for (int k = 0; k < np; ++k) {
-        d.free_stack[fc + all - 1 - (run + ex + k)] = row[k];
+      np = (d.lens[b] + kPage - 1) / kPage;
+      msb = min(np, d.seq_info[(size_t)b * kSeqInfo + SI_NSHARED]);
+    }
+    int tot;
+    const int ex = block_exclusive_scan<kPlanThreads>(np - msb, s_wave, &tot);
+    s_np[t] = np;
+    s_ms[t] = msb;
+    s_off[t] = run + ex;
+    __syncthreads();
+    // all threads walk this chunk's flagged sequences, one page each
+    const int nb = min(kPlanThreads, d.B - base);
+    for (int i = 0; i < nb; ++i) {
+      const int n = s_np[i];
+      if (n == 0) continue;
+      const int m = s_ms[i], off = s_off[i];
+      int32_t *row = d.table + (size_t)(base + i) * d.maxpg;
+      for (int k = t; k < n; k += kPlanThreads) {
+        const int pg = row[k];
+        if (k >= m) {
+          d.free_stack[fc + all - 1 - (off + k - m)] = pg;
+        } else if (atomicSub(&d.share[pg], 1) == 0) {
+          // the last reference to a shared page
+          d.share[pg] = 0;
+          d.ex_list[atomicAdd(&s_nx, 1)] = pg;
+        }
         row[k] = -1;
       }
+    }
+    if (np || (b < d.B && sel[b])) {
       d.lens[b] = 0;
       d.next_pos[b] = 0;
+      d.seq_info[(size_t)b * kSeqInfo + SI_NSHARED] = 0;
     }
     run += tot;
+    __syncthreads();
   }
-  __syncthreads();
-  if (t == 0) *d.free_count = fc + run;
+  for (int i = t; i < s_nx; i += kPlanThreads) d.free_stack[fc + all + i] = d.ex_list[i];
+  if (t == 0) *d.free_count = fc + all + s_nx;
 }
 
 // ---------------------------------------------------------------------------
@@ -714,8 +883,12 @@ __global__ void reset_kernel(Dev d, const int32_t *order) {
     d.seq_info[i * kSeqInfo + SI_ERR] = 0;
     d.seq_info[i * kSeqInfo + SI_LSRC_ROW] = -1;     // no gather map yet
     d.seq_info[i * kSeqInfo + SI_LSRC_LEN] = 0;
+    d.seq_info[i * kSeqInfo + SI_NSHARED] = 0;      // nothing shared
   }
-  if (i < d.NB) d.free_stack[d.NB - 1 - i] = order ? order[i] : (int)i;
+  if (i < d.NB) {
+    d.free_stack[d.NB - 1 - i] = order ? order[i] : (int)i;
+    d.share[i] = 0;
+  }
   if (i == 0) {
     *d.free_count = d.NB;
     for (int c = 0; c < CTL_COUNT; ++c) d.ctl[c] = 0;

@@ -58,6 +58,7 @@ struct akv_cache {
   int n_cu = 256;
   int move_grid = 2048;
   int oneshot_cap = 1;     // blocks of the one-shot move launch (the largest op it moves)
+  long long layer_groups = 1;   // one-shot blocks per rebuilt page
   bool move_persistent = true;   // some op could be too large for the one-shot launch
   int attn_per_cu = 2;
   int op_groups = 1;       // (move, commit) rounds of a drop / reposition (1: the pool always fits)
@@ -152,19 +153,28 @@ int nsplit_for(const akv_cache *c, int nL) {
 // split; other ops get c->op_groups rounds (rounds past the groups the plan
 // made exit at once).
 akv_status run_compaction(akv_cache *c, const uint8_t *mask, const int32_t *new_pos,
-                          const int32_t *old_pos, int mode, void *stream) {
+                          const int32_t *old_pos, int mode, void *stream,
+                          long long max_pages = -1) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int rounds = (mode & akv::M_FORK) ? 1 : c->op_groups;
+  // a one-sequence cache is committed by the plan (one group, no fork)
+  if (c->desc.n_seqs == 1) mode |= akv::M_STAGED;
   {
     Timed tm(c, AKV_KERNEL_PLAN, st);
     AKV_HIP(akv::launch_plan(c->dev, mask, new_pos, old_pos, mode, rounds, st));
   }
+  // the persistent grid is needed only if this call could rebuild more
+  // (page, layer group) units than the one-shot grid holds: the cache-wide
+  // bound, or the caller's per-call bound (a fork copies at most
+  // max_blocks_per_seq pages per source)
+  bool persistent = c->move_persistent;
+  if (max_pages >= 0) persistent = max_pages * c->layer_groups > c->oneshot_cap;
   {
     Timed tm(c, AKV_KERNEL_MOVE, st);
-    AKV_HIP(akv::launch_move(c->dev, mode, c->move_persistent ? c->move_grid : 0,
-                             c->oneshot_cap, 0, st));
+    AKV_HIP(akv::launch_move(c->dev, mode, persistent ? c->move_grid : 0, c->oneshot_cap, 0,
+                             st));
   }
-  {
+  if (!(mode & akv::M_STAGED)) {
     Timed tm(c, AKV_KERNEL_COMMIT, st);
     AKV_HIP(akv::launch_commit(c->dev, 0, st));
   }
@@ -248,6 +258,8 @@ akv_status akv_cache_init(const akv_cache_desc *d, akv_cache **out) {
   v.window = reinterpret_cast<const int32_t *>(sb + c->layout.window);
   v.last_src = reinterpret_cast<int32_t *>(sb + c->layout.last_src);
   v.groups = reinterpret_cast<int32_t *>(sb + c->layout.groups);
+  v.share = reinterpret_cast<int32_t *>(sb + c->layout.share);
+  v.ex_list = reinterpret_cast<int32_t *>(sb + c->layout.ex_list);
   v.RD = rd;
   v.any_window = any_window;
   c->n_full_layers = d->n_layers;
@@ -279,6 +291,7 @@ akv_status akv_cache_init(const akv_cache_desc *d, akv_cache **out) {
                                                 (long long)d->n_seqs * d->max_blocks_per_seq);
     const int lpb = AKV_MOVE_OS_LAYERS > 0 ? AKV_MOVE_OS_LAYERS : (d->head_dim == 128 ? 1 : 2);
     const long long groups = (d->n_layers + lpb - 1) / lpb;
+    c->layer_groups = groups;
     long long cap = AKV_MOVE_ONESHOT_CAP;
     if (const char *e = getenv("AKV_MOVE_ONESHOT_CAP")) cap = std::max(0LL, atoll(e));
     c->oneshot_cap = (int)std::max(1LL, std::min<long long>(pages * groups, cap));
@@ -438,7 +451,8 @@ akv_status akv_fork(akv_cache *c, const int32_t *dst_of, const uint8_t *drop_mas
   if (drop_mask) mode |= akv::M_DROP;
   if (reposition) mode |= akv::M_REPOS;
   if (new_pos) mode |= akv::M_NEWPOS;
-  return run_compaction(c, drop_mask, new_pos, nullptr, mode, stream);
+  return run_compaction(c, drop_mask, new_pos, nullptr, mode, stream,
+                        (long long)n * c->desc.max_blocks_per_seq);
 }
 
 size_t akv_decode_workspace_bytes(const akv_cache *c, int32_t n_layers, int32_t n_q_heads) {

@@ -18,6 +18,7 @@ enum Ctl : int {
   CTL_DONE = 1,       // last-block ticket of the plan kernels
   CTL_OP_OK = 2,      // 1 when the planned op may commit
   CTL_NGROUPS = 3,    // sequence groups of the planned op (move + commit rounds that run)
+  CTL_NEXTRA = 4,     // shared pages the op released for the last time (pushed by the last round)
   CTL_MODE = 8,       // mode bits of the planned op
   CTL_COUNT = 64
 };
@@ -63,6 +64,10 @@ enum SeqInfo : int {
   SI_DST = 15,       // fork: destination sequence (-1 = none)
   SI_LSRC_ROW = 16,  // row of last_src holding this sequence's gather map (-1: none)
   SI_LSRC_LEN = 17,  // entries of that map
+  SI_NSHARED = 18,   // pages [0, NSHARED) of this sequence may be shared with other
+                     // sequences (kept across ops; pages at or past it are its own)
+  SI_N_SHREL = 19,   // the first N_SHREL released pages may be shared (reference-counted)
+  SI_SH_NEW = 20,    // SI_NSHARED after the planned op
   kSeqInfo = 24
 };
 
@@ -84,6 +89,8 @@ enum Mode : int {
   M_NEWPOS = 4,      // explicit new positions
   M_OLDPOS = 8,      // validate old positions
   M_FORK = 16,       // write a new position version into an empty sequence
+  M_STAGED = 32,     // one-sequence cache: the plan fills the fresh page ids into the
+                     // staging array and commits the op itself (no commit kernel)
 };
 
 // Device view of one cache, passed by value to every kernel.
@@ -92,6 +99,8 @@ struct Dev {
   int32_t *table, *lens, *next_pos, *pos, *tok, *free_stack, *free_count;
   int32_t *ctl, *seq_info, *src_map, *delta_map, *stage, *chunk_info, *fork_dst;
   int32_t *last_src;          // [B][S] gather map of the last drop / reposition / fork
+  int32_t *share;             // [NB] references to a page beyond the first (0: one holder)
+  int32_t *ex_list;           // [NB] shared pages an op released for the last time
   int32_t *groups;            // [kMaxOpGroups][kGroupRec] sequence groups of the planned op
   const double *theta;        // [RD/2] rotation frequencies
   const int32_t *window;      // [L] sliding-window length per layer, 0 = full attention
@@ -151,7 +160,7 @@ __device__ inline int first_pos_at_least(const Dev &d, const int32_t *trow, int 
 // Scratch layout (byte offsets from the scratch base, each 256-B aligned).
 struct ScratchLayout {
   size_t ctl, theta, seq_info, src_map, delta_map, stage, chunk_info, fork_dst, window, last_src,
-      groups, total;
+      groups, share, ex_list, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -174,6 +183,8 @@ inline ScratchLayout scratch_layout(int B, int S, int NB, int L) {
   s.window = o;    o = align256(o + size_t(L) * 4);
   s.last_src = o;  o = align256(o + size_t(B) * S * 4);
   s.groups = o;    o = align256(o + size_t(kMaxOpGroups) * kGroupRec * 4);
+  s.share = o;     o = align256(o + size_t(NB) * 4);
+  s.ex_list = o;   o = align256(o + size_t(NB) * 4);
   s.total = o;
   return s;
 }

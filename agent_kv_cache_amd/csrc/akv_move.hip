@@ -169,7 +169,10 @@ __device__ __forceinline__ void move_body(const Dev &d, int mode, int oneshot_ca
       const int b = lo;
       const int *si = d.seq_info + (size_t)b * kSeqInfo;
       const int po = (mv ? si[SI_FBD] : si[SI_FIP]) + (key - si[of]);
-      const int dst = mv ? d.free_stack[fc_old - 1 - pg] : d.table[(size_t)b * d.maxpg + po];
+      // fresh page: popped from the free stack (or, staged by the plan, read
+      // from the staging array); in place: the page itself
+      const int dst = !mv ? d.table[(size_t)b * d.maxpg + po]
+                      : (mode & M_STAGED) ? d.stage[moff + pg] : d.free_stack[fc_old - 1 - pg];
       const int j = po * kPage + t;
       const bool valid = j < si[SI_NEW_LEN];
       // physical source slot (page * 16 + row); in place: the slot itself
@@ -183,7 +186,7 @@ __device__ __forceinline__ void move_body(const Dev &d, int mode, int oneshot_ca
       if (t == 0) {
         s_dst = dst;
         s_mv = mv;
-        if (mv && l0 == 0) d.stage[moff + pg] = dst;
+        if (mv && l0 == 0 && !(mode & M_STAGED)) d.stage[moff + pg] = dst;
       }
       if (l0 == 0) {
         const size_t dn = (size_t)dst * kPage + t;

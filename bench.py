@@ -444,11 +444,18 @@ def restore_counts(rs):
         ln = int((m == 0).sum())
         pairs = n * (ln - n) + n * (n + 1) // 2          # (row, visible entry) pairs
         flops = 4 * pairs * sh.head_dim * sh.n_q_heads * sh.n_layers
-        # fork: every survivor's K and V read and written, its position and
-        # token id moved, the mask and positions read
-        fork_b = ln * (2 * row) * 2 + ln * 12 + len(m) + 4 * ln
+        # fork: the version shares the source's leading full pages before the
+        # first dropped entry (the source's positions are 0..n-1, so the
+        # canonical reposition changes nothing before it); every other
+        # survivor's K and V are read and written, its position and token id
+        # moved; the mask and the survivors' positions are read
+        f = int(np.flatnonzero(m)[0]) if m.any() else len(m)
+        shared = (min(f, ln) // 16) * 16
+        copied = ln - shared
+        fork_b = copied * (2 * row) * 2 + copied * 12 + len(m) + 4 * ln
         kv_b = ln * 2 * row
-        out.append(dict(len=ln, rows=n, pairs=pairs, flops=flops, fork_bytes=fork_b, kv_bytes=kv_b))
+        out.append(dict(len=ln, rows=n, pairs=pairs, flops=flops, fork_bytes=fork_b, kv_bytes=kv_b,
+                        shared=shared, copied=copied))
     return out
 
 
@@ -572,7 +579,8 @@ def run_restore(args):
     ms_step = (t1 - t0) * 1e3 / args.steps
     seg_ms = tot("segment")
     fork_ms = tot("plan") + tot("move") + tot("commit")
-    move_b = sum(c["len"] * 2 * (sh.n_layers * sh.n_kv_heads * sh.head_dim * 2) * 2 for c in cnt)
+    move_b = sum(c["copied"] * 2 * (sh.n_layers * sh.n_kv_heads * sh.head_dim * 2) * 2
+                 for c in cnt)
     seg_tf = flops / (seg_ms * 1e-3) / 1e12
     peak_tf = 2500.0
     traffic = counted_traffic("segment_fa_kernel_restore_llama8b_32k_counters.json")
@@ -589,6 +597,7 @@ def run_restore(args):
             "q_heads": sh.n_q_heads, "rope_base": sh.rope_base, "page_tokens": 16,
             "tokens": rs.n_tokens, "segments": nv, "query_rows": nq,
             "version_lens": [c["len"] for c in cnt], "segment_rows": rows,
+            "version_shared_entries": [c["shared"] for c in cnt],
             "parallelism": "single GPU",
         },
         "roofline": {

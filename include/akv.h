@@ -176,7 +176,9 @@ akv_status akv_append_rope(akv_cache *c, const int32_t *counts, int64_t n_new,
                            const int32_t *token_ids, void *stream);
 
 /* End of a request ([CE] sec. 3.1: the request's resident KV is released):
- * every sequence b with release[b] != 0 returns all its
+ * every sequence b with release[b] != 0 gives up all its pages (a page
+ * shared with a position version that survives stays with it; the others
+ * return to the free stack) and
  * pages to the device free stack and becomes empty with next_pos = 0, ready
  * for a new request (or as the destination of akv_fork).  release: DEVICE
  * uint8 [B].  A no-op while a device error is latched. */
@@ -216,12 +218,20 @@ akv_status akv_reposition(akv_cache *c, const int32_t *old_pos,
 akv_status akv_drop_reposition(akv_cache *c, const uint8_t *drop_mask,
                                const int32_t *new_pos, void *stream);
 
-/* New position versions ([CE] sec. 4.2.3, Appendix A.1.1): for every
- * source sequence b with dst_of[b] >= 0, the empty sequence dst_of[b]
+/* New position versions ([CE] sec. 4.2.3, Appendix A.1.1; [AKV] sec. 5.4:
+ * an existing version is reused, borrowed or allocated and copied): for
+ * every source sequence b with dst_of[b] >= 0, the empty sequence dst_of[b]
  * becomes a copy of b's active entries with drop_mask applied (optional)
  * and, if reposition != 0, its positions moved to new_pos (NULL = canonical
- * 0..r-1): K re-rotated, V and token ids copied into fresh pages.  The
- * source sequence is not modified (copy on transform).
+ * 0..r-1).  The source sequence is not modified (copy on transform).
+ * Pages: the version shares the source's leading full pages whose entries
+ * it leaves as they are (before the first dropped entry and the first
+ * changed position): those pages gain one reference each; the remaining
+ * survivors are written to fresh pages (K re-rotated, V and token ids
+ * copied).  A page returns to the free stack when its last holder drops or
+ * releases it; a reposition never turns a page another sequence holds in
+ * place, it rebuilds the sequence in fresh pages from the first changed page
+ * on (copy on write), so it may need free pages.
  *   dst_of    : HOST int32 [B]; -1 = no fork.  Host-checked: destinations
  *               in range, distinct, not equal to their source, and not
  *               themselves sources.  Read during the call only (the map is

@@ -1,0 +1,189 @@
+"""Position versions that share pages with their source (akv_fork): the
+version holds the source's leading full pages whose entries it leaves as they
+are (one more reference each) and copies the rest.  Against the oracle, whose
+versions are plain copies: the observable state must be the same.  After every
+step the pool is accounted for exactly: a page is either free (once, with no
+holder) or held, and its reference count equals the number of page-table
+entries pointing at it."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+from agent_kv_cache_amd import harness as Hn  # noqa: E402
+from agent_kv_cache_amd import workloads as W  # noqa: E402
+
+from gpu_util import (append_seeded, check_kv, check_meta, oracle_for, say,  # noqa: E402
+                      snapshot, same_state)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from agent_kv_cache_amd.binding import lib
+    lib()
+
+
+def _share_counts(cache):
+    """Reference counts the library keeps: the int32 per-page array in its
+    scratch (extra holders beyond the first)."""
+    import ctypes as C
+
+    from agent_kv_cache_amd import binding as Bd
+    # the layout is internal; recompute its offset the way the library does
+    # (256-B aligned regions in a fixed order) -- test-only introspection
+    B, S, NB, L = cache.B, cache.S, cache.NB, cache.L
+    al = lambda x: (x + 255) & ~255
+    o = 0
+    o = al(o + 64 * 4)                 # control words
+    o = al(o + 64 * 8)                 # frequencies
+    o = al(o + B * 24 * 4)             # per-sequence records
+    o = al(o + B * S * 4)              # gather map
+    o = al(o + B * S * 4)              # rotation deltas
+    o = al(o + NB * 4)                 # staging
+    o = al(o + B * ((S // 16 + 255) // 256) * 2 * 4)   # plan chunks
+    o = al(o + B * 4)                  # fork map
+    o = al(o + L * 4)                  # windows
+    o = al(o + B * S * 4)              # last_src
+    o = al(o + 64 * 16 * 4)            # groups
+    del C, Bd
+    return cache.scratch[o:o + NB * 4].view(torch.int32).cpu().numpy()
+
+
+def check_pool(cache):
+    """Every page free exactly once with no holder, or held by exactly
+    1 + share[p] page-table entries and not free."""
+    lens = cache.seq_lens.cpu().numpy()
+    tab = cache.block_table.cpu().numpy()
+    held = np.zeros(cache.NB, np.int64)
+    for b in range(cache.B):
+        pg = tab[b, :Hn.pages_for(int(lens[b]))]
+        assert (pg >= 0).all()
+        np.add.at(held, pg, 1)
+    fc = int(cache.free_count.item())
+    free = cache.free_stack[:fc].cpu().numpy()
+    assert len(np.unique(free)) == fc, "a page is on the free stack twice"
+    assert (held[free] == 0).all(), "a free page is still held"
+    share = _share_counts(cache)
+    hp = np.flatnonzero(held)
+    assert np.array_equal(held[hp], 1 + share[hp]), "reference counts differ from the tables"
+    assert fc + len(hp) == cache.NB, "pages lost"
+    return int(held.max()) if hp.size else 0
+
+
+SH = W.Shape(2, 2, 64, 4, 1.0e4)
+
+
+def _setup(lens, seed, extra=300, maxpg=80):
+    cache = Hn.make_cache(SH, lens, extra, max_blocks_per_seq=maxpg)
+    cache.reset(np.random.default_rng(seed).permutation(cache.NB).astype(np.int32))
+    Hn.fill(cache, SH, lens, seed, gen_device="cpu")
+    assert cache.sync_status() == 0
+    return cache, oracle_for(SH, lens, seed)
+
+
+def _fork(cache, oc, src, dst, mask=None, repos=False):
+    dst_of = [-1] * cache.B
+    dst_of[src] = dst
+    mm = None
+    if mask is not None:
+        rows = [None] * cache.B
+        rows[src] = mask
+        mm = Hn.mask_tensor(cache, rows)
+    before = snapshot(cache, src)
+    cache.fork(dst_of, mm, reposition=repos)
+    assert cache.sync_status() == 0
+    oc.fork(src, dst, mask, reposition=repos)
+    same_state(before, snapshot(cache, src))
+
+
+def _release(cache, oc, seqs):
+    sel = np.zeros(cache.B, np.uint8)
+    sel[list(seqs)] = 1
+    cache.release(torch.tensor(sel, device=cache.device))
+    assert cache.sync_status() == 0
+    for b in seqs:
+        oc.release(b)
+
+
+def test_fork_shares_the_unchanged_prefix_and_survives_its_source():
+    lens = [1000, 0, 0, 0]
+    cache, oc = _setup(lens, 71)
+    say("case fork: drop a span at 300, canonical positions -> 18 pages shared")
+    m = W.spans_to_mask(1000, [(300, 100)])
+    _fork(cache, oc, 0, 1, m, repos=True)
+    tab = cache.block_table.cpu().numpy()
+    assert np.array_equal(tab[1, :18], tab[0, :18])            # 300 // 16 pages shared
+    assert not np.isin(tab[1, 18:57], tab[0, :63]).any()        # the rest copied
+    assert check_pool(cache) == 2
+    check_meta(cache, oc)
+    check_kv(cache, oc, k_ulp=1)
+    say("case fork of the whole sequence: every full page shared, the partial last copied")
+    _fork(cache, oc, 0, 2)
+    tab = cache.block_table.cpu().numpy()
+    assert np.array_equal(tab[2, :62], tab[0, :62]) and tab[2, 62] != tab[0, 62]
+    assert check_pool(cache) == 3
+    say("case release the source; both versions keep their entries")
+    _release(cache, oc, [0])
+    check_pool(cache)
+    check_meta(cache, oc)
+    check_kv(cache, oc, k_ulp=1)
+    say("case append to a version (into its own partial page)")
+    append_seeded(cache, oc, SH, [0, 0, 37, 0], 7100, 1 << 20)
+    assert cache.sync_status() == 0
+    check_meta(cache, oc)
+    check_kv(cache, oc, k_ulp=1)
+    check_pool(cache)
+    say("case release every version in one call: every page free again")
+    _release(cache, oc, [1, 2])
+    assert check_pool(cache) == 0
+    assert int(cache.free_count.item()) == cache.NB
+
+
+def test_drop_and_copy_on_write_inside_a_shared_prefix():
+    lens = [900, 0, 0, 0]
+    cache, oc = _setup(lens, 72)
+    _fork(cache, oc, 0, 1)                        # all 56 full pages shared
+    _fork(cache, oc, 1, 2, W.spans_to_mask(900, [(700, 50)]))   # fork of a fork
+    assert check_pool(cache) == 3
+    say("case drop inside the shared prefix of the version")
+    rows = [None, W.spans_to_mask(900, [(100, 40), (500, 2)]), None, None]
+    cache.drop(Hn.mask_tensor(cache, rows))
+    assert cache.sync_status() == 0
+    oc.drop(1, rows[1])
+    check_pool(cache)
+    check_meta(cache, oc)
+    check_kv(cache, oc, k_ulp=0)
+    say("case reposition in place of pages other sequences hold (copy on write)")
+    src0 = snapshot(cache, 0)
+    src1 = snapshot(cache, 1)
+    # only sequence 2 moves (to 2i + 5); the others keep their own positions
+    pos_rows = [oc.seqs[b].pos.copy() for b in range(4)]
+    pos_rows[2] = np.arange(len(oc.seqs[2])) * 2 + 5
+    cache.reposition(None, Hn.pos_tensor(cache, pos_rows))
+    assert cache.sync_status() == 0
+    for b in range(4):
+        oc.reposition(b, pos_rows[b])
+    same_state(src0, snapshot(cache, 0))
+    same_state(src1, snapshot(cache, 1))
+    tab = cache.block_table.cpu().numpy()
+    assert not np.isin(tab[2, :Hn.pages_for(len(oc.seqs[2]))], tab[0, :57]).any()
+    check_pool(cache)
+    check_meta(cache, oc)
+    check_kv(cache, oc, k_ulp=1)
+    say("case drop + canonical reposition of the source while versions hold its prefix")
+    rows = [W.spans_to_mask(900, [(0, 3)]), None, None, None]
+    cache.drop_reposition(Hn.mask_tensor(cache, rows))
+    assert cache.sync_status() == 0
+    for b in range(4):
+        if len(oc.seqs[b]):
+            oc.drop_reposition(b, rows[b] if rows[b] is not None
+                               else np.zeros(len(oc.seqs[b]), np.uint8))
+    check_pool(cache)
+    check_meta(cache, oc)
+    check_kv(cache, oc, k_ulp=1)
+    _release(cache, oc, [0, 1, 2])
+    assert check_pool(cache) == 0 and int(cache.free_count.item()) == cache.NB

@@ -196,15 +196,20 @@ def test_fork_errors():
     with pytest.raises(AkvError):
         cache.fork([3, -1, -1, -1], None, reposition=False,
                    new_pos=Hn.pos_tensor(cache, [None] * 4))
-    # pool exhaustion: 8 spare pages, a copy of 30 entries needs 2, of 20 needs 2 ...
+    # pool exhaustion: 2 spare pages.  A plain copy of 60 entries shares its
+    # 3 full pages and copies 1 (fits); dropping the first entry leaves
+    # nothing to share, and 59 entries need 4 fresh pages (rejected)
     big = Hn.make_cache(sh, [60, 0], 2, max_blocks_per_seq=4)
     big.reset()
     Hn.fill(big, sh, [60, 0], 2, gen_device="cpu")
     b0 = _snapshot(big, 0)
-    big.fork([1, -1])
+    first = Hn.mask_tensor(big, [np.r_[1, np.zeros(59, np.uint8)].astype(np.uint8), None])
+    big.fork([1, -1], first)
     assert big.sync_status() == 4
     _same(b0, _snapshot(big, 0))
     assert int(big.seq_lens[1]) == 0
+    big.fork([1, -1])
+    assert big.sync_status() == 0 and int(big.seq_lens[1]) == 60
     for b in range(4):
         _same(before[b], _snapshot(cache, b))
     # the cache still works after the rejected calls
