@@ -74,7 +74,8 @@ __device__ __forceinline__ short f32_to_bf16_bits(float x) {
 template <int D>
 __global__ __launch_bounds__(kAttnWaves * 64, AKV_ATTN_MIN_WAVES) void attn_kernel(
     Dev d, const uint16_t *__restrict__ q, const int32_t *__restrict__ active_len, int l0,
-    int nL, int Hq, uint16_t *__restrict__ out, float *__restrict__ part, int nsplit) {
+    int nL, int Hq, uint16_t *__restrict__ out, float *__restrict__ part, int nsplit,
+    LayerOrder order) {
   constexpr int KC = D / 32;      // QK MFMA steps (K = 32 of d each)
   constexpr int NT = D / 16;      // PV output tiles of 16 dims
   constexpr int VC = D / 32;      // 16-B V chunks per lane per page
@@ -90,7 +91,19 @@ __global__ __launch_bounds__(kAttnWaves * 64, AKV_ATTN_MIN_WAVES) void attn_kern
   auto s_o = reinterpret_cast<float (*)[16][D]>(s_raw);
 
   const int s = blockIdx.x, g = blockIdx.y, bl = blockIdx.z;
-  const int b = bl / nL, li = bl - b * nL, l = l0 + li;
+  // With sliding-window layers the grid's layer axis runs over the ordered
+  // layers (full attention first) with the sequences fastest, so the long
+  // rows are dispatched first and spread over the CUs instead of pairing up
+  // on the same CUs as full and window layers alternate.
+  int b, li;
+  if (order.n) {
+    b = bl % d.B;
+    li = order.idx[bl / d.B];
+  } else {
+    b = bl / nL;
+    li = bl - b * nL;
+  }
+  const int l = l0 + li;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int hh = lane & 15, kg = lane >> 4;
   const int G = Hq / d.H;
@@ -294,14 +307,14 @@ __global__ __launch_bounds__(D) void combine_kernel(const float *__restrict__ pa
 
 hipError_t launch_attention(const Dev &d, const uint16_t *q, const int32_t *active_len, int l0,
                             int nL, int Hq, uint16_t *out, float *part, int nsplit,
-                            hipStream_t st) {
+                            const LayerOrder &order, hipStream_t st) {
   const dim3 grid(nsplit, d.H, d.B * nL), block(kAttnWaves * 64);
   if (d.D == 128)
     hipLaunchKernelGGL(attn_kernel<128>, grid, block, 0, st, d, q, active_len, l0, nL, Hq, out,
-                       part, nsplit);
+                       part, nsplit, order);
   else
     hipLaunchKernelGGL(attn_kernel<64>, grid, block, 0, st, d, q, active_len, l0, nL, Hq, out,
-                       part, nsplit);
+                       part, nsplit, order);
   return hipGetLastError();
 }
 

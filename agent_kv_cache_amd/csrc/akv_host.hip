@@ -64,6 +64,7 @@ struct akv_cache {
   int op_groups = 1;       // (move, commit) rounds of a drop / reposition (1: the pool always fits)
   int n_full_layers = 0;   // layers without a sliding window
   void *noalloc_ws = nullptr;   // this device's copy of `scratch`
+  std::vector<int32_t> window;  // per-layer sliding window (host copy)
   bool profile = false;
   struct Rec {
     int kernel;
@@ -123,6 +124,10 @@ bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 // workgroups is fullest (ties: fewer splits, less combine work).  Each split's
 // page range is then cut on the device from the actual length.
 int nsplit_for(const akv_cache *c, int nL) {
+#ifdef AKV_DECODE_NSPLIT
+  // launch-shape knob: a fixed split count (sweeps)
+  return std::max(1, std::min(AKV_DECODE_NSPLIT, std::max(1, c->desc.max_blocks_per_seq / 4)));
+#endif
   // Rows that carry the work: with sliding-window layers the full-attention
   // layers dominate (a window row reads at most W entries), so the split
   // count is sized for their share of the layers.
@@ -317,6 +322,7 @@ akv_status akv_cache_init(const akv_cache_desc *d, akv_cache **out) {
     theta[i] = d->inv_freq ? d->inv_freq[i] : pow(d->rope_base, -2.0 * (double)i / (double)rd);
   std::vector<int32_t> win(d->n_layers, 0);
   if (d->layer_window) std::copy(d->layer_window, d->layer_window + d->n_layers, win.begin());
+  c->window = win;
   if (hipMemcpy(sb + c->layout.theta, theta, sizeof(theta), hipMemcpyHostToDevice) != hipSuccess ||
       hipMemcpy(sb + c->layout.window, win.data(), sizeof(int32_t) * win.size(),
                 hipMemcpyHostToDevice) != hipSuccess) {
@@ -487,10 +493,25 @@ static akv_status decode_impl(akv_cache *c, const uint16_t *q, const int32_t *ac
     }
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  // full-attention layers first along the grid when the call mixes them
+  // with sliding-window layers (natural order otherwise)
+  akv::LayerOrder order;
+  order.n = 0;
+  if (n_layers <= akv::kMaxOrderedLayers) {
+    int nfull = 0, nwin = 0;
+    for (int li = 0; li < n_layers; ++li) (c->window[layer_begin + li] ? nwin : nfull) += 1;
+    if (nwin && nfull) {
+      int k = 0;
+      for (int pass = 0; pass < 2; ++pass)
+        for (int li = 0; li < n_layers; ++li)
+          if ((c->window[layer_begin + li] != 0) == (pass == 1)) order.idx[k++] = (int16_t)li;
+      order.n = n_layers;
+    }
+  }
   {
     Timed tm(c, AKV_KERNEL_ATTN, st);
     AKV_HIP(akv::launch_attention(c->dev, q, active_len, layer_begin, n_layers, n_q_heads, out,
-                                  static_cast<float *>(workspace), ns, st));
+                                  static_cast<float *>(workspace), ns, order, st));
   }
   if (ns > 1) {
     Timed tm(c, AKV_KERNEL_COMBINE, st);

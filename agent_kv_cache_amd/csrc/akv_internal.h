@@ -206,9 +206,16 @@ hipError_t launch_release(const Dev &d, const uint8_t *sel, hipStream_t st);
 hipError_t launch_query(const Dev &d, int32_t *lens, int32_t *next, int32_t *pos, int32_t *tok,
                         int32_t *last_src, hipStream_t st);
 hipError_t launch_reset(const Dev &d, const int32_t *order_dev, hipStream_t st);
+// Order of a decode call's layers along the grid when some have a sliding
+// window: full-attention layers first (passed in kernel arguments).
+constexpr int kMaxOrderedLayers = 512;
+struct LayerOrder {
+  int n;                          // 0: natural order (sequence-major, layers fastest)
+  int16_t idx[kMaxOrderedLayers]; // layer offsets within the call, full-attention first
+};
 hipError_t launch_attention(const Dev &d, const uint16_t *q, const int32_t *active_len,
                             int l0, int nL, int Hq, uint16_t *out, float *part,
-                            int nsplit, hipStream_t st);
+                            int nsplit, const LayerOrder &order, hipStream_t st);
 int attn_blocks_per_cu(int D);
 hipError_t launch_combine(const float *part, uint16_t *out, int rows, int nsplit,
                           int D, hipStream_t st);
