@@ -77,9 +77,12 @@ enum SeqInfo : int {
 #ifndef AKV_MOVE_ONESHOT_CAP
 #define AKV_MOVE_ONESHOT_CAP 131072
 #endif
-// Layers per one-shot block (0: 1 at head_dim 128, 2 at 64).
+// Layers per one-shot block (0: 1 at head_dim 128, 2 at 64).  One layer at
+// both sizes: at d = 64 a block then moves 32 KiB instead of 64, and the
+// launch's tail is shorter (50-turn history, three alternating process pairs
+// on one box: move 10.01-10.04 -> 9.91-9.94 ms).
 #ifndef AKV_MOVE_OS_LAYERS
-#define AKV_MOVE_OS_LAYERS 0
+#define AKV_MOVE_OS_LAYERS 1
 #endif
 
 // Mode bits of the compaction plan.

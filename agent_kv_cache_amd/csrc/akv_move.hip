@@ -12,7 +12,7 @@
 //
 // Two launch shapes, chosen on the device from the planned unit count:
 //  * one-shot (ops of up to 131072 blocks): one block per page and layer
-//    group (one layer at d = 128, two at d = 64) in layer-major order.
+//    group (one layer) in layer-major order.
 //    Blocks are dispatched in index order, so the blocks in flight read and
 //    write a compact, sliding address range; on MI355X this streams ~15%
 //    faster than a persistent grid whose workgroups each walk their own
