@@ -206,11 +206,26 @@ __global__ __launch_bounds__(kChunkPages) void plan_kernel(
     if (fpos != INT_MAX) atomicMin(&si[SI_FPOS], fpos);
   }
   // ---- last workgroup: finalize every sequence, prefix sums, pool check ----
+  // Two-level ticket: chunks past a sequence's pages have nothing to report
+  // and leave at once; the chunks of a sequence count on its own ticket, and
+  // the last of them takes the one global ticket for the sequence, so the
+  // global counter sees B increments instead of one per workgroup (1024 on
+  // the 64-sequence batch, where contention on it cost ~100 us).
   if (gridDim.x * gridDim.y > 1) {
+    const int nch_b = max(1, (P + kChunkPages - 1) / kChunkPages);
+    if (c >= nch_b) return;
     __threadfence();
     __syncthreads();
-    if (t == 0)
-      s_last = (atomicAdd(&d.ctl[CTL_DONE], 1) == (int)(gridDim.x * gridDim.y) - 1);
+    if (t == 0) {
+      bool seq_done = true;
+      if (nch_b > 1) {
+        int *tk = &d.seq_info[(size_t)b * kSeqInfo + SI_TICKET];
+        seq_done = atomicAdd(tk, 1) == nch_b - 1;
+        if (seq_done) *tk = 0;          // re-armed for the next op
+        __threadfence();                // the sequence's chunks before the global ticket
+      }
+      s_last = seq_done && atomicAdd(&d.ctl[CTL_DONE], 1) == (int)gridDim.y - 1;
+    }
     __syncthreads();
     if (!s_last) return;
     __threadfence();
@@ -884,6 +899,7 @@ __global__ void reset_kernel(Dev d, const int32_t *order) {
     d.seq_info[i * kSeqInfo + SI_LSRC_ROW] = -1;     // no gather map yet
     d.seq_info[i * kSeqInfo + SI_LSRC_LEN] = 0;
     d.seq_info[i * kSeqInfo + SI_NSHARED] = 0;      // nothing shared
+    d.seq_info[i * kSeqInfo + SI_TICKET] = 0;
   }
   if (i < d.NB) {
     d.free_stack[d.NB - 1 - i] = order ? order[i] : (int)i;

@@ -68,6 +68,7 @@ enum SeqInfo : int {
                      // sequences (kept across ops; pages at or past it are its own)
   SI_N_SHREL = 19,   // the first N_SHREL released pages may be shared (reference-counted)
   SI_SH_NEW = 20,    // SI_NSHARED after the planned op
+  SI_TICKET = 21,    // plan chunks of this sequence done (re-armed to 0 by the last)
   kSeqInfo = 24
 };
 

@@ -402,7 +402,7 @@ def run_history(args):
                      "launch_bytes_note": "per-op launches of different sizes: achieved = "
                                           "moved bytes of all ops / move kernel time of all ops"},
         "ops": n_ops, "ops_ms_total": round(tot_ms, 4), "ops_bytes_total": int(tot_bytes),
-        "move_ms_total": round(mv_ms, 4),
+        "move_ms_total": round(mv_ms, 4), "move_bytes_total": int(mv_bytes),
         "drop_reposition_gbps": round(tot_bytes / (tot_ms * 1e-3) / 1e9, 1),
         "drop_reposition_frac_of_peak": round(tot_bytes / (tot_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
         "decode_ms": round(att_ms, 4), "decode_bytes": b_att,
