@@ -112,6 +112,50 @@ def oracle_from_device(cache, b: int, layers, rope_base: float, **kw) -> O.Oracl
     return oc
 
 
+def share_counts(cache):
+    """Reference counts the library keeps: the int32 per-page array in its
+    scratch (extra holders beyond the first)."""
+    import torch
+    # the layout is internal; recompute its offset the way the library does
+    # (256-B aligned regions in a fixed order) -- test-only introspection
+    B, S, NB, L = cache.B, cache.S, cache.NB, cache.L
+    al = lambda x: (x + 255) & ~255
+    o = 0
+    o = al(o + 64 * 4)                 # control words
+    o = al(o + 64 * 8)                 # frequencies
+    o = al(o + B * 24 * 4)             # per-sequence records
+    o = al(o + B * S * 4)              # gather map
+    o = al(o + B * S * 4)              # rotation deltas
+    o = al(o + NB * 4)                 # staging
+    o = al(o + B * ((S // 16 + 255) // 256) * 2 * 4)   # plan chunks
+    o = al(o + B * 4)                  # fork map
+    o = al(o + L * 4)                  # windows
+    o = al(o + B * S * 4)              # last_src
+    o = al(o + 64 * 16 * 4)            # groups
+    return cache.scratch[o:o + NB * 4].view(torch.int32).cpu().numpy()
+
+
+def check_pool(cache):
+    """Every page free exactly once with no holder, or held by exactly
+    1 + share[p] page-table entries and not free."""
+    lens = cache.seq_lens.cpu().numpy()
+    tab = cache.block_table.cpu().numpy()
+    held = np.zeros(cache.NB, np.int64)
+    for b in range(cache.B):
+        pg = tab[b, :Hn.pages_for(int(lens[b]))]
+        assert (pg >= 0).all()
+        np.add.at(held, pg, 1)
+    fc = int(cache.free_count.item())
+    free = cache.free_stack[:fc].cpu().numpy()
+    assert len(np.unique(free)) == fc, "a page is on the free stack twice"
+    assert (held[free] == 0).all(), "a free page is still held"
+    share = share_counts(cache)
+    hp = np.flatnonzero(held)
+    assert np.array_equal(held[hp], 1 + share[hp]), "reference counts differ from the tables"
+    assert fc + len(hp) == cache.NB, "pages lost"
+    return int(held.max()) if hp.size else 0
+
+
 def q_tensor(shape: Shape, B: int, n_layers: int, seed: int, device="cpu"):
     return randn_bf16((B, n_layers, shape.n_q_heads, shape.head_dim), seed, device=device)
 
