@@ -391,10 +391,12 @@ __global__ __launch_bounds__(kChunkPages) void plan_kernel(
       if (!latched) d.ctl[CTL_ERR] = e;
       d.ctl[CTL_OP_OK] = 0;
       d.ctl[CTL_NGROUPS] = 0;
+      d.ctl[CTL_NPG0] = 0;
     } else {
       d.ctl[CTL_OP_OK] = 1;
       d.ctl[CTL_NGROUPS] = ng;
       d.ctl[CTL_MODE] = mode;
+      d.ctl[CTL_NPG0] = d.groups[GR_TM] + d.groups[GR_TI];
     }
     d.ctl[CTL_DONE] = 0;
     s_ok = !(e || latched);

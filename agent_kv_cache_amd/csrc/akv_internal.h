@@ -19,6 +19,7 @@ enum Ctl : int {
   CTL_OP_OK = 2,      // 1 when the planned op may commit
   CTL_NGROUPS = 3,    // sequence groups of the planned op (move + commit rounds that run)
   CTL_NEXTRA = 4,     // shared pages the op released for the last time (pushed by the last round)
+  CTL_NPG0 = 5,       // pages group 0 of the planned op rebuilds (0: nothing to move)
   CTL_MODE = 8,       // mode bits of the planned op
   CTL_COUNT = 64
 };

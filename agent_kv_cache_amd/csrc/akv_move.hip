@@ -46,6 +46,9 @@ namespace akv {
 #ifndef AKV_MOVE_FR_NT
 #define AKV_MOVE_FR_NT 1       // nontemporal hint with the full-row mapping
 #endif
+#ifndef AKV_MOVE_FR_ITEMS
+#define AKV_MOVE_FR_ITEMS 4    // full-row mapping: (plane, slice) items loaded before any store
+#endif
 
 constexpr int kMoveThreads = 256;
 
@@ -91,15 +94,26 @@ __device__ __forceinline__ void move_body(const Dev &d, int mode, int oneshot_ca
   constexpr int CPR = FR ? 2 * CH : CH;  // threads per row
   constexpr int TPH = kPage * CPR;       // threads per (layer, head) slice
   constexpr int NS = kMoveThreads / TPH; // slices per pass
-  // slices loaded before any store (a full-row thread holds half the bytes
-  // of a half-row thread per slice, so it takes twice as many)
-  constexpr int U = FR ? 2 * AKV_MOVE_UNROLL : AKV_MOVE_UNROLL;
+  // (plane, slice) items loaded before any store (a full-row thread holds
+  // half the bytes of a half-row thread per item, so it takes more)
+  constexpr int U = FR ? AKV_MOVE_FR_ITEMS : AKV_MOVE_UNROLL;
   __shared__ int s_dst, s_mv;
   __shared__ int s_src[kPage], s_valid[kPage], s_delta[kPage], s_rep[kPage];
   __shared__ int s_repval[kPage], s_nrep;
   __shared__ double2 s_cs[kPage][HALF];
 
-  if (d.ctl[CTL_OP_OK] == 0 || group >= d.ctl[CTL_NGROUPS]) return;
+  constexpr int LPB = AKV_MOVE_OS_LAYERS > 0 ? AKV_MOVE_OS_LAYERS : (D == 128 ? 1 : 2);
+  const long long ngroups = (d.L + LPB - 1) / LPB;
+  if (group == 0) {
+    // One load decides for the blocks with nothing to do (an op's one-shot
+    // grid is sized for the largest op the cache can plan, so most of its
+    // blocks usually leave here): the pages of group 0, 0 when nothing moves.
+    const long long np0 = d.ctl[CTL_NPG0];
+    if (np0 == 0 || (np0 * ngroups <= oneshot_cap) != ONESHOT) return;
+    if (ONESHOT && blockIdx.x >= np0 * ngroups) return;
+  } else if (group >= d.ctl[CTL_NGROUPS]) {
+    return;
+  }
   // this round's group of sequences: its moved pages take the fresh pages
   // below the group's free count, its rebuilt pages are numbered from 0
   const int *gr = d.groups + (size_t)group * kGroupRec;
@@ -116,8 +130,6 @@ __device__ __forceinline__ void move_body(const Dev &d, int mode, int oneshot_ca
   // LPB consecutive layers (64 KiB of K+V read per block at the Llama-8B
   // shape, whatever the head size; blocks per (page, layer, plane) or per
   // head group were measured slower: each repeats the per-page set-up).
-  constexpr int LPB = AKV_MOVE_OS_LAYERS > 0 ? AKV_MOVE_OS_LAYERS : (D == 128 ? 1 : 2);
-  const long long ngroups = (d.L + LPB - 1) / LPB;
   const long long os_blocks = npages * ngroups;
   if ((os_blocks <= oneshot_cap) != ONESHOT) return;
   long long u0, u1;
@@ -223,31 +235,34 @@ __device__ __forceinline__ void move_body(const Dev &d, int mode, int oneshot_ca
     const int sp = s_src[r];
     const size_t src_row = (size_t)(sp >> 4) * ps.page + (size_t)(sp & 15) * D + xo;
     const size_t dst_row = (size_t)dst * ps.page + (size_t)r * D + xo;
-    // Batches of U slices; K slices of the unit range first, then V slices
-    // (each pass streams one pool).  The first batch is loaded before the
-    // cos/sin set-up so that its latency covers the set-up.
-    int plane = 0, i0 = slot;
-    bool more = do_k && plane < pend && i0 < nsl;
+    // Items: the (plane, slice) pairs of the unit range, K slices first,
+    // then V slices, taken in batches of U per thread (a batch may hold both
+    // planes).  The first batch is loaded before the cos/sin set-up so that
+    // its latency covers the set-up.
+    const int nit = do_k ? pend * nsl : 0;
+    int i0 = slot;
     u32x4 lo[U], hi[U];
     size_t dofs[U];
-    bool on[U];
+    bool on[U], kp[U];
     auto issue = [&]() {
-      uint16_t *pool = plane ? d.v : d.k;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int idx = i0 + u * NS;
-        on[u] = idx < nsl;
-        const int l = l0 + idx / d.H, h = idx % d.H;
+        on[u] = idx < nit;
+        kp[u] = idx < nsl;
+        const int sl = kp[u] ? idx : idx - nsl;
+        const int l = l0 + sl / d.H, h = sl % d.H;
         const size_t off = (size_t)l * lstride + (size_t)h * hstride;
         dofs[u] = dst_row + off;
         lo[u] = hi[u] = u32x4{0u, 0u, 0u, 0u};
         if (on[u] && valid) {
+          const uint16_t *pool = kp[u] ? d.k : d.v;
           lo[u] = ld_stream<NT>(pool + src_row + off);
           if constexpr (!FR) hi[u] = ld_stream<NT>(pool + src_row + off + yoff);
         }
       }
     };
-    if (more) issue();
+    if (i0 < nit) issue();
     if (rot_any) {
       const int RH = d.RD / 2;
       const int ntask = s_nrep * RH;
@@ -263,12 +278,12 @@ __device__ __forceinline__ void move_body(const Dev &d, int mode, int oneshot_ca
     // cos/sin of this thread's 8 pairs stay in LDS and are read per use
     const double2 *cs_row = &s_cs[(rot_any && delta != 0) ? s_rep[r] : 0]
                                  [!rot_chunk ? 0 : x_chunk ? 8 * pc : 8 * (pc - rch)];
-    while (more) {
-      uint16_t *pool = plane ? d.v : d.k;
-      const bool rot_plane = plane == 0 && turn;
+    while (i0 < nit) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (!on[u]) continue;
+        uint16_t *pool = kp[u] ? d.k : d.v;
+        const bool rot_plane = kp[u] && turn;
         if constexpr (FR) {
           if (rot_plane) {
             // both lanes of a pair hold the same row, so they turn together
@@ -286,12 +301,7 @@ __device__ __forceinline__ void move_body(const Dev &d, int mode, int oneshot_ca
         }
       }
       i0 += NS * U;
-      if (i0 >= nsl) {
-        ++plane;
-        i0 = slot;
-      }
-      more = plane < pend && i0 < nsl;
-      if (more) issue();
+      if (i0 < nit) issue();
     }
   }
 }
