@@ -215,19 +215,25 @@ __global__ __launch_bounds__(kSegWaves * 64, 2) void segment_attn_kernel(
 // of them (two MFMA column tiles) and keeps their Q fragments, exponent
 // references, weight sums and O^T accumulators in registers.  The workgroup sweeps the
 // causal KV range in 64-token tiles staged in LDS (K as rows, V transposed)
-// and double-buffered: the next tile's global loads are in flight while the
-// current one is multiplied, so every KV byte is fetched once per workgroup
-// and reused by 256 columns.
+// (K double-buffered, V triple-buffered): the next tile's global loads are in
+// flight while the current one is multiplied, so every KV byte is fetched
+// once per workgroup and reused by 256 columns.
 //   S^T tile (16 tokens x 16 columns) = K (16 x 32 dims) * Q^T, 16x16x32 MFMA.
 //   O^T (16 dims x 16 columns) += V^T (16 dims x 32 tokens) * P^T: the 32
 //   tokens of one MFMA step are ordered so that a lane's 8 k-values are the
 //   4 + 4 probabilities it already holds from two S^T tiles.
 //   Each column's weight sum is one more MFMA (a ones operand times P^T).
-// On this GPU the matrix core and the vector ALU of a SIMD hardly overlap,
-// so the tile time is the MFMA time plus the VALU time: the loop keeps VALU
-// work to the softmax itself (per-thread load offsets fixed before the
-// sweep, zeroing only on the tile where the sequence ends, a reference that
-// moves lazily, cross-row maxima with the row-swap instructions).
+// Per tile a wave's MFMA time and its softmax VALU time (half of it the
+// quarter-rate exponentials) are about equal, and a wave's QK -> softmax ->
+// PV chain is serial; the waves of a SIMD also run in step (one barrier per
+// tile).  So a tile's PV product is taken one iteration late, in the same
+// basic block as the next tile's exponentials: the two are independent, and
+// the matrix core multiplies while the VALU exponentiates.  The accumulation
+// order is unchanged (a moved reference scales the sum that includes the
+// previous tile, then the next tile is added).  The loop keeps other VALU
+// work small (per-thread load offsets fixed before the sweep, zeroing only
+// on the tile where the sequence ends, a reference that moves lazily,
+// cross-row maxima with the row-swap instructions).
 // ---------------------------------------------------------------------------
 #ifndef AKV_FA_VPAD
 #define AKV_FA_VPAD 4      // halfwords of padding per transposed-V row in LDS
@@ -235,7 +241,13 @@ __global__ __launch_bounds__(kSegWaves * 64, 2) void segment_attn_kernel(
 #ifndef AKV_FA_KPAD
 #define AKV_FA_KPAD 8      // halfwords of padding per K row in LDS (keeps 16-B alignment)
 #endif
-constexpr int kFaWaves = 8, kFaKT = 64, kFaCols = 256;
+#ifndef AKV_FA_WAVES
+#define AKV_FA_WAVES 8     // waves per workgroup (32 columns each)
+#endif
+#ifndef AKV_FA_MIN_WAVES
+#define AKV_FA_MIN_WAVES 1 // waves per SIMD the register budget must allow
+#endif
+constexpr int kFaWaves = AKV_FA_WAVES, kFaKT = 64, kFaCols = 32 * kFaWaves;
 #ifndef AKV_FA_TAU
 #define AKV_FA_TAU 8.0f    // log2 of the largest weight allowed before a column's reference moves
 #endif
@@ -280,7 +292,7 @@ __device__ __forceinline__ float fa_rows_max(float x) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kFaWaves * 64, 1) void segment_fa_kernel(
+__global__ __launch_bounds__(kFaWaves * 64, AKV_FA_MIN_WAVES) void segment_fa_kernel(
     Dev d, const uint16_t *__restrict__ q, const int32_t *__restrict__ seg_seq,
     const int32_t *__restrict__ seg_q_off, int max_q, int l0, int nL, int Hq,
     uint16_t *__restrict__ out) {
@@ -292,7 +304,7 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void segment_fa_kernel(
   constexpr int VPT = (VPAIRS + NTH - 1) / NTH;
   static_assert(KPT * NTH == kFaKT * C8, "K tile must split evenly");
   __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kFaKT][KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][D][VROW];
+  __shared__ __attribute__((aligned(16))) uint16_t s_vt[3][D][VROW];
   __shared__ __attribute__((aligned(16))) int32_t s_pos[2][kFaKT];   // sliding-window layers only
 
   const int G = Hq / d.H;
@@ -449,7 +461,7 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void segment_fa_kernel(
   };
   // registers -> LDS (V transposed); rows past the end of the sequence
   // become zeros here, which only the tile holding its end needs
-  auto lstore = [&](int t, int buf) {
+  auto lstore = [&](int t, int buf, int vbuf) {
     const int T0 = t * kFaKT;
     if (W > 0 && tid < kFaKT) s_pos[buf][tid] = rpos;
     if (T0 + kFaKT > len) {
@@ -474,9 +486,9 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void segment_fa_kernel(
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           // dims 8ch+2w (low halves) and 8ch+2w+1 (high halves) of rows 2a, 2a+1
-          *reinterpret_cast<uint32_t *>(&s_vt[buf][8 * ch + 2 * w][2 * a]) =
+          *reinterpret_cast<uint32_t *>(&s_vt[vbuf][8 * ch + 2 * w][2 * a]) =
               __builtin_amdgcn_perm(x1[w], x0[w], 0x05040100u);
-          *reinterpret_cast<uint32_t *>(&s_vt[buf][8 * ch + 2 * w + 1][2 * a]) =
+          *reinterpret_cast<uint32_t *>(&s_vt[vbuf][8 * ch + 2 * w + 1][2 * a]) =
               __builtin_amdgcn_perm(x1[w], x0[w], 0x07060302u);
         }
       }
@@ -487,14 +499,59 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void segment_fa_kernel(
     pidx(t0);
     gload(t0);
     if (t0 + 1 < ntile) pidx(t0 + 1);
-    lstore(t0, 0);
+    lstore(t0, 0, 0);
   }
+  // V buffer 2 holds zeros for the first tile's (empty) pending product
+  for (int e = tid; e < D * VROW / 8; e += NTH)
+    reinterpret_cast<uint4 *>(&s_vt[2][0][0])[e] = make_uint4(0u, 0u, 0u, 0u);
   // Q and the first tile are in registers / LDS before the loop: no wait on
   // the loop's own prefetches inside it
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  // O^T += V^T P^T and the weight sums for one tile's probabilities
+  auto pv_tile = [&](const bf16x8s (&p)[2][2], int vbuf) {
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+        lacc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, p[ct][kc], lacc[ct], 0, 0, 0);
+#pragma unroll
+    for (int dt = 0; dt < NT; ++dt)
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        const uint2 lo = *reinterpret_cast<const uint2 *>(&s_vt[vbuf][16 * dt + cl][32 * kc + 4 * kg]);
+        const uint2 hi = *reinterpret_cast<const uint2 *>(&s_vt[vbuf][16 * dt + cl][32 * kc + 16 + 4 * kg]);
+        const bf16x8s vf = __builtin_bit_cast(bf16x8s, make_uint4(lo.x, lo.y, hi.x, hi.y));
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+          acc[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, p[ct][kc], acc[ct][dt], 0, 0, 0);
+      }
+  };
+  // the weights of one tile as bf16 MFMA operands: a lane's 8 k-values are
+  // its 4 + 4 exponentials of two S^T tiles
+  bf16x8s pb[2][2], pbp[2][2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) pbp[ct][kc] = __builtin_bit_cast(bf16x8s, make_uint4(0u, 0u, 0u, 0u));
+  auto weights = [&](const floatx4s (&sa)[2][4]) {
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        const floatx4s &a0 = sa[ct][2 * kc], &a1 = sa[ct][2 * kc + 1];
+        pb[ct][kc] = bf16x8s{(__bf16)seg_exp2(a0[0]), (__bf16)seg_exp2(a0[1]), (__bf16)seg_exp2(a0[2]),
+                             (__bf16)seg_exp2(a0[3]), (__bf16)seg_exp2(a1[0]), (__bf16)seg_exp2(a1[1]),
+                             (__bf16)seg_exp2(a1[2]), (__bf16)seg_exp2(a1[3])};
+      }
+  };
+  // V buffer of the tile whose PV product is pending (-1: none).  A wave's
+  // first visible tile is the sweep's first tile, and its pending product is
+  // zero weights times the zeroed buffer 2; once a wave is past its last
+  // visible entry it stays past it.
+  int vprev = 2;
   for (int t = t0; t < ntile; ++t) {
-    const int buf = (t - t0) & 1;
+    const int buf = (t - t0) & 1, vbuf = (t - t0) % 3;
     if (t + 1 < ntile) gload(t + 1);
     if (t + 2 < ntile) pidx(t + 2);
     const int T0 = t * kFaKT;
@@ -516,8 +573,6 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void segment_fa_kernel(
         }
       }
       const bool diag = T0 + kFaKT - 1 > wave_lo;            // wave-uniform
-      float mx[2];
-      bool up[2];
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
         if (diag) {
@@ -539,25 +594,68 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void segment_fa_kernel(
               if (pj4[j] < wlo[ct]) sacc[ct][tt][j] = -INFINITY;
           }
         }
-        // exponents against the current reference, and their column maximum
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) sacc[ct][tt][j] = fmaf(sacc[ct][tt][j], scale, nref[ct]);
-        // this lane's maximum (a quarter of the column)
-        const float m0 = fmaxf(fmaxf(sacc[ct][0][0], sacc[ct][0][1]), fmaxf(sacc[ct][0][2], sacc[ct][0][3]));
-        const float m1 = fmaxf(fmaxf(sacc[ct][1][0], sacc[ct][1][1]), fmaxf(sacc[ct][1][2], sacc[ct][1][3]));
-        const float m2 = fmaxf(fmaxf(sacc[ct][2][0], sacc[ct][2][1]), fmaxf(sacc[ct][2][2], sacc[ct][2][3]));
-        const float m3 = fmaxf(fmaxf(sacc[ct][3][0], sacc[ct][3][1]), fmaxf(sacc[ct][3][2], sacc[ct][3][3]));
-        mx[ct] = fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
-        up[ct] = mx[ct] > thr[ct];
       }
+      // The previous tile's PV product and this tile's exponents against the
+      // current reference, their column maxima and weights, written out in
+      // 16 chunks whose order the compiler keeps (scheduling barriers): each
+      // chunk issues the V fragment reads two PV steps ahead, one PV step
+      // (two MFMAs; the first four chunks also one weight-sum MFMA) and two
+      // softmax elements, so the VALU works while the matrix core multiplies.
+      float mx[2] = {-INFINITY, -INFINITY};
+      bool up[2];
+      {
+        uint2 vlo[2 * NT], vhi[2 * NT];
+        auto vread = [&](int k) {
+          const int dt = k >> 1, kc = k & 1;
+          vlo[k] = *reinterpret_cast<const uint2 *>(&s_vt[vprev][16 * dt + cl][32 * kc + 4 * kg]);
+          vhi[k] = *reinterpret_cast<const uint2 *>(&s_vt[vprev][16 * dt + cl][32 * kc + 16 + 4 * kg]);
+        };
+        float ex[2][4][4];
+        vread(0);
+        vread(1);
+        // softmax element e = 2k, 2k + 1 of 32 per lane goes with PV step k
+        // (the 16 of D = 64 take two elements' pairs per step)
+        constexpr int EPS = 32 / (2 * NT);
+#pragma unroll
+        for (int k = 0; k < 2 * NT; ++k) {
+          __builtin_amdgcn_sched_barrier(0);
+          if (k + 2 < 2 * NT) vread(k + 2);
+          if (k < 4) lacc[k >> 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pbp[k >> 1][k & 1], lacc[k >> 1], 0, 0, 0);
+          const int dt = k >> 1, kc = k & 1;
+          const bf16x8s vf = __builtin_bit_cast(bf16x8s, make_uint4(vlo[k].x, vlo[k].y, vhi[k].x, vhi[k].y));
+          acc[0][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pbp[0][kc], acc[0][dt], 0, 0, 0);
+          acc[1][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pbp[1][kc], acc[1][dt], 0, 0, 0);
+#pragma unroll
+          for (int u = 0; u < EPS; ++u) {
+            const int e = EPS * k + u, ct = e >> 4, tt = (e & 15) >> 2, j = e & 3;
+            const float v = fmaf(sacc[ct][tt][j], scale, nref[ct]);
+            sacc[ct][tt][j] = v;
+            mx[ct] = fmaxf(mx[ct], v);
+            ex[ct][tt][j] = seg_exp2(v);
+            if ((e & 7) == 7) {
+              // the 8 weights of operand pb[ct][kc2]: S^T tiles 2 kc2 and 2 kc2 + 1
+              const int kc2 = (e & 15) >> 3;
+              const float *a0 = ex[ct][2 * kc2], *a1 = ex[ct][2 * kc2 + 1];
+              pb[ct][kc2] = bf16x8s{(__bf16)a0[0], (__bf16)a0[1], (__bf16)a0[2], (__bf16)a0[3],
+                                    (__bf16)a1[0], (__bf16)a1[1], (__bf16)a1[2], (__bf16)a1[3]};
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) up[ct] = mx[ct] > thr[ct];
+      // (kept here, next to the MFMAs, rather than sunk past the branch below)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) asm volatile("" ::"v"(pb[ct][kc]));
       // A column's reference moves only if one of its four lanes sees an
-      // exponent above the threshold; only then are the column maxima
-      // needed, reduced across the lane rows inside the (rare) branch.
+      // exponent above the threshold (rare): then the column maxima are
+      // reduced across the lane rows, the exponents shift, the weights are
+      // taken again, and what the column has accumulated -- the previous
+      // tile included -- is scaled (by 0 on its first visible tile).
       if (__any(up[0] || up[1])) {
-        // some column's reference moves to its maximum: shift its exponents
-        // and scale what it has accumulated (by 0 on its first visible tile)
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
           mx[ct] = fa_rows_max(mx[ct]);
@@ -574,33 +672,23 @@ __global__ __launch_bounds__(kFaWaves * 64, 1) void segment_fa_kernel(
 #pragma unroll
           for (int dt = 0; dt < NT; ++dt) acc[ct][dt] *= alpha;
         }
+        weights(sacc);
       }
-      bf16x8s pb[2][2];
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-          const floatx4s &a0 = sacc[ct][2 * kc], &a1 = sacc[ct][2 * kc + 1];
-          pb[ct][kc] = bf16x8s{(__bf16)seg_exp2(a0[0]), (__bf16)seg_exp2(a0[1]), (__bf16)seg_exp2(a0[2]),
-                               (__bf16)seg_exp2(a0[3]), (__bf16)seg_exp2(a1[0]), (__bf16)seg_exp2(a1[1]),
-                               (__bf16)seg_exp2(a1[2]), (__bf16)seg_exp2(a1[3])};
-          lacc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[ct][kc], lacc[ct], 0, 0, 0);
-        }
-#pragma unroll
-      for (int dt = 0; dt < NT; ++dt)
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-          const uint2 lo = *reinterpret_cast<const uint2 *>(&s_vt[buf][16 * dt + cl][32 * kc + 4 * kg]);
-          const uint2 hi = *reinterpret_cast<const uint2 *>(&s_vt[buf][16 * dt + cl][32 * kc + 16 + 4 * kg]);
-          const bf16x8s vf = __builtin_bit_cast(bf16x8s, make_uint4(lo.x, lo.y, hi.x, hi.y));
-#pragma unroll
-          for (int ct = 0; ct < 2; ++ct)
-            acc[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[ct][kc], acc[ct][dt], 0, 0, 0);
-        }
+        for (int kc = 0; kc < 2; ++kc) pbp[ct][kc] = pb[ct][kc];
+      vprev = vbuf;
+    } else if (vprev >= 0) {
+      // past this wave's last visible entry: the pending product, while its
+      // V tile is still in LDS (the next iteration overwrites that buffer)
+      pv_tile(pbp, vprev);
+      vprev = -1;
     }
-    if (t + 1 < ntile) lstore(t + 1, buf ^ 1);
+    if (t + 1 < ntile) lstore(t + 1, buf ^ 1, (t + 1 - t0) % 3);
     __syncthreads();
   }
+  if (vprev >= 0) pv_tile(pbp, vprev);
 
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
