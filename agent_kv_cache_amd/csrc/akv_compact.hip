@@ -224,7 +224,8 @@ __global__ __launch_bounds__(kChunkPages) void plan_kernel(
         if (seq_done) *tk = 0;          // re-armed for the next op
         __threadfence();                // the sequence's chunks before the global ticket
       }
-      s_last = seq_done && atomicAdd(&d.ctl[CTL_DONE], 1) == (int)gridDim.y - 1;
+      // (one sequence: its own ticket already names the last workgroup)
+      s_last = seq_done && (gridDim.y == 1 || atomicAdd(&d.ctl[CTL_DONE], 1) == (int)gridDim.y - 1);
     }
     __syncthreads();
     if (!s_last) return;
@@ -232,9 +233,14 @@ __global__ __launch_bounds__(kChunkPages) void plan_kernel(
   } else {
     __syncthreads();
   }
+  // the free count and the latched error, loaded now so that their round
+  // trip overlaps the per-sequence pass below
+  int fc_pre = 0, latched_pre = 0;
   if (t == 0) {
     s_gerr = 0;
     s_nextra = 0;
+    fc_pre = *d.free_count;
+    latched_pre = d.ctl[CTL_ERR];
   }
   __syncthreads();
   int run_m = 0, run_i = 0, run_f = 0;
@@ -343,8 +349,8 @@ __global__ __launch_bounds__(kChunkPages) void plan_kernel(
   __syncthreads();
   if (t == 0) {
     int e = s_gerr;
-    const int fc = *d.free_count;
-    const int latched = d.ctl[CTL_ERR];
+    const int fc = fc_pre;
+    const int latched = latched_pre;
     int ng = 0;
     if (!e && !latched) {
       if (run_m <= fc) {
@@ -473,6 +479,40 @@ __global__ __launch_bounds__(kChunkPages) void plan_kernel(
     constexpr int kB = 8;
     const int *gr = d.groups;
     const int Tm = gr[GR_TM], fc0 = gr[GR_FC], F = gr[GR_F];
+    const int *si = d.seq_info;
+    const int fbd = si[SI_FBD], nmove = si[SI_N_MOVE], nfreed = si[SI_N_FREED];
+    const int base = fc0 - Tm;
+    int32_t *trow = d.table;
+    // (a one-sequence cache shares no page: every released page is pushed,
+    // F == nfreed)
+    if (Tm <= kChunkPages * kB && nfreed <= kChunkPages * kB) {
+      // one pass: every entry read (fresh page ids from the top of the free
+      // stack, the table entries they replace), one barrier, then the writes
+      // -- the pushed pages land where the fresh ones were popped
+      int fresh[kB], old[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        const int k = t + u * kChunkPages;
+        fresh[u] = k < Tm ? d.free_stack[fc0 - 1 - k] : -1;
+        old[u] = k < nfreed ? trow[fbd + k] : 0;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        const int k = t + u * kChunkPages;
+        if (k < Tm) d.stage[k] = fresh[u];
+        if (k < nfreed) {
+          d.free_stack[base + F - 1 - k] = old[u];   // reversed, as in commit_kernel
+          trow[fbd + k] = k < nmove ? fresh[u] : -1;
+        }
+      }
+      if (t == 0) {
+        d.lens[0] = si[SI_NEW_LEN];
+        d.next_pos[0] = si[SI_NEW_NEXT];
+        *d.free_count = base + F;
+      }
+      return;
+    }
     for (int k0 = t; k0 < Tm; k0 += kChunkPages * kB) {
       int v[kB];
 #pragma unroll
@@ -487,10 +527,6 @@ __global__ __launch_bounds__(kChunkPages) void plan_kernel(
       }
     }
     __syncthreads();
-    const int *si = d.seq_info;
-    const int fbd = si[SI_FBD], nmove = si[SI_N_MOVE], nfreed = si[SI_N_FREED];
-    const int base = fc0 - Tm;
-    int32_t *trow = d.table;
     for (int k0 = t; k0 < nfreed; k0 += kChunkPages * kB) {
       int old[kB], fresh[kB];
 #pragma unroll
