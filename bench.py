@@ -295,9 +295,10 @@ def run_history(args):
     sh = W.SHAPES["history_50_turns"]
     hist = W.history_50_turns()
     row = sh.n_layers * sh.n_kv_heads * sh.head_dim * 2
-    # per-sequence page capacity: the run's largest active length, in whole
-    # plan chunks of 256 pages (it also bounds the move's one-shot grid)
-    maxpg = -(-Hn.pages_for(hist.max_active()) // 256) * 256
+    # per-sequence page capacity: the run's largest active length (it also
+    # bounds the move's one-shot grid, whose blocks past an op's units exit
+    # at once)
+    maxpg = Hn.pages_for(hist.max_active())
     cache = Hn.make_cache(sh, [1], 4096, max_blocks_per_seq=maxpg)
     cache.reset()
     dev = cache.device
