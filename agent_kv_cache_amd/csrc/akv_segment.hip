@@ -247,7 +247,11 @@ __global__ __launch_bounds__(kSegWaves * 64, 2) void segment_attn_kernel(
 #ifndef AKV_FA_MIN_WAVES
 #define AKV_FA_MIN_WAVES 1 // waves per SIMD the register budget must allow
 #endif
-constexpr int kFaWaves = AKV_FA_WAVES, kFaKT = 64, kFaCols = 32 * kFaWaves;
+#ifndef AKV_FA_CT
+#define AKV_FA_CT 2        // 16-column MFMA tiles per wave
+#endif
+constexpr int kFaWaves = AKV_FA_WAVES, kFaCT = AKV_FA_CT, kFaKT = 64,
+              kFaCols = 16 * kFaCT * kFaWaves;
 #ifndef AKV_FA_TAU
 #define AKV_FA_TAU 8.0f    // log2 of the largest weight allowed before a column's reference moves
 #endif
@@ -330,13 +334,13 @@ __global__ __launch_bounds__(kFaWaves * 64, AKV_FA_MIN_WAVES) void segment_fa_ke
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int cl = lane & 15, kg = lane >> 4;
 
-  // this lane's column in each of the wave's two column tiles
-  int lim[2];
-  bool rok[2], cok[2];   // the column is a row of the segment / and the segment is valid
-  size_t qrow[2];
+  // this lane's column in each of the wave's column tiles
+  int lim[kFaCT];
+  bool rok[kFaCT], cok[kFaCT];   // the column is a row of the segment / and the segment is valid
+  size_t qrow[kFaCT];
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-    const int c = 32 * wave + 16 * ct + cl;
+  for (int ct = 0; ct < kFaCT; ++ct) {
+    const int c = 16 * kFaCT * wave + 16 * ct + cl;
     const int tq = c / G, hh = c - tq * G, i = i0 + tq;
     rok[ct] = tq < TBW && i < n;
     cok[ct] = !bad && rok[ct];
@@ -347,7 +351,7 @@ __global__ __launch_bounds__(kFaWaves * 64, AKV_FA_MIN_WAVES) void segment_fa_ke
   // valid column cannot see (tiles wholly before it need no causal mask)
   int wave_lim = -1, wave_lo = -1;
   {
-    const int tlo = (32 * wave) / G, thi = min((32 * wave + 31) / G, TBW - 1);
+    const int tlo = (16 * kFaCT * wave) / G, thi = min((16 * kFaCT * wave + 16 * kFaCT - 1) / G, TBW - 1);
     if (!bad && tlo < TBW && i0 + tlo < n) {
       wave_lim = len - n + min(i0 + thi, n - 1);
       wave_lo = len - n + i0 + tlo;
@@ -361,20 +365,22 @@ __global__ __launch_bounds__(kFaWaves * 64, AKV_FA_MIN_WAVES) void segment_fa_ke
   // >= p_i - W + 1.  The sweep starts at the tile of the first row's first
   // visible entry; entries are masked by position (kept in LDS per tile).
   const int W = (d.any_window && !bad) ? d.window[l] : 0;
-  int wlo[2] = {INT_MIN, INT_MIN};
+  int wlo[kFaCT];
+#pragma unroll
+  for (int ct = 0; ct < kFaCT; ++ct) wlo[ct] = INT_MIN;
   int t0 = 0;
   if (W > 0) {
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
+    for (int ct = 0; ct < kFaCT; ++ct)
       if (cok[ct]) wlo[ct] = entry_pos(d, trow, lim[ct]) - W + 1;
     const int me0 = len - n + i0;
     t0 = first_pos_at_least(d, trow, max(0, me0 - W + 1), me0 + 1,
                             entry_pos(d, trow, me0) - W + 1) / kFaKT;
   }
 
-  bf16x8s qf[2][KC];
+  bf16x8s qf[kFaCT][KC];
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct)
+  for (int ct = 0; ct < kFaCT; ++ct)
 #pragma unroll
     for (int c = 0; c < KC; ++c)
       qf[ct][c] = cok[ct] ? seg_load8(q + qrow[ct] * D + 8 * kg + 32 * c)
@@ -389,10 +395,12 @@ __global__ __launch_bounds__(kFaWaves * 64, AKV_FA_MIN_WAVES) void segment_fa_ke
   // cancels the reference.
   // nref = -ref (0 while ref = -inf); thr = the exponent above which the
   // reference moves (-inf while nothing is visible, then AKV_FA_TAU)
-  float nref[2] = {0.f, 0.f}, thr[2] = {-INFINITY, -INFINITY};
-  floatx4s acc[2][NT], lacc[2];
+  float nref[kFaCT], thr[kFaCT];
+  floatx4s acc[kFaCT][NT], lacc[kFaCT];
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
+  for (int ct = 0; ct < kFaCT; ++ct) {
+    nref[ct] = 0.f;
+    thr[ct] = -INFINITY;
     lacc[ct] = floatx4s{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[ct][t] = floatx4s{0.f, 0.f, 0.f, 0.f};
@@ -509,9 +517,9 @@ __global__ __launch_bounds__(kFaWaves * 64, AKV_FA_MIN_WAVES) void segment_fa_ke
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   // O^T += V^T P^T and the weight sums for one tile's probabilities
-  auto pv_tile = [&](const bf16x8s (&p)[2][2], int vbuf) {
+  auto pv_tile = [&](const bf16x8s (&p)[kFaCT][2], int vbuf) {
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
+    for (int ct = 0; ct < kFaCT; ++ct)
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc)
         lacc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, p[ct][kc], lacc[ct], 0, 0, 0);
@@ -523,20 +531,20 @@ __global__ __launch_bounds__(kFaWaves * 64, AKV_FA_MIN_WAVES) void segment_fa_ke
         const uint2 hi = *reinterpret_cast<const uint2 *>(&s_vt[vbuf][16 * dt + cl][32 * kc + 16 + 4 * kg]);
         const bf16x8s vf = __builtin_bit_cast(bf16x8s, make_uint4(lo.x, lo.y, hi.x, hi.y));
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
+        for (int ct = 0; ct < kFaCT; ++ct)
           acc[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, p[ct][kc], acc[ct][dt], 0, 0, 0);
       }
   };
   // the weights of one tile as bf16 MFMA operands: a lane's 8 k-values are
   // its 4 + 4 exponentials of two S^T tiles
-  bf16x8s pb[2][2], pbp[2][2];
+  bf16x8s pb[kFaCT][2], pbp[kFaCT][2];
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct)
+  for (int ct = 0; ct < kFaCT; ++ct)
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) pbp[ct][kc] = __builtin_bit_cast(bf16x8s, make_uint4(0u, 0u, 0u, 0u));
-  auto weights = [&](const floatx4s (&sa)[2][4]) {
+  auto weights = [&](const floatx4s (&sa)[kFaCT][4]) {
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
+    for (int ct = 0; ct < kFaCT; ++ct)
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
         const floatx4s &a0 = sa[ct][2 * kc], &a1 = sa[ct][2 * kc + 1];
@@ -556,7 +564,7 @@ __global__ __launch_bounds__(kFaWaves * 64, AKV_FA_MIN_WAVES) void segment_fa_ke
     if (t + 2 < ntile) pidx(t + 2);
     const int T0 = t * kFaKT;
     if (T0 <= wave_lim) {
-      floatx4s sacc[2][4];
+      floatx4s sacc[kFaCT][4];
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
         bf16x8s kf[KC];
@@ -565,7 +573,7 @@ __global__ __launch_bounds__(kFaWaves * 64, AKV_FA_MIN_WAVES) void segment_fa_ke
           kf[c] = __builtin_bit_cast(bf16x8s,
                                      *reinterpret_cast<const uint4 *>(&s_k[buf][16 * tt + cl][32 * c + 8 * kg]));
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
+        for (int ct = 0; ct < kFaCT; ++ct) {
           floatx4s sa = floatx4s{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int c = 0; c < KC; ++c) sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[c], qf[ct][c], sa, 0, 0, 0);
@@ -574,7 +582,7 @@ __global__ __launch_bounds__(kFaWaves * 64, AKV_FA_MIN_WAVES) void segment_fa_ke
       }
       const bool diag = T0 + kFaKT - 1 > wave_lo;            // wave-uniform
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
+      for (int ct = 0; ct < kFaCT; ++ct) {
         if (diag) {
           // entry T0 + 16 tt + 4 kg + j is visible while <= lim
           const int rel = lim[ct] - T0 - 4 * kg;
@@ -601,8 +609,10 @@ __global__ __launch_bounds__(kFaWaves * 64, AKV_FA_MIN_WAVES) void segment_fa_ke
       // chunk issues the V fragment reads two PV steps ahead, one PV step
       // (two MFMAs; the first four chunks also one weight-sum MFMA) and two
       // softmax elements, so the VALU works while the matrix core multiplies.
-      float mx[2] = {-INFINITY, -INFINITY};
-      bool up[2];
+      float mx[kFaCT];
+      bool up[kFaCT];
+#pragma unroll
+      for (int ct = 0; ct < kFaCT; ++ct) mx[ct] = -INFINITY;
       {
         uint2 vlo[2 * NT], vhi[2 * NT];
         auto vread = [&](int k) {
@@ -610,21 +620,23 @@ __global__ __launch_bounds__(kFaWaves * 64, AKV_FA_MIN_WAVES) void segment_fa_ke
           vlo[k] = *reinterpret_cast<const uint2 *>(&s_vt[vprev][16 * dt + cl][32 * kc + 4 * kg]);
           vhi[k] = *reinterpret_cast<const uint2 *>(&s_vt[vprev][16 * dt + cl][32 * kc + 16 + 4 * kg]);
         };
-        float ex[2][4][4];
+        float ex[kFaCT][4][4];
         vread(0);
         vread(1);
-        // softmax element e = 2k, 2k + 1 of 32 per lane goes with PV step k
-        // (the 16 of D = 64 take two elements' pairs per step)
-        constexpr int EPS = 32 / (2 * NT);
+        // softmax elements EPS k .. EPS k + EPS - 1 of the lane's 16 per
+        // column tile go with PV step k
+        constexpr int EPS = 16 * kFaCT / (2 * NT);
 #pragma unroll
         for (int k = 0; k < 2 * NT; ++k) {
           __builtin_amdgcn_sched_barrier(0);
           if (k + 2 < 2 * NT) vread(k + 2);
-          if (k < 4) lacc[k >> 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pbp[k >> 1][k & 1], lacc[k >> 1], 0, 0, 0);
+          if (k < 2 * kFaCT)
+            lacc[k >> 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pbp[k >> 1][k & 1], lacc[k >> 1], 0, 0, 0);
           const int dt = k >> 1, kc = k & 1;
           const bf16x8s vf = __builtin_bit_cast(bf16x8s, make_uint4(vlo[k].x, vlo[k].y, vhi[k].x, vhi[k].y));
-          acc[0][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pbp[0][kc], acc[0][dt], 0, 0, 0);
-          acc[1][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pbp[1][kc], acc[1][dt], 0, 0, 0);
+#pragma unroll
+          for (int ct = 0; ct < kFaCT; ++ct)
+            acc[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pbp[ct][kc], acc[ct][dt], 0, 0, 0);
 #pragma unroll
           for (int u = 0; u < EPS; ++u) {
             const int e = EPS * k + u, ct = e >> 4, tt = (e & 15) >> 2, j = e & 3;
@@ -644,10 +656,10 @@ __global__ __launch_bounds__(kFaWaves * 64, AKV_FA_MIN_WAVES) void segment_fa_ke
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) up[ct] = mx[ct] > thr[ct];
+      for (int ct = 0; ct < kFaCT; ++ct) up[ct] = mx[ct] > thr[ct];
       // (kept here, next to the MFMAs, rather than sunk past the branch below)
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
+      for (int ct = 0; ct < kFaCT; ++ct)
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) asm volatile("" ::"v"(pb[ct][kc]));
       // A column's reference moves only if one of its four lanes sees an
@@ -655,9 +667,12 @@ __global__ __launch_bounds__(kFaWaves * 64, AKV_FA_MIN_WAVES) void segment_fa_ke
       // reduced across the lane rows, the exponents shift, the weights are
       // taken again, and what the column has accumulated -- the previous
       // tile included -- is scaled (by 0 on its first visible tile).
-      if (__any(up[0] || up[1])) {
+      bool any_up = false;
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
+      for (int ct = 0; ct < kFaCT; ++ct) any_up = any_up || up[ct];
+      if (__any(any_up)) {
+#pragma unroll
+        for (int ct = 0; ct < kFaCT; ++ct) {
           mx[ct] = fa_rows_max(mx[ct]);
           up[ct] = mx[ct] > thr[ct];
           const float sh = up[ct] ? mx[ct] : 0.f;
@@ -675,7 +690,7 @@ __global__ __launch_bounds__(kFaWaves * 64, AKV_FA_MIN_WAVES) void segment_fa_ke
         weights(sacc);
       }
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
+      for (int ct = 0; ct < kFaCT; ++ct)
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) pbp[ct][kc] = pb[ct][kc];
       vprev = vbuf;
@@ -691,7 +706,7 @@ __global__ __launch_bounds__(kFaWaves * 64, AKV_FA_MIN_WAVES) void segment_fa_ke
   if (vprev >= 0) pv_tile(pbp, vprev);
 
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
+  for (int ct = 0; ct < kFaCT; ++ct) {
     if (!rok[ct]) continue;
     const float inv = cok[ct] ? 1.f / lacc[ct][0] : 0.f;   // an invalid segment's rows are zero
     uint16_t *orow = out + qrow[ct] * D + 4 * kg;
