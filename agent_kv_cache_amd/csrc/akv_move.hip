@@ -29,7 +29,10 @@ namespace akv {
 // Launch-shape knobs of the move kernel (compile-time; defaults are the
 // measured best on MI355X for the configurations of the benchmark).
 #ifndef AKV_MOVE_UNROLL
-#define AKV_MOVE_UNROLL 2      // (layer, head) slices loaded before any store
+#define AKV_MOVE_UNROLL 2      // (layer, head) slices loaded before any store (one-shot grid)
+#endif
+#ifndef AKV_MOVE_UNROLL_PERSIST
+#define AKV_MOVE_UNROLL_PERSIST 1  // the same for the persistent grid
 #endif
 #ifndef AKV_MOVE_MIN_WAVES
 #define AKV_MOVE_MIN_WAVES 4   // waves per SIMD the register budget must allow
@@ -96,7 +99,7 @@ __device__ __forceinline__ void move_body(const Dev &d, int mode, int oneshot_ca
   constexpr int NS = kMoveThreads / TPH; // slices per pass
   // (plane, slice) items loaded before any store (a full-row thread holds
   // half the bytes of a half-row thread per item, so it takes more)
-  constexpr int U = FR ? AKV_MOVE_FR_ITEMS : AKV_MOVE_UNROLL;
+  constexpr int U = FR ? AKV_MOVE_FR_ITEMS : ONESHOT ? AKV_MOVE_UNROLL : AKV_MOVE_UNROLL_PERSIST;
   __shared__ int s_dst, s_mv;
   __shared__ int s_src[kPage], s_valid[kPage], s_delta[kPage], s_rep[kPage];
   __shared__ int s_repval[kPage], s_nrep;
