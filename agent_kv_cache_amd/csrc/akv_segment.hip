@@ -553,11 +553,12 @@ __global__ __launch_bounds__(kFaWaves * 64, AKV_FA_MIN_WAVES) void segment_fa_ke
                              (__bf16)seg_exp2(a1[2]), (__bf16)seg_exp2(a1[3])};
       }
   };
-  // V buffer of the tile whose PV product is pending (-1: none).  A wave's
-  // first visible tile is the sweep's first tile, and its pending product is
-  // zero weights times the zeroed buffer 2; once a wave is past its last
-  // visible entry it stays past it.
+  // V buffer of the tile whose PV product is pending, and whether one is.  A
+  // wave's first visible tile is the sweep's first tile, and the product it
+  // takes then is zero weights times the zeroed buffer 2; once a wave is
+  // past its last visible entry it stays past it.
   int vprev = 2;
+  bool pend = false;
   for (int t = t0; t < ntile; ++t) {
     const int buf = (t - t0) & 1, vbuf = (t - t0) % 3;
     if (t + 1 < ntile) gload(t + 1);
@@ -694,16 +695,17 @@ __global__ __launch_bounds__(kFaWaves * 64, AKV_FA_MIN_WAVES) void segment_fa_ke
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) pbp[ct][kc] = pb[ct][kc];
       vprev = vbuf;
-    } else if (vprev >= 0) {
+      pend = true;
+    } else if (pend) {
       // past this wave's last visible entry: the pending product, while its
       // V tile is still in LDS (the next iteration overwrites that buffer)
       pv_tile(pbp, vprev);
-      vprev = -1;
+      pend = false;
     }
     if (t + 1 < ntile) lstore(t + 1, buf ^ 1, (t + 1 - t0) % 3);
     __syncthreads();
   }
-  if (vprev >= 0) pv_tile(pbp, vprev);
+  if (pend) pv_tile(pbp, vprev);
 
 #pragma unroll
   for (int ct = 0; ct < kFaCT; ++ct) {
