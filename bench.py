@@ -17,9 +17,10 @@ Llama-70B shape and the 50-turn history follow under `configs`.
 `value` = algorithmic KV bytes of the whole step (drop+reposition and
 decode) / wall time per step, in GB/s.  The `roofline` object covers the
 dominant kernel (per-launch algorithmic bytes / average launch time from HIP
-events recorded on the launch stream); `parts` gives both parts;
-`cpu_baseline` times the fp64 oracle on a bounded sample in a process pool
-on the host's cores.
+events recorded on the launch stream); `parts` gives both parts, with the
+move and decode kernels' per-step median / min / max from a second, untimed
+pass of the same steps; `cpu_baseline` times the fp64 oracle on a bounded
+sample in a process pool on the host's cores.
 """
 from __future__ import annotations
 
@@ -863,6 +864,25 @@ def run_step(name, args):
             },
         },
     }
+    # Per-step spread of the two kernels: the same steps once more, each
+    # step's event times read back on their own (outside the timed region).
+    # (a reset clears every kernel's accumulator: read both, then reset)
+    spread = {"move": [], "attn": []}
+    cache.profile_read("move", reset=True)
+    cache.profile_enable(True)
+    for _ in range(args.steps):
+        step()
+        for k in spread:
+            spread[k].append(cache.profile_read(k)[0])
+        cache.profile_read("move", reset=True)
+    cache.profile_enable(False)
+    if cache.sync_status() != 0:
+        raise RuntimeError("device status after the spread pass")
+    for part, k in (("drop_reposition", "move"), ("decode_attention", "attn")):
+        v = np.sort(np.array(spread[k]))
+        res["parts"][part][f"{k}_ms_per_step"] = {
+            "median": round(float(np.median(v)), 4), "min": round(float(v[0]), 4),
+            "max": round(float(v[-1]), 4), "steps": len(v)}
     if args.graph:
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
