@@ -50,12 +50,20 @@ def make_cache(shape: Shape, seq_lens: Sequence[int], extra_pages: int,
                     len(seq_lens), maxpg, shape.rope_base, device=device, **cache_kw)
 
 
+def default_token_base(b: int) -> int:
+    """First token id of sequence b in the seeded fills: (b mod 128) * 2^24,
+    so that every id of a sequence up to 2^24 tokens fits int32 (the cache's
+    id type); ids repeat across sequences 128 apart."""
+    return (int(b) & 127) << 24
+
+
 def fill(cache: AkvCache, shape: Shape, seq_lens: Sequence[int], data_seed: int,
          gen_device: str = "cuda", token_base: Optional[List[int]] = None,
          max_tokens_per_call: int = 16384, progress=None):
     """Append every sequence's tokens chunk by chunk (seeded per chunk).
 
-    Token ids of sequence b are token_base[b] + 0, 1, ... (default b * 2^24).
+    Token ids of sequence b are token_base[b] + 0, 1, ... (default
+    default_token_base(b)).
     Each akv_append call carries at most `max_tokens_per_call` tokens so the
     set-up temporaries stay small next to a large pool.
     """
@@ -80,7 +88,7 @@ def fill(cache: AkvCache, shape: Shape, seq_lens: Sequence[int], data_seed: int,
                 counts[b] = m
                 ks.append(seq_chunk(shape, data_seed, b, c, m, "k", gen_device).to(dev))
                 vs.append(seq_chunk(shape, data_seed, b, c, m, "v", gen_device).to(dev))
-                base = (b << 24) if token_base is None else token_base[b]
+                base = default_token_base(b) if token_base is None else token_base[b]
                 toks.append(torch.arange(base + c * CHUNK, base + c * CHUNK + m,
                                          dtype=torch.int32, device=dev))
             k = torch.cat(ks, dim=1).contiguous() if len(ks) > 1 else ks[0]

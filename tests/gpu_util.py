@@ -45,7 +45,7 @@ def oracle_for(shape: Shape, seq_lens: Sequence[int], data_seed: int, layers=Non
         n = seq_lens[b]
         for c in range((int(n) + Hn.CHUNK - 1) // Hn.CHUNK):
             m = min(Hn.CHUNK, int(n) - c * Hn.CHUNK)
-            tid = (b << 24) + c * Hn.CHUNK + np.arange(m)
+            tid = Hn.default_token_base(b) + c * Hn.CHUNK + np.arange(m)
             if with_kv:
                 k = Hn.seq_chunk(shape, data_seed, b, c, m, "k", gen_device)[lay]
                 v = Hn.seq_chunk(shape, data_seed, b, c, m, "v", gen_device)[lay]
