@@ -709,9 +709,15 @@ __global__ __launch_bounds__(kPlanThreads) void append_plan_kernel(Dev d, const 
 // rotary chunk pair rotated in fp64 and rounded once, the non-rotary tail
 // copied.
 #ifndef AKV_APPEND_BATCH
-#define AKV_APPEND_BATCH 4
+#define AKV_APPEND_BATCH 2       // plain append: 16-B chunks per plane loaded before they are stored
 #endif
-constexpr int kAppendBatch = AKV_APPEND_BATCH;   // 16-B chunks loaded before they are stored
+#ifndef AKV_APPEND_ROPE_BATCH
+#define AKV_APPEND_ROPE_BATCH 8  // the same for the RoPE-fused append
+#endif
+// (Llama-8B shape, 32768 tokens, two A/B pairs on one box: plain batch 2
+// 0.694-0.697 of the HBM peak vs 4 0.685, 1 0.690, 8 0.674; RoPE-fused
+// batch 8 0.718 vs 4 0.711-0.715)
+constexpr int append_batch(bool rope) { return rope ? AKV_APPEND_ROPE_BATCH : AKV_APPEND_BATCH; }
 constexpr int kAppTok = 16;                      // new tokens per workgroup
 #ifndef AKV_APPEND_LAYERS
 #define AKV_APPEND_LAYERS 2
@@ -744,6 +750,7 @@ __global__ __launch_bounds__(256) void append_copy_kernel(Dev d, int64_t n_new, 
                                                           const int32_t *__restrict__ tok_new) {
   if (d.ctl[CTL_OP_OK] == 0) return;
   constexpr int LPB = append_layers(ROPE);
+  constexpr int kAppendBatch = append_batch(ROPE);
   constexpr int C8 = D / 8;                    // 16-B chunks per row
   __shared__ int s_page[kAppTok], s_row[kAppTok], s_pos[kAppTok];
   __shared__ double2 s_cs[ROPE ? kAppTok : 1][ROPE ? kMaxHalf : 1];
