@@ -171,13 +171,17 @@ akv_status run_compaction(akv_cache *c, const uint8_t *mask, const int32_t *new_
   // the persistent grid is needed only if this call could rebuild more
   // (page, layer group) units than the one-shot grid holds: the cache-wide
   // bound, or the caller's per-call bound (a fork copies at most
-  // max_blocks_per_seq pages per source)
+  // max_blocks_per_seq pages per source), which also trims the one-shot grid
+  // (its blocks past the op's units only exit)
   bool persistent = c->move_persistent;
-  if (max_pages >= 0) persistent = max_pages * c->layer_groups > c->oneshot_cap;
+  int cap = c->oneshot_cap;
+  if (max_pages >= 0) {
+    persistent = max_pages * c->layer_groups > c->oneshot_cap;
+    if (!persistent) cap = (int)std::max(1LL, max_pages * c->layer_groups);
+  }
   {
     Timed tm(c, AKV_KERNEL_MOVE, st);
-    AKV_HIP(akv::launch_move(c->dev, mode, persistent ? c->move_grid : 0, c->oneshot_cap, 0,
-                             st));
+    AKV_HIP(akv::launch_move(c->dev, mode, persistent ? c->move_grid : 0, cap, 0, st));
   }
   if (!(mode & akv::M_STAGED)) {
     Timed tm(c, AKV_KERNEL_COMMIT, st);
