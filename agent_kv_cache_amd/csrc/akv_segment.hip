@@ -242,7 +242,7 @@ __global__ __launch_bounds__(kSegWaves * 64, 2) void segment_attn_kernel(
 #define AKV_FA_KPAD 8      // halfwords of padding per K row in LDS (keeps 16-B alignment)
 #endif
 #ifndef AKV_FA_WAVES
-#define AKV_FA_WAVES 8     // waves per workgroup (32 columns each)
+#define AKV_FA_WAVES 8     // waves per workgroup (16 * AKV_FA_CT columns each)
 #endif
 #ifndef AKV_FA_MIN_WAVES
 #define AKV_FA_MIN_WAVES 1 // waves per SIMD the register budget must allow
@@ -606,10 +606,11 @@ __global__ __launch_bounds__(kFaWaves * 64, AKV_FA_MIN_WAVES) void segment_fa_ke
       }
       // The previous tile's PV product and this tile's exponents against the
       // current reference, their column maxima and weights, written out in
-      // 16 chunks whose order the compiler keeps (scheduling barriers): each
-      // chunk issues the V fragment reads two PV steps ahead, one PV step
-      // (two MFMAs; the first four chunks also one weight-sum MFMA) and two
-      // softmax elements, so the VALU works while the matrix core multiplies.
+      // 2 * NT chunks whose order the compiler keeps (scheduling barriers):
+      // each chunk issues the V fragment reads two PV steps ahead, one PV
+      // step (one MFMA per column tile; the first 2 * kFaCT chunks also one
+      // weight-sum MFMA) and EPS softmax elements, so the VALU works while the
+      // matrix core multiplies.
       float mx[kFaCT];
       bool up[kFaCT];
 #pragma unroll
