@@ -11,7 +11,8 @@ prints ONE JSON line.  The headline (`value`, `roofline`, `cpu_baseline`) is
 the largest single-GPU configuration, the ragged batch (64 sequences of
 8K..64K tokens, Llama-8B KV shape, shuffled pages, ~40% dropped, ~155 GB of
 KV); the Llama-8B-shaped single sequence, the one-layer 4K case, the
-Llama-70B shape and the 50-turn history follow under `configs`.
+Llama-70B shape and the 50-turn history follow under `configs` (the
+latency-bound one-layer step also as one HIP graph replay, `graph_ms_per_step`).
 `--workload NAME` runs one of them (or the restore / append workloads) alone.
 
 `value` = algorithmic KV bytes of the whole step (drop+reposition and
@@ -918,7 +919,7 @@ def compact(line):
     keep = ("value", "unit", "ms_per_step", "steps", "warmup", "roofline", "parts",
             "cpu_baseline", "ops", "ops_ms_total", "ops_bytes_total", "drop_reposition_gbps",
             "drop_reposition_frac_of_peak", "decode_ms", "decode_gbps", "decode_frac_of_peak",
-            "final_active")
+            "final_active", "graph_ms_per_step", "graph_value")
     out = {k: line[k] for k in keep if k in line}
     out["workload"] = line.get("config", {}).get("workload", line.get("workload"))
     return out
@@ -986,7 +987,9 @@ def main():
     print(f"[bench] ragged_batch_64 done ({time.time() - t0:.0f} s)", file=sys.stderr, flush=True)
     res["configs"] = {}
     for name in ("llama8b_32k", "one_layer_4k", "llama70b_4x64k"):
-        res["configs"][name] = compact(run_step(name, args))
+        # the latency-bound one-layer step is also timed as one HIP graph replay
+        a = argparse.Namespace(**{**vars(args), "graph": args.graph or name == "one_layer_4k"})
+        res["configs"][name] = compact(run_step(name, a))
         print(f"[bench] {name} done ({time.time() - t0:.0f} s)", file=sys.stderr, flush=True)
     res["configs"]["history_50_turns"] = compact(run_history(args))
     print(f"[bench] history_50_turns done ({time.time() - t0:.0f} s)", file=sys.stderr, flush=True)
