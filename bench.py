@@ -26,6 +26,7 @@ sample in a process pool on the host's cores.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -187,11 +188,14 @@ def _critical_path(results):
 
 def _cpu_step_unit(task):
     """One (sequence, layer) unit in a pool worker: the oracle holds that
-    layer of the sequence, applies the fused drop + reposition and the decode
-    attention; returns (pid, seconds of each)."""
+    layer of the sequence (with the run's partial RoPE, frequency table and
+    that layer's window, if any), applies the fused drop + reposition and the
+    decode attention; returns (pid, seconds of each)."""
     from oracle import akv_oracle as O
     n = task["k"].shape[0]
-    oc = O.OracleCache(1, task["H"], task["D"], task["base"])
+    oc = O.OracleCache(1, task["H"], task["D"], task["base"], rotary_dim=task.get("rotary_dim"),
+                       theta=task.get("theta"),
+                       window=[task["window"]] if task.get("window") else None)
     oc.append(0, np.arange(n), O.bf16_from_bits(task["k"])[:, None],
               O.bf16_from_bits(task["v"])[:, None])
     t0 = time.perf_counter()
@@ -208,17 +212,20 @@ def _u16(t):
     return t.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
 
 
-def cpu_baseline(wl, layers, seqs=None):
+def cpu_baseline(wl, layers, seqs=None, ropt=None):
     """The fp64 oracle as it stands, on a bounded sample of the workload
     (the listed layers of the listed sequences, every token), one (sequence,
-    layer) unit per task of a process pool; bytes are the sample's share of
-    the same algorithmic bytes as the GPU figure."""
+    layer) unit per task of a process pool, with the run's RoPE options
+    (`ropt`, as for the cache); bytes are the algorithmic bytes of the
+    sample itself (its layers and sequences)."""
     import torch
 
     from agent_kv_cache_amd import harness as Hn
     from agent_kv_cache_amd.workloads import randn_bf16
 
     sh = wl.shape
+    ropt = ropt or {}
+    win = ropt.get("layer_window")
     seqs = list(range(wl.n_seqs)) if seqs is None else list(seqs)
     q = randn_bf16((wl.n_seqs, sh.n_layers, sh.n_q_heads, sh.head_dim), 202, device="cuda")
     tasks = []
@@ -234,16 +241,26 @@ def cpu_baseline(wl, layers, seqs=None):
             tasks.append(dict(H=sh.n_kv_heads, D=sh.head_dim, base=sh.rope_base,
                               k=np.ascontiguousarray(k[i]), v=np.ascontiguousarray(v[i]),
                               mask=np.asarray(wl.masks[b][:n]),
-                              q=q[b, l].double().cpu().numpy()))
+                              q=q[b, l].double().cpu().numpy(),
+                              rotary_dim=ropt.get("rotary_dim"), theta=ropt.get("inv_freq"),
+                              window=win[l] if win else 0))
     del q
     torch.cuda.empty_cache()
     res, wall, nw = _pool_map(_cpu_step_unit, tasks)
     (t_dr, t_dec), t_all, used = _critical_path(res)
-    ab = algorithmic_bytes(sh, [wl.seq_lens[b] for b in seqs], [wl.masks[b] for b in seqs])
-    frac = len(layers) / sh.n_layers
+    # the sample's own algorithmic bytes: its layers (with their windows) and
+    # sequences, as if they were the whole cache
+    ab = algorithmic_bytes(dataclasses.replace(sh, n_layers=len(layers)),
+                           [wl.seq_lens[b] for b in seqs], [wl.masks[b] for b in seqs],
+                           [win[l] for l in layers] if win else None)
     cpu_s = sum(r[1] + r[2] for r in res)
+    variant = "".join(f", {k} {v}" for k, v in (
+        ("rotary_dim", ropt.get("rotary_dim")),
+        ("layer windows", sorted(set(win)) if win else None)) if v)
+    if ropt.get("inv_freq") is not None:
+        variant += ", explicit frequency table"
     return {
-        "value": round((ab["b_dr"] + ab["b_att"]) * frac / t_all / 1e9, 4),
+        "value": round((ab["b_dr"] + ab["b_att"]) / t_all / 1e9, 4),
         "unit": "GB/s",
         "cores": used,
         "kind": "oracle",
@@ -252,9 +269,9 @@ def cpu_baseline(wl, layers, seqs=None):
                   f"drop+reposition then decode per unit in a {nw}-process pool: "
                   f"{cpu_s:.1f} s of op work, {t_all:.2f} s on the busiest worker "
                   f"({wall:.1f} s pool wall time including unpacking the inputs); bytes are "
-                  f"the sample's share of the algorithmic bytes",
-        "drop_reposition_gbps": round(ab["b_dr"] * frac / t_dr / 1e9, 4),
-        "decode_gbps": round(ab["b_att"] * frac / t_dec / 1e9, 4),
+                  f"the sample's own algorithmic bytes{variant}",
+        "drop_reposition_gbps": round(ab["b_dr"] / t_dr / 1e9, 4),
+        "decode_gbps": round(ab["b_att"] / t_dec / 1e9, 4),
         **host_info(),
     }
 
@@ -906,9 +923,9 @@ def run_step(name, args):
         gms = (tg1 - tg0) * 1e3 / args.steps
         res["graph_ms_per_step"] = round(gms, 4)
         res["graph_value"] = round((ab["b_dr"] + ab["b_att"]) / (gms * 1e-3) / 1e9, 2)
-    if not args.no_cpu_baseline and not ropt:
+    if not args.no_cpu_baseline:
         layers, seqs = CPU_SAMPLE[wl.name]
-        res["cpu_baseline"] = cpu_baseline(wl, layers, seqs)
+        res["cpu_baseline"] = cpu_baseline(wl, layers, seqs, ropt)
     del cache, q, out, ws, mask, snap
     torch.cuda.empty_cache()
     return res
