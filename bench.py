@@ -76,6 +76,20 @@ def algorithmic_bytes(shape, seq_lens, masks, layer_window=None):
                 b_att=b_att, b_att_kv=seen * 2 * lrow)
 
 
+def variant_tag(args):
+    """Suffix naming a RoPE-variant run in its counter records ('' for the
+    plain configuration)."""
+    tag = ""
+    if args.rotary_dim:
+        tag += f"_rotary{args.rotary_dim}"
+    if args.freq != "base":
+        tag += f"_{args.freq}_freq"
+    if args.window:
+        tag += f"_window{args.window}" + ("_alternate" if args.window_every == 2
+                                           else f"_every{args.window_every}")
+    return tag
+
+
 def rope_options(args, shape):
     """Cache options for the RoPE-variant runs (partial RoPE, a frequency
     table, alternating sliding-window layers), as AkvCache keywords."""
@@ -831,7 +845,7 @@ def run_step(name, args):
     # kernel and workload (FETCH_SIZE and WRITE_SIZE scaled by what they read
     # for a plain copy of known size), used only while the kernel source is
     # unchanged since the counters were taken.
-    traffic = counted_traffic(f"{dom}_kernel_{wl.name}_counters.json") if not ropt else None
+    traffic = counted_traffic(f"{dom}_kernel_{wl.name}{variant_tag(args)}_counters.json")
 
     res = {
         "metric": METRIC,
