@@ -214,6 +214,29 @@ __global__ __launch_bounds__(kChunkPages) void plan_kernel(
   if (gridDim.x * gridDim.y > 1) {
     const int nch_b = max(1, (P + kChunkPages - 1) / kChunkPages);
     if (c >= nch_b) return;
+#if AKV_PLAN_SCOPED_FENCES
+    // One thread orders the workgroup's records (every wave's stores precede
+    // the barrier) before its ticket with a release fence, and the last
+    // workgroup acquires them all: one L2 write-back and one invalidate on
+    // the way to the finalize instead of full fences around each step.
+    __syncthreads();
+    if (t == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      bool seq_done = true;
+      if (nch_b > 1) {
+        int *tk = &d.seq_info[(size_t)b * kSeqInfo + SI_TICKET];
+        seq_done = atomicAdd(tk, 1) == nch_b - 1;
+        if (seq_done) *tk = 0;          // re-armed for the next op
+        // the sequence's chunks, acquired, are released again with the global ticket
+        if (seq_done && gridDim.y > 1) __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
+      }
+      // (one sequence: its own ticket already names the last workgroup)
+      s_last = seq_done && (gridDim.y == 1 || atomicAdd(&d.ctl[CTL_DONE], 1) == (int)gridDim.y - 1);
+      if (s_last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    __syncthreads();
+    if (!s_last) return;
+#else
     __threadfence();
     __syncthreads();
     if (t == 0) {
@@ -230,6 +253,7 @@ __global__ __launch_bounds__(kChunkPages) void plan_kernel(
     __syncthreads();
     if (!s_last) return;
     __threadfence();
+#endif
   } else {
     __syncthreads();
   }
