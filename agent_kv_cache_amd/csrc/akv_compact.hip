@@ -24,6 +24,12 @@ namespace akv {
 
 constexpr int kPlanThreads = 1024;
 
+// Plan tickets ordered by one release fence per workgroup and one acquire in
+// the last one (0: full fences around each ticket step).
+#ifndef AKV_PLAN_SCOPED_FENCES
+#define AKV_PLAN_SCOPED_FENCES 1
+#endif
+
 // ---------------------------------------------------------------------------
 // helpers
 // ---------------------------------------------------------------------------

@@ -76,11 +76,6 @@ enum SeqInfo : int {
 // Ops that need at most this many one-shot blocks (one per layer group of
 // each rebuilt page) are moved by a one-shot grid, larger ones by a
 // persistent grid.
-// Plan tickets ordered by one release fence per workgroup and one acquire in
-// the last one (0: full fences around each ticket step).
-#ifndef AKV_PLAN_SCOPED_FENCES
-#define AKV_PLAN_SCOPED_FENCES 1
-#endif
 #ifndef AKV_MOVE_ONESHOT_CAP
 #define AKV_MOVE_ONESHOT_CAP 131072
 #endif
