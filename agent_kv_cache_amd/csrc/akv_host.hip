@@ -104,7 +104,14 @@ struct Timed {
     if (c->profile) {
       a = take_event(c);
       b = take_event(c);
-      if (a && b) (void)hipEventRecord(a, st);
+      if (a && b) {
+        (void)hipEventRecord(a, st);
+      } else {
+        // (one of the two could not be created: time nothing, keep the other)
+        if (a) c->spare.push_back(a);
+        if (b) c->spare.push_back(b);
+        a = b = nullptr;
+      }
     }
   }
   ~Timed() {
@@ -602,16 +609,24 @@ akv_status akv_profile_enable(akv_cache *c, int on) {
 akv_status akv_profile_read(akv_cache *c, int kernel, double *total_ms, int64_t *launches,
                             int reset) {
   if (!c || kernel < 0 || kernel >= AKV_KERNEL_COUNT) return AKV_ERR_ARG;
-  for (auto &r : c->pending) {
-    AKV_HIP(hipEventSynchronize(r.b));
+  // pairs are folded in and recycled one at a time, so a failure leaves only
+  // the unread ones pending (none is counted twice)
+  size_t done = 0;
+  akv_status st = AKV_OK;
+  for (; done < c->pending.size(); ++done) {
+    const auto &r = c->pending[done];
     float ms = 0.f;
-    AKV_HIP(hipEventElapsedTime(&ms, r.a, r.b));
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) {
+      st = AKV_ERR_HIP;
+      break;
+    }
     c->total_ms[r.kernel] += ms;
     c->launches[r.kernel] += 1;
     c->spare.push_back(r.a);
     c->spare.push_back(r.b);
   }
-  c->pending.clear();
+  c->pending.erase(c->pending.begin(), c->pending.begin() + done);
+  if (st != AKV_OK) return st;
   if (total_ms) *total_ms = c->total_ms[kernel];
   if (launches) *launches = c->launches[kernel];
   if (reset) {
