@@ -338,7 +338,7 @@ def run_history(args):
     tot_bytes = tot_ms = mv_bytes = mv_ms = 0.0
     n_ops = 0
     per_op = []
-    cpu_layers = [0, 12, 24, sh.n_layers - 1]    # the CPU baseline's layer sample
+    cpu_layers = list(range(0, sh.n_layers, 3))  # the CPU baseline's layer sample (12 of 36)
     cpu_ops = []                                 # the same op list for the oracle
     for op in hist.ops:
         if op[0] == "append":
@@ -717,7 +717,11 @@ def run_append(args):
         kms = ms / max(cnt, 1)
         res[name] = {"ms": round(kms, 4), "gbps": round(alg / (kms * 1e-3) / 1e9, 1),
                      "frac_of_peak": round(alg / (kms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-                     "ms_per_step_wall": round((t1 - t0) * 1e3 / args.steps, 4)}
+                     "ms_per_step_wall": round((t1 - t0) * 1e3 / args.steps, 4),
+                     # HBM bytes per launch from the committed counter record of
+                     # this kernel and variant (None once its sources changed)
+                     "traffic": counted_traffic(
+                         f"{name}_kernel_append_llama8b_32k{variant_tag(args)}_counters.json")}
     fr = res["append_rope"]
     return {
         "metric": "append GB/s (K/V write of new tokens, plain and RoPE-fused), 1 GPU",
@@ -730,7 +734,7 @@ def run_append(args):
                    **({"rotary_dim": args.rotary_dim} if args.rotary_dim else {})},
         "roofline": {"bound": "hbm", "kernel": "append_copy_kernel (RoPE fused)",
                      "achieved": fr["gbps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": fr["frac_of_peak"], "traffic": None},
+                     "frac": fr["frac_of_peak"], "traffic": fr["traffic"]},
         "parts": res,
     }
 
