@@ -919,6 +919,37 @@ def run_step(name, args):
         res["parts"][part][f"{k}_ms_per_step"] = {
             "median": round(float(np.median(v)), 4), "min": round(float(v[0]), 4),
             "max": round(float(v[-1]), 4), "steps": len(v)}
+    if wl.n_seqs == 1 and sh.n_layers > 1:
+        # Secondary: the same decode as one launch per layer (as a model's
+        # forward issues it), timed over the state the steps left; its
+        # outputs are compared with the one-launch outputs of the last step.
+        L = sh.n_layers
+        wsl = torch.empty(max(256, cache.decode_workspace_bytes(1, sh.n_q_heads)),
+                          dtype=torch.uint8, device="cuda")
+        ql = [q[:, l:l + 1].contiguous() for l in range(L)]
+        ol = [torch.empty_like(x) for x in ql]
+
+        def per_layer():
+            for l in range(L):
+                cache.decode_attention(ql[l], ol[l], wsl, layer_begin=l, n_layers=1)
+        for _ in range(args.warmup):
+            per_layer()
+        torch.cuda.synchronize()
+        cache.profile_read("attn", reset=True)
+        cache.profile_enable(True)
+        for _ in range(args.steps):
+            per_layer()
+        cache.profile_enable(False)
+        if cache.sync_status() != 0:
+            raise RuntimeError("device status after the per-layer decode")
+        pl_ms = (cache.profile_read("attn")[0] + cache.profile_read("combine")[0]) / args.steps
+        diff = max(float((ol[l].float() - out[:, l:l + 1].float()).abs().max()) for l in range(L))
+        res["parts"]["decode_attention"]["per_layer_launches"] = {
+            "launches": L, "ms": round(pl_ms, 4),
+            "gbps": round(ab["b_att"] / (pl_ms * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(ab["b_att"] / (pl_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "max_abs_diff_vs_one_launch": diff}
+        del wsl, ql, ol
     if args.graph:
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
