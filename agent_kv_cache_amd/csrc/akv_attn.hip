@@ -261,11 +261,15 @@ __global__ __launch_bounds__(kAttnWaves * 64, AKV_ATTN_MIN_WAVES) void attn_kern
 }
 
 // Merge split partials of one (sequence, layer, query head) row.  All split
-// records of the row are loaded up front (independent loads in flight).
+// records of the row are loaded up front (independent loads in flight), in
+// batches of AKV_COMBINE_UNROLL records (one dependent round trip per batch).
+#ifndef AKV_COMBINE_UNROLL
+#define AKV_COMBINE_UNROLL 16
+#endif
 template <int D>
 __global__ __launch_bounds__(D) void combine_kernel(const float *__restrict__ part,
                                                     uint16_t *__restrict__ out, int nsplit) {
-  constexpr int kMaxUnroll = 16;
+  constexpr int kMaxUnroll = AKV_COMBINE_UNROLL;
   const size_t row = blockIdx.x;
   const int dim = threadIdx.x;
   const float *pr = part + row * nsplit * (size_t)(D + 2);
@@ -273,19 +277,23 @@ __global__ __launch_bounds__(D) void combine_kernel(const float *__restrict__ pa
   for (int s0 = 0; s0 < nsplit; s0 += kMaxUnroll) {
     const int n = min(kMaxUnroll, nsplit - s0);
     float ms[kMaxUnroll], ls[kMaxUnroll], os[kMaxUnroll];
+    // unconditional loads (a record past the last split reads the last
+    // one again and is then neutralised), so every load of the batch is
+    // issued before the first wait
 #pragma unroll
     for (int k = 0; k < kMaxUnroll; ++k) {
-      if (k < n) {
-        const float *ps = pr + (size_t)(s0 + k) * (D + 2);
-        ms[k] = ps[0];
-        ls[k] = ps[1];
-        os[k] = ps[2 + dim];
-      } else {
+      const float *ps = pr + (size_t)(s0 + min(k, n - 1)) * (D + 2);
+      ms[k] = ps[0];
+      ls[k] = ps[1];
+      os[k] = ps[2 + dim];
+    }
+#pragma unroll
+    for (int k = 0; k < kMaxUnroll; ++k)
+      if (k >= n) {
         ms[k] = -INFINITY;
         ls[k] = 0.f;
         os[k] = 0.f;
       }
-    }
     float Mn = M;
 #pragma unroll
     for (int k = 0; k < kMaxUnroll; ++k) Mn = fmaxf(Mn, ms[k]);
