@@ -340,6 +340,18 @@ def test_llama8b_full_size_sampled():
     out = _decode(cache, q)
     err = check_attention(cache, oc, q, out, layers=layers)
     say("llama8b_32k attention max abs err (sampled layers)", err)
+    # the same decode as one launch per layer (split-K over one layer's rows
+    # and the combine kernel), as the benchmark also times it
+    out_pl = torch.zeros_like(q)
+    ws = torch.empty(max(256, cache.decode_workspace_bytes(1, sh.n_q_heads)), dtype=torch.uint8,
+                     device=cache.device)
+    for l in layers:
+        ol = torch.empty_like(q[:, l:l + 1])
+        cache.decode_attention(q[:, l:l + 1].contiguous(), ol, ws, layer_begin=l, n_layers=1)
+        out_pl[:, l:l + 1] = ol
+    assert cache.sync_status() == 0
+    err = check_attention(cache, oc, q, out_pl, layers=layers, what="per-layer launches")
+    say("llama8b_32k per-layer attention max abs err (sampled layers)", err)
 
 
 def test_degenerate_masks_and_positions():
