@@ -193,3 +193,31 @@ def test_freed_pages_are_handed_out_in_their_old_order():
                  torch.arange(n_new, dtype=torch.int32, device=cache.device))
     assert cache.sync_status() == 0
     assert cache.block_table[1, :20].tolist() == list(range(10, 30))
+
+
+@pytest.mark.parametrize("rope", [False, True])
+def test_append_full_size_sampled(rope):
+    """The benchmark's append: the Llama-8B-shaped request's 32768 tokens
+    written into an empty sequence in one call, plain (keys given rotated)
+    and with the RoPE step fused in; every position, id and length checked,
+    K and V of three layers against the oracle."""
+    wl = W.llama8b_32k()
+    sh = wl.shape
+    n = wl.seq_lens[0]
+    layers = [0, 17, 31]
+    say(f"case append full size rope={rope}: {n} tokens x {sh.n_layers} layers")
+    cache = Hn.make_cache(sh, [n], 8)
+    cache.reset()
+    k = W.randn_bf16((sh.n_layers, n, sh.n_kv_heads, sh.head_dim), 205, device="cuda")
+    v = W.randn_bf16((sh.n_layers, n, sh.n_kv_heads, sh.head_dim), 206, device="cuda")
+    tid = torch.arange(n, dtype=torch.int32, device=cache.device)
+    counts = torch.tensor([n], dtype=torch.int32, device=cache.device)
+    (cache.append_rope if rope else cache.append)(counts, n, k, v, tid)
+    assert cache.sync_status() == 0
+    oc = O.OracleCache(len(layers), sh.n_kv_heads, sh.head_dim, sh.rope_base)
+    kl = to_f64(k[layers].permute(1, 0, 2, 3))
+    vl = to_f64(v[layers].permute(1, 0, 2, 3))
+    (oc.append_rotated if rope else oc.append)(0, np.arange(n), kl, vl)
+    check_meta(cache, oc)
+    worst = check_kv(cache, oc, layers=layers, k_ulp=1 if rope else 0)
+    say(" worst K ulp on sampled layers", worst)
