@@ -227,3 +227,46 @@ def test_window_with_partial_rope_after_reposition():
     out = run_segments(cache, qs, segs)
     assert cache.sync_status() == 0
     check_segments(oc, qs, out, segs)
+
+
+# ---------------------------------------------------------------------------
+# the benchmark's variant runs at full size (Llama-8B shape, 32768 tokens)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("variant", ["rotary64", "llama3", "window128"])
+def test_variants_full_size_sampled(variant):
+    """The Llama-8B-shaped drop + reposition and decode as the benchmark runs
+    it with partial RoPE (r = 64), the Llama 3.1 frequency table, or
+    128-token windows on every other layer; lengths, positions and ids
+    everywhere, K / V and attention on sampled layers (a windowed and two
+    full layers) against the oracle."""
+    wl = W.llama8b_32k()
+    sh = wl.shape
+    kw, okw = {}, {}
+    if variant == "rotary64":
+        kw["rotary_dim"] = okw["rotary_dim"] = 64
+    elif variant == "llama3":
+        th = O.llama3_theta(O.rope_theta(sh.head_dim, sh.rope_base), 8.0, 1.0, 4.0, 8192)
+        kw["inv_freq"] = okw["theta"] = th
+    else:
+        win = [128 if l % 2 == 0 else 0 for l in range(sh.n_layers)]
+        kw["layer_window"] = okw["window"] = win
+    layers = [0, 17, 30]
+    say(f"case variant {variant} full size")
+    extra = Hn.moved_pages(wl.seq_lens[0], wl.masks[0])
+    cache = Hn.make_cache(sh, wl.seq_lens, extra, **kw)
+    cache.reset()
+    Hn.fill(cache, sh, wl.seq_lens, wl.data_seed, gen_device="cuda")
+    oc = oracle_for(sh, wl.seq_lens, wl.data_seed, layers=layers, gen_device="cuda", **okw)
+    cache.drop_reposition(Hn.mask_tensor(cache, wl.masks))
+    assert cache.sync_status() == 0
+    oc.drop_reposition(0, wl.masks[0])
+    check_meta(cache, oc)
+    worst = check_kv(cache, oc, layers=layers, k_ulp=1)
+    say(" worst K ulp on sampled layers", worst)
+    q = W.randn_bf16((1, sh.n_layers, sh.n_q_heads, sh.head_dim), 202, device="cuda")
+    out = torch.empty_like(q)
+    ws = torch.empty(max(256, cache.decode_workspace_bytes(sh.n_layers, sh.n_q_heads)),
+                     dtype=torch.uint8, device=cache.device)
+    cache.decode_attention(q, out, ws)
+    assert cache.sync_status() == 0
+    check_attention(cache, oc, q, out, layers=layers, what=f"{variant} attention")
