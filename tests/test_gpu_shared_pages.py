@@ -15,8 +15,8 @@ pytestmark = pytest.mark.gpu
 from agent_kv_cache_amd import harness as Hn  # noqa: E402
 from agent_kv_cache_amd import workloads as W  # noqa: E402
 
-from gpu_util import (append_seeded, check_kv, check_meta, check_pool, oracle_for,  # noqa: E402
-                      say, snapshot, same_state)
+from gpu_util import (append_seeded, check_attention, check_kv, check_meta,  # noqa: E402
+                      check_pool, oracle_for, q_tensor, say, snapshot, same_state)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -140,3 +140,62 @@ def test_drop_and_copy_on_write_inside_a_shared_prefix():
     check_kv(cache, oc, k_ulp=1)
     _release(cache, oc, [0, 1, 2])
     assert check_pool(cache) == 0 and int(cache.free_count.item()) == cache.NB
+
+
+def test_prefix_reuse_at_new_positions():
+    """Reusing a compatible prefix of a stored sequence at other positions
+    ([CE] Appendix A.1.2: the longer prefix whose positions can be converted
+    is taken and its keys turned to the new positions): a fork that keeps the
+    prefix (drops the rest) and repositions it.  Pages whose entries keep
+    their positions are shared; the others are copied with K re-rotated."""
+    lens = [1000, 0, 0, 0]
+    cache, oc = _setup(lens, 73)
+    say("case the stored sequence has a position gap (drop without reposition)")
+    rows = [W.spans_to_mask(1000, [(200, 100)]), None, None, None]
+    cache.drop(Hn.mask_tensor(cache, rows))
+    assert cache.sync_status() == 0
+    oc.drop(0, rows[0])
+    n = len(oc.seqs[0])
+    assert n == 900
+    say("case prefix of 500 entries at canonical positions 0..499: 12 pages shared")
+    keep = np.zeros(n, np.uint8)
+    keep[500:] = 1
+    _fork(cache, oc, 0, 1, keep, repos=True)
+    tab = cache.block_table.cpu().numpy()
+    assert np.array_equal(tab[1, :12], tab[0, :12])             # entries 0..191 keep 0..191
+    assert not np.isin(tab[1, 12:32], tab[0, :57]).any()        # from the gap on: copied
+    assert np.array_equal(oc.seqs[1].pos, np.arange(500))
+    check_pool(cache)
+    check_meta(cache, oc)
+    check_kv(cache, oc, k_ulp=1)
+    say("case prefix of 320 entries moved to p + 37 (every position changes: nothing shared)")
+    keep = np.zeros(n, np.uint8)
+    keep[320:] = 1
+    newp = (oc.seqs[0].pos[:320] + 37).astype(np.int32)
+    dst_of = [2, -1, -1, -1]
+    pos_rows = [newp, None, None, None]
+    before = snapshot(cache, 0)
+    cache.fork(dst_of, Hn.mask_tensor(cache, [keep, None, None, None]), reposition=True,
+               new_pos=Hn.pos_tensor(cache, pos_rows))
+    assert cache.sync_status() == 0
+    oc.fork(0, 2, keep, reposition=True, new_pos=newp)
+    same_state(before, snapshot(cache, 0))
+    tab = cache.block_table.cpu().numpy()
+    assert not np.isin(tab[2, :20], tab[0, :57]).any()
+    assert np.array_equal(oc.seqs[2].pos, newp)
+    check_pool(cache)
+    check_meta(cache, oc)
+    check_kv(cache, oc, k_ulp=1)
+    say("case release the source: both reused prefixes keep their entries")
+    _release(cache, oc, [0])
+    check_pool(cache)
+    check_meta(cache, oc)
+    check_kv(cache, oc, k_ulp=1)
+    say("case decode over the reused prefixes")
+    q = q_tensor(SH, cache.B, SH.n_layers, 74, device=cache.device)
+    out = torch.empty_like(q)
+    ws = torch.empty(max(256, cache.decode_workspace_bytes(SH.n_layers, SH.n_q_heads)),
+                     dtype=torch.uint8, device=cache.device)
+    cache.decode_attention(q, out, ws)
+    assert cache.sync_status() == 0
+    check_attention(cache, oc, q, out, what="decode over reused prefixes")
