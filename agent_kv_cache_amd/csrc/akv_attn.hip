@@ -4,7 +4,8 @@
 // sequence (the active cache of [CE] sec. 3.1/3.3: dropped entries are no
 // longer present after compaction, so only surviving KV is read).
 //
-// Grid (split, kv head, sequence*layer); 8 waves per workgroup, wave w takes
+// Grid: split x kv head x (sequence, layer), flattened with the split
+// fastest; 8 waves per workgroup, wave w takes
 // pages w, w+8, ... of the split.  Per 16-token page a wave
 //   - loads K straight into MFMA A-operand registers (lane = token row,
 //     16-B loads) and computes S^T[16 tok x 16 q-head] with
@@ -90,7 +91,12 @@ __global__ __launch_bounds__(kAttnWaves * 64, AKV_ATTN_MIN_WAVES) void attn_kern
   auto s_v = reinterpret_cast<uint16_t (*)[kPage][VROW]>(s_raw);
   auto s_o = reinterpret_cast<float (*)[16][D]>(s_raw);
 
-  const int s = blockIdx.x, g = blockIdx.y, bl = blockIdx.z;
+  // one grid dimension, split fastest, then kv head, then (sequence, layer):
+  // the dispatch order of a (split, head, sequence x layer) grid without its
+  // 65535 limit on the last axis
+  const int s = (int)(blockIdx.x % (unsigned)nsplit);
+  const int gb = (int)(blockIdx.x / (unsigned)nsplit);
+  const int g = gb % d.H, bl = gb / d.H;
   // With sliding-window layers the grid's layer axis runs over the ordered
   // layers (full attention first) with the sequences fastest, so the long
   // rows are dispatched first and spread over the CUs instead of pairing up
@@ -316,7 +322,7 @@ __global__ __launch_bounds__(D) void combine_kernel(const float *__restrict__ pa
 hipError_t launch_attention(const Dev &d, const uint16_t *q, const int32_t *active_len, int l0,
                             int nL, int Hq, uint16_t *out, float *part, int nsplit,
                             const LayerOrder &order, hipStream_t st) {
-  const dim3 grid(nsplit, d.H, d.B * nL), block(kAttnWaves * 64);
+  const dim3 grid((unsigned)((long long)nsplit * d.H * d.B * nL)), block(kAttnWaves * 64);
   if (d.D == 128)
     hipLaunchKernelGGL(attn_kernel<128>, grid, block, 0, st, d, q, active_len, l0, nL, Hq, out,
                        part, nsplit, order);
@@ -325,6 +331,8 @@ hipError_t launch_attention(const Dev &d, const uint16_t *q, const int32_t *acti
                        part, nsplit, order);
   return hipGetLastError();
 }
+
+int attn_threads() { return kAttnWaves * 64; }
 
 int attn_blocks_per_cu(int D) {
   int n = 0;

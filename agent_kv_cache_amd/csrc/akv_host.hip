@@ -14,6 +14,10 @@
 
 using akv::Dev;
 
+namespace akv {
+int attn_threads();   // work-items per decode workgroup (akv_attn.hip)
+}
+
 // Decode workspace of akv_decode_attention_noalloc, for callers that cannot
 // allocate: one fixed array in the library's code object, so every GPU the
 // library runs on holds its own copy until the process ends.  In host code
@@ -221,6 +225,8 @@ akv_status akv_cache_init(const akv_cache_desc *d, akv_cache **out) {
   if (d->n_layers < 1 || d->n_kv_heads < 1 || d->n_blocks < 1 || d->n_seqs < 1 ||
       d->max_blocks_per_seq < 1)
     return AKV_ERR_ARG;
+  // the plan and state-export grids index sequences on their second axis
+  if (d->n_seqs > 65535) return AKV_ERR_ARG;
   if (d->block_size != akv::kPage) return AKV_ERR_ARG;
   if (d->head_dim != 64 && d->head_dim != 128) return AKV_ERR_ARG;
   // rotation frequencies must lie in [0, 1] (rope_base >= 1): the move's sine
@@ -491,8 +497,14 @@ static akv_status decode_impl(akv_cache *c, const uint16_t *q, const int32_t *ac
       n_q_heads / c->desc.n_kv_heads > 16)
     return AKV_ERR_ARG;
   if (!aligned(q, 16) || !aligned(out, 2)) return AKV_ERR_ARG;
-  if ((long long)c->desc.n_seqs * n_layers > 65535) return AKV_ERR_ARG;
   const int ns = nsplit_for(c, n_layers);
+  // one-dimensional grids: (split, kv head, sequence, layer) workgroups for
+  // the decode, (sequence, layer, query head) ones for the combine; each
+  // launch's size in work-items must fit 32 bits
+  const long long rows = (long long)c->desc.n_seqs * n_layers;
+  if (rows * ns * c->desc.n_kv_heads * akv::attn_threads() > (long long)UINT32_MAX ||
+      rows * n_q_heads * c->desc.head_dim > (long long)UINT32_MAX)
+    return AKV_ERR_ARG;
   if (ns > 1) {
     const size_t need = akv_decode_workspace_bytes(c, n_layers, n_q_heads);
     if (static_ws) {

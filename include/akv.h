@@ -96,7 +96,7 @@ typedef struct {
   int32_t head_dim;           /* d: 64 or 128 */
   int32_t block_size;         /* must be 16 */
   int32_t n_blocks;           /* NB pages in the pool, >= 1 */
-  int32_t n_seqs;             /* B sequences, >= 1 */
+  int32_t n_seqs;             /* B sequences, 1 .. 65535 */
   int32_t max_blocks_per_seq; /* page-table row length, >= 1 */
   double rope_base;           /* >= 1; theta_i = rope_base^(-2i/r), NeoX half split over the r rotary dims */
   uint16_t *k_pool;           /* bf16 [L][NB][Hkv][16][d] */
@@ -261,7 +261,9 @@ akv_status akv_fork(akv_cache *c, const int32_t *dst_of, const uint8_t *drop_mas
  * head h reads kv head h / (n_q_heads / n_kv_heads); no entry beyond
  * active_len and no self token; an empty sequence gives zeros.
  * Host-checked: n_q_heads multiple of n_kv_heads with ratio <= 16, layer
- * range inside [0, L).
+ * range inside [0, L), and each launch within 2^32 work-items (splits x
+ * n_kv_heads x B x n_layers workgroups of 512, B x n_layers x n_q_heads
+ * combine rows of d), else AKV_ERR_ARG.
  * akv_decode_workspace_bytes: bytes of `workspace` a call with these sizes
  * needs (its split-K partials; 256 when it runs unsplit), 0 for bad sizes. */
 size_t akv_decode_workspace_bytes(const akv_cache *c, int32_t n_layers,

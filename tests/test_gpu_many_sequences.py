@@ -106,3 +106,42 @@ def test_many_short_sequences():
     cache.decode_attention(q, out, ws)
     assert cache.sync_status() == 0
     check_attention(cache, oc, q, out, what=f"decode over {B} sequences")
+
+
+def test_decode_with_more_sequence_layer_rows_than_one_grid_axis_holds():
+    """2100 sequences x 32 layers = 67200 (sequence, layer) rows, more than
+    the 65535 one axis of a launch grid holds: the decode's one-dimensional
+    grid covers them.  A fused drop + reposition first; ids and positions of
+    every sequence, K/V and attention of 70 sampled sequences on 3 layers
+    against the oracle."""
+    sh = W.Shape(32, 1, 64, 2, 1.0e4)
+    n_seq = 2100
+    rng = np.random.default_rng(95)
+    lens = [int(n) for n in rng.integers(1, 48, size=n_seq)]
+    assert n_seq * sh.n_layers > 65535
+    cache = Hn.make_cache(sh, lens, 4500, max_blocks_per_seq=4)
+    cache.reset()
+    Hn.fill(cache, sh, lens, 96, gen_device="cpu")
+    assert cache.sync_status() == 0
+    say(f"case {n_seq} sequences x {sh.n_layers} layers, {sum(lens)} tokens")
+    masks = [(rng.random(n) < 0.3).astype(np.uint8) for n in lens]
+    cache.drop_reposition(Hn.mask_tensor(cache, masks))
+    assert cache.sync_status() == 0
+    meta = oracle_for(sh, lens, 96, with_kv=False)
+    for b in range(n_seq):
+        meta.drop_reposition(b, masks[b])
+    check_meta(cache, meta)
+    seqs = sorted(rng.choice(n_seq, size=70, replace=False).tolist())
+    lay = [0, 17, 31]
+    oc = oracle_for(sh, lens, 96, layers=lay, seqs=seqs)
+    for i, b in enumerate(seqs):
+        oc.drop_reposition(i, masks[b])
+    check_kv(cache, oc, k_ulp=1, seqs=seqs, layers=lay)
+    q = q_tensor(sh, n_seq, sh.n_layers, 97, device="cuda")
+    out = torch.empty_like(q)
+    ws = torch.empty(max(256, cache.decode_workspace_bytes(sh.n_layers, sh.n_q_heads)),
+                     dtype=torch.uint8, device=cache.device)
+    cache.decode_attention(q, out, ws)
+    assert cache.sync_status() == 0
+    check_attention(cache, oc, q, out, layers=lay, seqs=seqs,
+                    what=f"decode over {n_seq * sh.n_layers} (sequence, layer) rows")
