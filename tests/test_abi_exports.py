@@ -46,7 +46,7 @@ def test_scratch_size_formula():
 
 @pytest.mark.parametrize("field,value", [
     ("head_dim", 96), ("head_dim", 256), ("block_size", 32), ("n_layers", 0),
-    ("n_kv_heads", 0), ("n_blocks", 0), ("n_seqs", 0), ("max_blocks_per_seq", 0),
+    ("n_kv_heads", 0), ("n_blocks", 0), ("n_seqs", 0), ("n_seqs", 65536), ("max_blocks_per_seq", 0),
     ("rope_base", 0.0), ("rope_base", 0.5), ("rope_base", float("inf")), ("k_pool", None),
     ("scratch", None),
     ("scratch", 4096 + 8), ("scratch_bytes", 16), ("k_pool", 4096 + 2),
