@@ -289,24 +289,26 @@ def test_errors_leave_state_unchanged():
         _decode(c, q)                    # 5 query heads is not a multiple of 2
 
 
-@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
-def test_decode_gqa_ratios(G):
-    sh = W.Shape(2, 2, 128, 2 * G, 5.0e5)
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 8, 16])
+def test_decode_gqa_ratios(G, d):
+    sh = W.Shape(2, 2, d, 2 * G, 5.0e5)
     lens = [1, 16, 250, 513]
-    say(f"case decode G={G}")
-    c = _setup(sh, lens, seed=20 + G)
-    oc = oracle_for(sh, lens, 20 + G)
-    q = q_tensor(sh, len(lens), 2, 40 + G).to(c.device)
+    say(f"case decode G={G} d={d}")
+    c = _setup(sh, lens, seed=20 + G + d)
+    oc = oracle_for(sh, lens, 20 + G + d)
+    q = q_tensor(sh, len(lens), 2, 40 + G + d).to(c.device)
     out = _decode(c, q)
     check_attention(c, oc, q, out)
     out = _decode(c, q, [0, 3, 250, 100])
     check_attention(c, oc, q, out, active=[0, 3, 250, 100])
 
 
-def test_decode_sharp_softmax():
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_sharp_softmax(d):
     """Scaled-up queries make the softmax nearly one-hot: checks the running
     max and the rescaling across pages and splits."""
-    sh = W.Shape(1, 1, 128, 4, 5.0e5)
+    sh = W.Shape(1, 1, d, 4, 5.0e5)
     lens = [3000]
     c = _setup(sh, lens, seed=31)
     oc = oracle_for(sh, lens, 31)

@@ -248,15 +248,16 @@ def test_segment_attention_gqa(G, d):
     assert torch.equal(out1, out[:, 1:2])
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("G", [1, 3, 4, 16])
-def test_segment_attention_short_segments(G):
+def test_segment_attention_short_segments(G, d):
     """Every segment within one 16-column tile (16 // G rows): the split-KV
     kernel; many segments over few sequences, ragged lengths."""
-    H, d = 2, 128
+    H = 2
     sh = W.Shape(3, H, d, H * G, 5.0e5)
     lens = [5, 16, 17, 300, 1111]
     tb = 16 // G
-    say(f"case short segments G={G}")
+    say(f"case short segments G={G} d={d}")
     cache = Hn.make_cache(sh, lens, 0)
     cache.reset(np.random.default_rng(40 + G).permutation(cache.NB).astype(np.int32))
     Hn.fill(cache, sh, lens, 60 + G, gen_device="cpu")
