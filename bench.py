@@ -290,6 +290,26 @@ def cpu_baseline(wl, layers, seqs=None, ropt=None):
     }
 
 
+def _cpu_append_unit(task):
+    """One layer of the append in a pool worker: the oracle appends the
+    layer's keys as given (plain) and, into a second empty cache, rotated at
+    their positions (RoPE fused); returns (pid, seconds of each)."""
+    from oracle import akv_oracle as O
+    k = O.bf16_from_bits(task["k"])[:, None]
+    v = O.bf16_from_bits(task["v"])[:, None]
+    tid = np.arange(k.shape[0])
+    kw = dict(rotary_dim=task.get("rotary_dim"), theta=task.get("theta"))
+    oc = O.OracleCache(1, task["H"], task["D"], task["base"], **kw)
+    t0 = time.perf_counter()
+    oc.append(0, tid, k, v)
+    t1 = time.perf_counter()
+    oc = O.OracleCache(1, task["H"], task["D"], task["base"], **kw)
+    t2 = time.perf_counter()
+    oc.append_rotated(0, tid, k, v)
+    t3 = time.perf_counter()
+    return os.getpid(), t1 - t0, t3 - t2
+
+
 def _cpu_history_unit(task):
     """One layer of the 50-turn history in a pool worker: the oracle replays
     every op on that layer (appends untimed), then the final decode."""
@@ -723,6 +743,28 @@ def run_append(args):
                      "traffic": counted_traffic(
                          f"{name}_kernel_append_llama8b_32k{variant_tag(args)}_counters.json")}
     fr = res["append_rope"]
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the oracle on every layer of the same append, one layer per task
+        layers = list(range(sh.n_layers))
+        tasks = [dict(H=sh.n_kv_heads, D=sh.head_dim, base=sh.rope_base,
+                      k=_u16(k[l]), v=_u16(v[l]), rotary_dim=ropt.get("rotary_dim"),
+                      theta=ropt.get("inv_freq")) for l in layers]
+        del cache
+        torch.cuda.empty_cache()
+        out, wall, nw = _pool_map(_cpu_append_unit, tasks)
+        (t_plain, t_rope), t_all, used = _critical_path(out)
+        ab = n * 2 * (len(layers) * sh.n_kv_heads * sh.head_dim * 2) * 2 + n * 12
+        cpu = {"value": round(ab / t_rope / 1e9, 4), "unit": "GB/s", "cores": used,
+               "kind": "oracle",
+               "sample": f"append of {n} tokens: layers {layers} of {sh.n_layers}, one layer per task "
+                         f"of a {nw}-process pool, the plain append and the RoPE-fused "
+                         f"append per layer: {t_all:.2f} s on the busiest worker ({wall:.1f} s "
+                         f"pool wall time including unpacking the inputs); bytes are the "
+                         f"sample's share of the algorithmic bytes; value is the RoPE-fused "
+                         f"append",
+               "append_plain_gbps": round(ab / t_plain / 1e9, 4),
+               **host_info()}
     return {
         "metric": "append GB/s (K/V write of new tokens, plain and RoPE-fused), 1 GPU",
         "value": fr["gbps"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -736,6 +778,7 @@ def run_append(args):
                      "achieved": fr["gbps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": fr["frac_of_peak"], "traffic": fr["traffic"]},
         "parts": res,
+        **({"cpu_baseline": cpu} if cpu else {}),
     }
 
 
